@@ -1,0 +1,264 @@
+"""Plain, slow CPU oracle for the AWQ W4A16 hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this module. The product path (the C-ABI library
+and its Python binding) never calls it; it shares no code, header, table or
+helper with the HIP implementation.
+
+What it computes, step by step, in the pages' own order (calibration ->
+activation statistic -> per-channel scale s = s_X^alpha -> quantize W*diag(s)
+with group-wise round-to-nearest -> pack -> the W4A16 product with the
+folded activation X*diag(s)^-1):
+
+* Equivalence transform: W' = W diag(s), X' = diag(s)^-1 X, so W'X' = WX
+  before quantization (hungho77 blog "AWQ explained" -- "Scaling instead of
+  mixed precision"; AWQ Explained: Protecting the Weights That Matter Most --
+  "Scaling instead of mixed precision").
+* Scale parameterisation and search: s_j = mean_t |x_tj| ** alpha, alpha
+  grid-searched in [0, 1] to minimise || W x - Q(W diag(s)) diag(s)^-1 x || on
+  the calibration batch (AWQ Explained -- "How the scale is chosen"; hungho77
+  blog -- "Scaling instead of mixed precision").
+* Quantizer: plain round-to-nearest (ai360xpert "AWQ" -- "How It Works",
+  step 4), group-wise, 3 or 4 bits, groups of 128 (Real Python glossary
+  "activation-aware weight quantization (AWQ)"), asymmetric grid with an
+  integer zero point, defaults bits=4 / group 128 / zero_point=true
+  (AWQ Explained -- "How the scale is chosen", last paragraph); the grid step
+  is the group's range divided by the number of levels and the rounding error
+  is about half a step (AWQ Explained -- "Scaling instead of mixed precision").
+
+Precision: the quantizer runs in float32 with single IEEE roundings
+(multiply, subtract, divide) and round-half-to-even, exactly as the
+hot path is required to; statistics, losses and the matmul run in float64.
+
+Readings taken where the pages are silent or garbled (each one is also
+listed in the design notes):
+
+R1  s_X is the mean of |x| over calibration tokens (not RMS, not max).
+R2  a channel whose statistic is exactly 0 gets s = 1 for every alpha.
+R3  s = float32(pow(m, alpha)) with pow evaluated in double precision.
+R3b s is not normalised.
+R4  "number of levels" is read as the number of steps 2^b - 1, so that both
+    ends of the range are on the grid.
+R4b the range always contains 0: lo = min(0, min W'), hi = max(0, max W').
+R5  q = clamp(rint(W' / delta) + z, 0, 2^b - 1), z = rint(-lo / delta): the
+    zero point is an integer added after rounding.
+R6  round-half-to-even everywhere; an all-zero group gets delta = 1, z = 0.
+R7  the layer-output error is the squared Frobenius norm over calibration
+    tokens and output channels, evaluated in exact (float64) arithmetic with
+    the original fp16 W; the first minimum over the grid wins.
+R9  packing: see ``pack``.
+R10 scales are stored as the float32 delta, zero points as uint8.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# calibration statistic and scale candidates
+# ----------------------------------------------------------------------------
+
+
+def act_stats(xcal: np.ndarray) -> np.ndarray:
+    """m_j = (1/T) * sum_t |x_tj| in float64 (R1).
+
+    fp16 values are integer multiples of 2^-24 below 2^16, so for T < 8192
+    the float64 sum is exact and independent of summation order; the only
+    rounding is the final division by T.
+    """
+    x = np.abs(np.asarray(xcal, dtype=np.float16).astype(np.float64))
+    return x.sum(axis=0) / x.shape[0]
+
+
+def scale_from_stats(m: np.ndarray, alpha) -> np.ndarray:
+    """s_j = float32(pow(m_j, alpha)) (R2, R3). alpha is taken as float32."""
+    a = float(np.float32(alpha))
+    out = np.empty(len(m), dtype=np.float32)
+    for j, mj in enumerate(np.asarray(m, dtype=np.float64)):
+        out[j] = np.float32(math.pow(float(mj), a)) if mj > 0.0 else np.float32(1.0)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# group-wise asymmetric round-to-nearest
+# ----------------------------------------------------------------------------
+
+
+def scaled_weight(W: np.ndarray, s) -> np.ndarray:
+    """W' = W diag(s) as float32: one float32 multiply per element.
+
+    s scales input channels, i.e. the columns of W [N, K] (p3/p4 "Scaling
+    instead of mixed precision"). s = None means s = 1 (plain RTN).
+    """
+    w = np.asarray(W, dtype=np.float16).astype(np.float32)
+    if s is None:
+        return w
+    s = np.asarray(s, dtype=np.float32)
+    assert s.shape == (w.shape[1],)
+    return (w * s[None, :]).astype(np.float32)
+
+
+def quantize_groups(wp: np.ndarray, bits: int, group: int):
+    """RTN quantization of float32 W' [N, K] in groups of `group` along K.
+
+    Returns (q int64 [N, K], delta float32 [N, K/group], z int64 [N, K/group]).
+    """
+    wp = np.asarray(wp, dtype=np.float32)
+    N, K = wp.shape
+    assert K % group == 0
+    qmax = (1 << bits) - 1
+    g = wp.reshape(N, K // group, group)
+    lo = np.minimum(g.min(axis=2), np.float32(0.0))          # R4b
+    hi = np.maximum(g.max(axis=2), np.float32(0.0))
+    r = (hi - lo).astype(np.float32)
+    flat = r == 0                                            # all-zero group (R6)
+    safe_r = np.where(flat, np.float32(1.0), r).astype(np.float32)
+    delta = (safe_r / np.float32(qmax)).astype(np.float32)   # R4: range / (2^b - 1)
+    delta = np.where(flat, np.float32(1.0), delta).astype(np.float32)
+    z = np.rint((-lo / delta).astype(np.float32)).astype(np.int64)
+    z = np.where(flat, 0, z)
+    q = np.rint((g / delta[..., None]).astype(np.float32)).astype(np.int64) + z[..., None]
+    q = np.clip(q, 0, qmax)                                  # R5
+    return q.reshape(N, K), delta, z
+
+
+def quantize(W: np.ndarray, s, bits: int, group: int):
+    """(q, scales fp32 [N, K/G], zeros uint8 [N, K/G]) of W diag(s)."""
+    q, delta, z = quantize_groups(scaled_weight(W, s), bits, group)
+    return q, delta.astype(np.float32), z.astype(np.uint8)
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int) -> np.ndarray:
+    """(q - z) * delta, exact in float64 [N, K]."""
+    N, K = q.shape
+    qq = q.reshape(N, K // group, group).astype(np.int64) - zeros.astype(np.int64)[..., None]
+    return (qq.astype(np.float64) * scales.astype(np.float64)[..., None]).reshape(N, K)
+
+
+# ----------------------------------------------------------------------------
+# packing (R9)
+# ----------------------------------------------------------------------------
+
+
+def words_per_group(bits: int, group: int) -> int:
+    """int4: 8 codes per 32-bit word; int3: 10 codes per word (bits 30-31 unused)."""
+    if bits == 4:
+        assert group % 8 == 0
+        return group // 8
+    if bits == 3:
+        return -(-group // 10)
+    raise ValueError("bits must be 3 or 4")
+
+
+def words_per_row(K: int, bits: int, group: int) -> int:
+    """Groups are stored back to back, each starting on a word boundary; the
+    row is padded with zero words to a multiple of 4 words (16 bytes)."""
+    assert K % group == 0
+    w = (K // group) * words_per_group(bits, group)
+    return -(-w // 4) * 4
+
+
+def pack(q: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Pack codes q [N, K] into uint32 [N, words_per_row].
+
+    Inside group g of row n, the code at position j (k = g*group + j) sits in
+    word g*words_per_group + j // c at bits [b*(j % c), b*(j % c) + b), with
+    c = 8 for int4 and c = 10 for int3. Unused slots, the two top bits of an
+    int3 word and the row padding are zero.
+    """
+    N, K = q.shape
+    cpw = 8 if bits == 4 else 10
+    wpg = words_per_group(bits, group)
+    ng = K // group
+    out = np.zeros((N, words_per_row(K, bits, group)), dtype=np.uint64)
+    qg = q.reshape(N, ng, group).astype(np.uint64)
+    for j in range(group):
+        word = j // cpw
+        shift = np.uint64(bits * (j % cpw))
+        cols = np.arange(ng) * wpg + word
+        out[:, cols] |= qg[:, :, j] << shift
+    return out.astype(np.uint32)
+
+
+def unpack(qpacked: np.ndarray, bits: int, group: int, K: int) -> np.ndarray:
+    N = qpacked.shape[0]
+    cpw = 8 if bits == 4 else 10
+    wpg = words_per_group(bits, group)
+    ng = K // group
+    mask = np.uint64((1 << bits) - 1)
+    w = qpacked.astype(np.uint64)
+    q = np.empty((N, ng, group), dtype=np.int64)
+    for j in range(group):
+        cols = np.arange(ng) * wpg + j // cpw
+        q[:, :, j] = ((w[:, cols] >> np.uint64(bits * (j % cpw))) & mask).astype(np.int64)
+    return q.reshape(N, K)
+
+
+def quantize_pack(W: np.ndarray, s, bits: int, group: int):
+    """The quantize-and-pack step: (qpacked uint32, scales fp32, zeros uint8)."""
+    q, scales, zeros = quantize(W, s, bits, group)
+    return pack(q, bits, group), scales, zeros
+
+
+# ----------------------------------------------------------------------------
+# folding diag(s)^-1 into the activation, and the W4A16 product
+# ----------------------------------------------------------------------------
+
+
+def fold_inv_scale(X: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """X' = fp16(float32(X) / s): one float32 division, then one rounding to
+    fp16 (AWQ Explained -- "Scaling instead of mixed precision": the
+    activation channel is divided by the same s)."""
+    x = np.asarray(X, dtype=np.float16).astype(np.float32)
+    return (x / np.asarray(s, dtype=np.float32)[None, :]).astype(np.float32).astype(np.float16)
+
+
+def matmul(Xp: np.ndarray, qpacked: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+           bits: int, group: int, K: int) -> np.ndarray:
+    """Y = X' dequant(Q)^T in float64 [M, N]; X' is the fp16 activation."""
+    Wd = dequantize(unpack(qpacked, bits, group, K), scales, zeros, group)
+    return np.asarray(Xp, dtype=np.float16).astype(np.float64) @ Wd.T
+
+
+def matmul_rows(Xp, qpacked, scales, zeros, bits, group, K, rows) -> np.ndarray:
+    """Y[:, rows] only (for sampled checks at large N)."""
+    rows = np.asarray(rows)
+    return matmul(Xp, qpacked[rows], scales[rows], zeros[rows], bits, group, K)
+
+
+# ----------------------------------------------------------------------------
+# layer-output loss and the alpha grid search
+# ----------------------------------------------------------------------------
+
+
+def quant_error(W: np.ndarray, s: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """D = W - Q(W diag(s)) diag(s)^-1 in float64 [N, K]."""
+    q, scales, zeros = quantize(W, s, bits, group)
+    what = dequantize(q, scales, zeros, group)
+    return np.asarray(W, dtype=np.float16).astype(np.float64) - what / np.asarray(s, np.float64)[None, :]
+
+
+def layer_loss(xcal: np.ndarray, W: np.ndarray, s: np.ndarray, bits: int, group: int) -> float:
+    """L = || Xcal D^T ||_F^2 (R7): the layer-output error on the calibration
+    batch, sum over tokens t and output channels n of
+    (sum_k x_tk (W_nk - Wq_nk / s_k))^2."""
+    D = quant_error(W, s, bits, group)
+    E = np.asarray(xcal, dtype=np.float16).astype(np.float64) @ D.T
+    return float(np.sum(E * E))
+
+
+def scale_search(W: np.ndarray, xcal: np.ndarray, alpha_grid, bits: int, group: int):
+    """Grid search over alpha; returns (s float32 [K], best index, losses float64).
+
+    The grid is scanned in the given order with a strict '<', so the first
+    minimum wins (R7).
+    """
+    m = act_stats(xcal)
+    losses = np.empty(len(alpha_grid), dtype=np.float64)
+    best = 0
+    for i, a in enumerate(alpha_grid):
+        losses[i] = layer_loss(xcal, W, scale_from_stats(m, a), bits, group)
+        if losses[i] < losses[best]:
+            best = i
+    return scale_from_stats(m, alpha_grid[best]), best, losses
