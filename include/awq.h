@@ -1,0 +1,176 @@
+/*
+ * awq.h -- C ABI of libawq: the data-parallel hot path of AWQ
+ * (activation-aware weight quantization) with 4-bit or 3-bit group-wise
+ * weights and fp16 activations (W4A16 / W3A16), for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (as stated on the pages this library follows):
+ *   - a linear layer Y = W X is rewritten as (W diag(s)) (diag(s)^-1 X),
+ *     which is exact before quantization (hungho77 blog "AWQ explained" --
+ *     "Scaling instead of mixed precision"; AWQ Explained: Protecting the
+ *     Weights That Matter Most -- "Scaling instead of mixed precision");
+ *   - s_j = mean_t |x_tj| ** alpha with alpha grid-searched in [0, 1] to
+ *     minimise the layer-output error on a calibration batch (AWQ Explained
+ *     -- "How the scale is chosen");
+ *   - W diag(s) is quantized with plain round-to-nearest, group-wise along
+ *     the input dimension, 3 or 4 bits, groups of 128, asymmetric grid with
+ *     an integer zero point (ai360xpert "AWQ" -- "How It Works"; Real Python
+ *     glossary "activation-aware weight quantization (AWQ)"; AWQ Explained --
+ *     "How the scale is chosen");
+ *   - at run time the packed weights are loaded, unpacked, dequantized and
+ *     multiplied with fp16 activations (hungho77 blog -- "Why the engine is
+ *     part of the method").
+ *
+ * Conventions for every call:
+ *   - All arrays are dense, row-major and contiguous. fp16 values are passed
+ *     as uint16_t bit patterns.
+ *   - W is [N, K]: row n = output channel, column k = input channel.
+ *     Activations are [tokens, K]; Y = X' dequant(Q)^T is [M, N].
+ *   - "dev" pointers are HIP device memory; "host" pointers are host memory.
+ *     Device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer. The library never allocates or frees
+ *     device memory; its only scratch is the caller's `workspace`.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls enqueue
+ *     their kernels on it and return without waiting, except
+ *     awq_scale_search, which synchronizes `stream` (it returns host values).
+ *   - Arguments are validated before any HIP call; a bad argument returns
+ *     AWQ_ERR_INVALID_ARG or AWQ_ERR_UNSUPPORTED and enqueues nothing. With
+ *     no usable GPU the calls return AWQ_ERR_NO_DEVICE. A failed launch
+ *     returns AWQ_ERR_HIP.
+ *   - Inputs must be finite; the result is unspecified otherwise.
+ *   - The library keeps no state between calls; calls on different streams
+ *     may run concurrently as long as their output buffers do not overlap.
+ *
+ * Supported shapes: bits in {3, 4}; group in {128, 256, 512} (or -1,
+ * meaning group = K, when K is one of those); K a multiple of group.
+ *
+ * Packed weight layout (Qpacked, uint32 [N, awq_packed_words_per_row]):
+ *   group g of row n holds its codes along K; the code at position j of the
+ *   group (k = g*group + j) sits in word g*wpg + j / c, bits
+ *   [b*(j % c), b*(j % c) + b), where c = 8 codes per word for int4 and
+ *   c = 10 codes per word for int3 (bits 30-31 zero), and
+ *   wpg = ceil(group / c) words per group. Every group starts on a word
+ *   boundary; unused slots are zero; each row is padded with zero words to a
+ *   multiple of 4 words (16 bytes).
+ *   scales: float32 [N, K/group], the grid step delta of each group.
+ *   zeros:  uint8   [N, K/group], the integer zero point z of each group.
+ *   A weight dequantizes to (q - z) * delta.
+ */
+#ifndef AWQ_H
+#define AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misaligned pointer */
+  AWQ_ERR_UNSUPPORTED = 2, /* valid request outside the supported shapes */
+  AWQ_ERR_NO_DEVICE = 3,   /* no HIP device visible */
+  AWQ_ERR_HIP = 4,         /* a HIP runtime call or a launch failed */
+  AWQ_ERR_WORKSPACE = 5    /* workspace NULL or smaller than required */
+} awq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* awq_status_string(int status);
+
+/* ABI version of this library (major * 100 + minor). */
+int awq_version(void);
+
+/* uint32 words per packed row for (K, bits, group); 0 if the combination is
+ * invalid. int4 + group 128: K/8. int3 + group 128: 13 words per group,
+ * rounded up to a multiple of 4. */
+size_t awq_packed_words_per_row(int K, int bits, int group);
+
+/* Activation statistic (AWQ Explained -- "How the scale is chosen": the
+ * scale is driven by mean(|x_j|) per input channel):
+ *   m[k] = (sum_t |Xcal[t, k]|) / T, in float64.
+ * Xcal: dev fp16 [T, K]; m: dev float64 [K]. 1 <= T < 8192 (the fp16 sum is
+ * then exact in float64, so the result does not depend on summation order). */
+awq_status awq_act_stats(const uint16_t* Xcal, int T, int K, double* m, void* stream);
+
+/* Scale candidates s = s_X ** alpha for every alpha of the grid (AWQ
+ * Explained -- "How the scale is chosen"):
+ *   s[a, k] = float32(pow(m[k], alpha[a])) (pow in float64), or 1 if
+ *   m[k] == 0.
+ * m: dev float64 [K]; alpha: dev float32 [n_alpha]; s: dev float32
+ * [n_alpha, K]. */
+awq_status awq_scale_candidates(const double* m, int K, const float* alpha, int n_alpha,
+                                float* s, void* stream);
+
+/* Round-to-nearest quantize-and-pack of W diag(s) (ai360xpert "AWQ" --
+ * "How It Works", step 4; AWQ Explained -- "Scaling instead of mixed
+ * precision" and "How the scale is chosen"). Per row n and group g, in
+ * float32 with single roundings and round-half-to-even:
+ *   W' = float32(W) * s[k]          (s == NULL means s = 1, plain RTN)
+ *   lo = min(0, min W'), hi = max(0, max W'), r = hi - lo
+ *   r == 0:  delta = 1, z = 0
+ *   else:    delta = r / (2^bits - 1), z = rint(-lo / delta)
+ *   q = clamp(rint(W' / delta) + z, 0, 2^bits - 1)
+ * W: dev fp16 [N, K]; s: dev float32 [K] or NULL; outputs as in the layout
+ * above (qpacked dev uint32 [N, words_per_row], scales dev float32
+ * [N, K/group], zeros dev uint8 [N, K/group]). Padding words are written as
+ * zero. Asynchronous on `stream`. */
+awq_status awq_quantize_pack(const uint16_t* W, const float* s, int N, int K, int bits, int group,
+                             uint32_t* qpacked, float* scales, uint8_t* zeros, void* stream);
+
+/* Fold diag(s)^-1 into the activation (AWQ Explained -- "Scaling instead of
+ * mixed precision": the matching activation channel is divided by s):
+ *   Xout[m, k] = fp16(float32(X[m, k]) / s[k])   (round-to-nearest-even)
+ * X, Xout: dev fp16 [M, K] (may be the same buffer); s: dev float32 [K]. */
+awq_status awq_fold_inv_scale(const uint16_t* X, const float* s, int M, int K, uint16_t* Xout,
+                              void* stream);
+
+/* The W4A16 (or W3A16) product (hungho77 blog -- "Why weight-only
+ * quantization fits decoding" and "Why the engine is part of the method"):
+ *   Y[m, n] = sum_k X'[m, k] * (q[n, k] - z[n, g(k)]) * delta[n, g(k)]
+ * accumulated in float32 and rounded once to fp16.
+ * X': dev fp16 [M, K] (already divided by s); qpacked/scales/zeros as
+ * produced by awq_quantize_pack; Y: dev fp16 [M, N].
+ * M <= 16 runs the decode kernels (memory-bound weight streaming), larger M
+ * the prefill kernels (fp16 matrix cores). Asynchronous on `stream`. */
+awq_status awq_w4a16_matmul(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                            const uint8_t* zeros, int M, int N, int K, int bits, int group,
+                            uint16_t* Y, void* stream);
+
+/* awq_w4a16_matmul with an explicit kernel choice, so that every kernel can
+ * be checked and timed on every shape: kernel 0 = automatic (as
+ * awq_w4a16_matmul), 1 = decode kernel (M <= 16 for int4, M <= 4 for int3),
+ * 2 = int4 decode kernel in exact-dequant form (M <= 16), 3 = prefill
+ * kernel (any M). Returns AWQ_ERR_UNSUPPORTED for a kernel that does not
+ * cover the request. */
+awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                                   const uint8_t* zeros, int M, int N, int K, int bits, int group,
+                                   uint16_t* Y, int kernel, void* stream);
+
+/* Bytes of device workspace awq_scale_search needs for these sizes
+ * (0 if the sizes are invalid). */
+size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);
+
+/* Per-layer grid search over alpha (AWQ Explained -- "How the scale is
+ * chosen"; hungho77 blog -- "Scaling instead of mixed precision"):
+ *   m = awq_act_stats(Xcalib); for each alpha_i: s_i = m ** alpha_i,
+ *   D_i = W - Q(W diag(s_i)) diag(s_i)^-1  (Q as in awq_quantize_pack),
+ *   loss[i] = || Xcalib D_i^T ||_F^2  (sum over tokens and output channels),
+ *   best = first index of the minimum loss; s_out = s_best.
+ * W: dev fp16 [N, K]; Xcalib: dev fp16 [T, K]; alpha_grid: host float32
+ * [n_alpha] (values in [0, 1]); s_out: dev float32 [K]; loss_out: host
+ * float64 [n_alpha] (may be NULL); best_index: host int (may be NULL);
+ * workspace: dev, at least awq_scale_search_workspace_bytes(...) bytes.
+ * The losses are computed with float32 products of fp16-rounded error
+ * terms and float64 sums; they agree with an exact evaluation to about
+ * 1e-5 relative. Synchronizes `stream` before returning. */
+awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
+                            const float* alpha_grid, int n_alpha, int bits, int group, float* s_out,
+                            double* loss_out, int* best_index, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_H */

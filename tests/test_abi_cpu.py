@@ -1,0 +1,146 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+symbol include/awq.h declares, and rejects bad arguments before any HIP
+call. With no device visible, valid requests return AWQ_ERR_NO_DEVICE."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT
+from oracle import awq_oracle as O
+import weight_only_bit_w4a16_amd as awq
+from weight_only_bit_w4a16_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    h = awq.lib()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    h = awq.lib()
+    for code, name in _lib.STATUS.items():
+        assert h.awq_status_string(code).decode() == name
+    assert h.awq_status_string(99).decode() == "AWQ_ERR_UNKNOWN"
+    assert h.awq_version() == 100
+
+
+@pytest.mark.parametrize("K,bits,group", [(128, 4, 128), (4096, 4, 128), (8192, 4, 128),
+                                          (11008, 4, 128), (512, 3, 128), (4096, 3, 128),
+                                          (11008, 3, 128), (4096, 4, 256), (4096, 3, 512),
+                                          (1024, 3, 256)])
+def test_words_per_row_matches_layout(K, bits, group):
+    assert awq.packed_words_per_row(K, bits, group) == O.words_per_row(K, bits, group)
+
+
+def test_words_per_row_rejects():
+    h = awq.lib()
+    assert h.awq_packed_words_per_row(4096, 5, 128) == 0
+    assert h.awq_packed_words_per_row(4000, 4, 128) == 0
+    assert h.awq_packed_words_per_row(4096, 4, 64) == 0
+    assert h.awq_packed_words_per_row(256, 4, -1) == 256 // 8
+    assert h.awq_packed_words_per_row(0, 4, 128) == 0
+
+
+# fake, aligned, never-dereferenced device addresses
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+NULL = None
+
+
+def _mm(*, X=P, q=P, s=P, z=P, M=1, N=64, K=256, bits=4, group=128, Y=P2, kernel=None):
+    h = awq.lib()
+    if kernel is None:
+        return h.awq_w4a16_matmul(X, q, s, z, M, N, K, bits, group, Y, NULL)
+    return h.awq_w4a16_matmul_kernel(X, q, s, z, M, N, K, bits, group, Y, kernel, NULL)
+
+
+def test_matmul_validation():
+    E = _lib
+    assert _mm(X=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(Y=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(M=0) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(N=-1) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(X=MIS) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(bits=5) == E.AWQ_ERR_UNSUPPORTED
+    assert _mm(K=200) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(group=64) == E.AWQ_ERR_UNSUPPORTED
+    assert _mm(group=0) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(kernel=7) == E.AWQ_ERR_INVALID_ARG
+    assert _mm(kernel=1, M=17) == E.AWQ_ERR_UNSUPPORTED
+    assert _mm(kernel=2, bits=3) == E.AWQ_ERR_UNSUPPORTED
+    assert _mm(kernel=1, bits=3, M=5) == E.AWQ_ERR_UNSUPPORTED
+
+
+def test_valid_calls_without_device_report_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    h = awq.lib()
+    E = _lib
+    assert _mm() == E.AWQ_ERR_NO_DEVICE
+    assert _mm(M=2048, K=8192, N=128) == E.AWQ_ERR_NO_DEVICE
+    assert h.awq_quantize_pack(P, NULL, 64, 256, 4, 128, P, P, P, NULL) == E.AWQ_ERR_NO_DEVICE
+    assert h.awq_fold_inv_scale(P, P, 4, 256, P2, NULL) == E.AWQ_ERR_NO_DEVICE
+    assert h.awq_act_stats(P, 64, 256, P2, NULL) == E.AWQ_ERR_NO_DEVICE
+    assert h.awq_scale_candidates(P, 256, P, 20, P2, NULL) == E.AWQ_ERR_NO_DEVICE
+
+
+def test_quantize_pack_validation():
+    h = awq.lib()
+    E = _lib
+    assert h.awq_quantize_pack(NULL, NULL, 64, 256, 4, 128, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_quantize_pack(P, MIS, 64, 256, 4, 128, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_quantize_pack(P, NULL, 0, 256, 4, 128, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_quantize_pack(P, NULL, 64, 256, 2, 128, P, P, P, NULL) == E.AWQ_ERR_UNSUPPORTED
+    assert h.awq_quantize_pack(P, NULL, 64, 300, 4, 128, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+
+
+def test_other_validation():
+    h = awq.lib()
+    E = _lib
+    assert h.awq_fold_inv_scale(P, NULL, 4, 256, P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_fold_inv_scale(P, P, 4, 250, P2, NULL) == E.AWQ_ERR_UNSUPPORTED
+    assert h.awq_act_stats(P, 0, 256, P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_act_stats(P, 8192, 256, P2, NULL) == E.AWQ_ERR_UNSUPPORTED
+    assert h.awq_scale_candidates(P, 256, P, 0, P2, NULL) == E.AWQ_ERR_INVALID_ARG
+
+
+def test_scale_search_validation():
+    h = awq.lib()
+    E = _lib
+    a = np.arange(20, dtype=np.float32) / 20
+    ap = a.ctypes.data_as(ctypes.c_void_p)
+    loss = np.zeros(20)
+    lp = loss.ctypes.data_as(ctypes.c_void_p)
+    best = ctypes.c_int(0)
+    need = h.awq_scale_search_workspace_bytes(64, 256, 32, 20, 4, 128)
+    assert h.awq_scale_search_workspace_bytes(64, 256, 0, 20, 4, 128) == 0
+    assert h.awq_scale_search_workspace_bytes(64, 250, 32, 20, 4, 128) == 0
+
+    def call(ws=P, nbytes=need, alpha=ap, T=32, K=256):
+        return h.awq_scale_search(P, P, 64, K, T, alpha, 20, 4, 128, P2, lp, ctypes.byref(best),
+                                  ws, nbytes, NULL)
+    assert need > 0
+    assert call(alpha=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert call(T=0) == E.AWQ_ERR_INVALID_ARG
+    assert call(ws=NULL) == E.AWQ_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == E.AWQ_ERR_WORKSPACE
+    bad = a.copy()
+    bad[3] = 1.5
+    assert call(alpha=bad.ctypes.data_as(ctypes.c_void_p)) == E.AWQ_ERR_INVALID_ARG

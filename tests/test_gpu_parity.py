@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: packed codes, scales, zero points, the activation statistic, the
+scale candidates and the folded activation. Matmul outputs: per output row
+m, max_n |Y - Y*| <= 1e-3 * max_n |Y*| against the oracle's float64 product
+over the same dequantized weights (elementwise relative error is ill-posed
+for outputs near zero). Full-size workloads are checked on sampled output
+rows, which the oracle computes row by row.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import datagen
+from oracle import awq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import weight_only_bit_w4a16_amd as awq  # noqa: E402
+
+TOL = 1e-3
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def assert_rows_close(Yg, Yref, tol=TOL):
+    Yg = np.asarray(Yg, dtype=np.float64)
+    assert Yg.shape == Yref.shape
+    assert np.all(np.isfinite(Yg))
+    for m in range(Yref.shape[0]):
+        scale = np.abs(Yref[m]).max()
+        err = np.abs(Yg[m] - Yref[m]).max()
+        assert err <= tol * scale, (m, err / scale)
+
+
+def assert_same_bits(a, b):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    assert a.shape == b.shape
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def sample_rows(N, count=256, seed=0):
+    g = np.random.default_rng(seed)
+    rows = set([0, 1, N - 1, N - 2, N // 2]) | set(g.choice(N, size=min(count, N), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@functools.lru_cache(maxsize=2)
+def workload_host(name):
+    w = datagen.WORKLOADS[name]
+    return datagen.weight(w), datagen.calibration(w)
+
+
+# ---------------------------------------------------------------------------
+# quantize-and-pack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("N,K,group", [(1, 128, 128), (17, 384, 128), (64, 512, 128),
+                                       (33, 1024, 256), (5, 2048, 512), (40, 11008, 128)])
+@pytest.mark.parametrize("with_s", [False, True])
+def test_quantize_pack_small(bits, N, K, group, with_s):
+    say("quantize_pack", bits, N, K, group, with_s)
+    W = datagen.random_f16((N, K), 0.02, seed=N + K)
+    s = datagen.random_f32_positive(K, 0.2, 9.0, seed=K) if with_s else None
+    qo, so, zo = O.quantize_pack(W, s, bits, group)
+    q, sc, z = awq.quantize_pack(dev(W), dev(s) if with_s else None, bits, group)
+    torch.cuda.synchronize()
+    assert_same_bits(host(q), qo)
+    assert_same_bits(host(sc), so)
+    assert_same_bits(host(z), zo)
+
+
+def test_quantize_pack_degenerate_groups():
+    # all-zero, single-signed and exactly-representable groups
+    K = 512
+    W = np.zeros((4, K), np.float16)
+    W[1] = np.linspace(0.1, 0.5, K).astype(np.float16)
+    W[2] = -np.linspace(0.1, 0.5, K).astype(np.float16)
+    W[3] = ((np.arange(K) % 16 - 7) / 16).astype(np.float16)
+    for bits in (3, 4):
+        qo, so, zo = O.quantize_pack(W, None, bits, 128)
+        q, sc, z = awq.quantize_pack(dev(W), None, bits, 128)
+        assert_same_bits(host(q), qo)
+        assert_same_bits(host(sc), so)
+        assert_same_bits(host(z), zo)
+
+
+@pytest.mark.parametrize("name", list(datagen.WORKLOADS))
+def test_quantize_pack_workload(name):
+    w = datagen.WORKLOADS[name]
+    say("quantize_pack workload", name)
+    W, Xc = workload_host(name)
+    m = O.act_stats(Xc)
+    s = O.scale_from_stats(m, 0.5)
+    q, sc, z = awq.quantize_pack(dev(W), dev(s), w.bits, w.group)
+    rows = sample_rows(w.N)
+    qo, so, zo = O.quantize_pack(W[rows], s, w.bits, w.group)
+    assert_same_bits(host(q)[rows], qo)
+    assert_same_bits(host(sc)[rows], so)
+    assert_same_bits(host(z)[rows], zo)
+
+
+# ---------------------------------------------------------------------------
+# statistic, scale candidates, fold
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,K", [(1, 128), (64, 512), (512, 4096), (512, 11008), (7, 1000)])
+def test_act_stats_exact(T, K):
+    X = datagen.random_f16((T, K), 3.0, seed=T * K)
+    assert_same_bits(host(awq.act_stats(dev(X))), O.act_stats(X))
+
+
+def test_scale_candidates_exact():
+    w = datagen.WORKLOADS["llama7b_mlp_down_11008x4096_int4"]
+    _, Xc = workload_host(w.name)
+    m = O.act_stats(Xc)
+    m[5] = 0.0
+    a = datagen.alpha_grid(20)
+    s = host(awq.scale_candidates(dev(m), dev(a)))
+    ref = np.stack([O.scale_from_stats(m, ai) for ai in a])
+    assert_same_bits(s, ref)
+
+
+@pytest.mark.parametrize("M,K", [(1, 512), (3, 4096), (2048, 8192), (5, 11008)])
+def test_fold_exact(M, K):
+    X = datagen.random_f16((M, K), 1.0, seed=M + K)
+    s = datagen.random_f32_positive(K, 0.05, 20.0, seed=K + 1)
+    assert_same_bits(host(awq.fold_inv_scale(dev(X), dev(s))), O.fold_inv_scale(X, s))
+
+
+# ---------------------------------------------------------------------------
+# W4A16 product: decode kernels
+# ---------------------------------------------------------------------------
+
+def _packed(W, s, bits, group):
+    q, sc, z = awq.quantize_pack(dev(W), dev(s) if s is not None else None, bits, group)
+    return q, sc, z
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("N,K", [(16, 128), (17, 384), (100, 1024), (257, 4096)])
+@pytest.mark.parametrize("kernel", [awq.KERNEL_AUTO, awq.KERNEL_DECODE_EXACT])
+def test_decode_int4_small(M, N, K, kernel):
+    say("decode int4", M, N, K, kernel)
+    W = datagen.random_f16((N, K), 0.02, seed=7 * N + K)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 3)
+    X = datagen.random_f16((M, K), 1.0, seed=M + 11)
+    q, sc, z = _packed(W, s, 4, 128)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, 128, kernel=kernel))
+    qo, so, zo = O.quantize_pack(W, s, 4, 128)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, 128, K))
+
+
+@pytest.mark.parametrize("group", [256, 512])
+def test_decode_int4_larger_groups(group):
+    N, K, M = 48, 2048, 2
+    W = datagen.random_f16((N, K), 0.02, seed=group)
+    X = datagen.random_f16((M, K), 1.0, seed=group + 1)
+    q, sc, z = _packed(W, None, 4, group)
+    qo, so, zo = O.quantize_pack(W, None, 4, group)
+    for kernel in (awq.KERNEL_AUTO, awq.KERNEL_DECODE_EXACT):
+        Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group, kernel=kernel))
+        assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, group, K))
+
+
+def test_decode_deterministic():
+    W = datagen.random_f16((300, 4096), 0.02, seed=1)
+    X = datagen.random_f16((1, 4096), 1.0, seed=2)
+    q, sc, z = _packed(W, None, 4, 128)
+    a = host(awq.w4a16_matmul(dev(X), q, sc, z))
+    b = host(awq.w4a16_matmul(dev(X), q, sc, z))
+    assert_same_bits(a, b)
+
+
+def _decode_cases():
+    out = []
+    for name, w in datagen.WORKLOADS.items():
+        for M in w.decode_M:
+            out.append((name, M))
+    return out
+
+
+@pytest.mark.parametrize("name,M", _decode_cases())
+def test_decode_workload(name, M):
+    w = datagen.WORKLOADS[name]
+    if w.bits == 3:
+        pytest.skip("int3 decode kernel not built yet")
+    say("decode workload", name, M)
+    W, Xc = workload_host(name)
+    s = O.scale_from_stats(O.act_stats(Xc), 0.5)
+    X = O.fold_inv_scale(datagen.decode_input(w, M), s)
+    q, sc, z = _packed(W, s, w.bits, w.group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, w.bits, w.group))
+    rows = sample_rows(w.N)
+    qo, so, zo = O.quantize_pack(W[rows], s, w.bits, w.group)
+    assert_rows_close(Y[:, rows], O.matmul(X, qo, so, zo, w.bits, w.group, w.K))
+
+
+# ---------------------------------------------------------------------------
+# W4A16 / W3A16 product: prefill kernels (and the int3 decode kernel)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (17, 130, 384), (128, 128, 512),
+                                   (200, 300, 1024), (256, 257, 4096)])
+def test_prefill_small(bits, M, N, K):
+    say("prefill", bits, M, N, K)
+    W = datagen.random_f16((N, K), 0.02, seed=3 * N + K + bits)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 5)
+    X = datagen.random_f16((M, K), 1.0, seed=M + 13)
+    q, sc, z = _packed(W, s, bits, 128)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, bits, 128, kernel=awq.KERNEL_PREFILL))
+    qo, so, zo = O.quantize_pack(W, s, bits, 128)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, bits, 128, K))
+
+
+@pytest.mark.parametrize("group", [256, 512])
+def test_prefill_int4_larger_groups(group):
+    M, N, K = 40, 96, 2048
+    W = datagen.random_f16((N, K), 0.02, seed=group + 7)
+    X = datagen.random_f16((M, K), 1.0, seed=group + 8)
+    q, sc, z = _packed(W, None, 4, group)
+    qo, so, zo = O.quantize_pack(W, None, 4, group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group))
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, group, K))
+
+
+def _prefill_cases():
+    return [(name, M) for name, w in datagen.WORKLOADS.items() for M in w.prefill_M]
+
+
+@pytest.mark.parametrize("name,M", _prefill_cases())
+def test_prefill_workload(name, M):
+    w = datagen.WORKLOADS[name]
+    say("prefill workload", name, M)
+    W, Xc = workload_host(name)
+    s = O.scale_from_stats(O.act_stats(Xc), 0.5)
+    X = O.fold_inv_scale(datagen.decode_input(w, M), s)
+    q, sc, z = _packed(W, s, w.bits, w.group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, w.bits, w.group))
+    rows = sample_rows(w.N, count=128)
+    qo, so, zo = O.quantize_pack(W[rows], s, w.bits, w.group)
+    assert_rows_close(Y[:, rows], O.matmul(X, qo, so, zo, w.bits, w.group, w.K))
+
+
+# ---------------------------------------------------------------------------
+# scale search
+# ---------------------------------------------------------------------------
+
+def check_search(W, Xc, grid, bits, group, oracle_idx=None):
+    s_g, best_g, loss_g = awq.scale_search(dev(W), dev(Xc), grid, bits, group)
+    s_g = host(s_g)
+    m = O.act_stats(Xc)
+    idx = range(len(grid)) if oracle_idx is None else sorted(set(oracle_idx) | {best_g})
+    loss_o = {i: O.layer_loss(Xc, W, O.scale_from_stats(m, grid[i]), bits, group) for i in idx}
+    for i, lo in loss_o.items():
+        assert abs(loss_g[i] - lo) <= 1e-4 * lo, (i, loss_g[i], lo)
+    assert best_g == int(np.argmin(loss_g))
+    assert np.all(loss_g[:best_g] > loss_g[best_g])
+    if oracle_idx is None:
+        best_o = min(loss_o, key=lambda i: (loss_o[i], i))
+        assert best_g == best_o or loss_o[best_g] <= (1 + 1e-4) * loss_o[best_o]
+    assert_same_bits(s_g, O.scale_from_stats(m, grid[best_g]))
+    return best_g, loss_g
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("N,K,T", [(64, 512, 64), (130, 1024, 100), (16, 128, 8)])
+def test_search_small(bits, N, K, T):
+    say("search", bits, N, K, T)
+    W, Xc, _ = datagen.small_layer(K, N, T, max(1, K // 100), 40.0, seed=N + K + T)
+    check_search(W, Xc, datagen.alpha_grid(20), bits, 128)
+
+
+def test_search_tiny_workload_full_grid():
+    w = datagen.WORKLOADS[datagen.SMALL]
+    W, Xc = workload_host(w.name)
+    best, loss = check_search(W, Xc, datagen.alpha_grid(w.n_alpha), w.bits, w.group)
+    assert loss[best] < loss[0]
+
+
+@pytest.mark.parametrize("name", [n for n in datagen.WORKLOADS if n != datagen.SMALL])
+def test_search_workload_sampled(name):
+    """Full-size search on the device; the oracle recomputes alpha = 0, the
+    device's argmin and the last grid point (each one a full float64 pass)."""
+    w = datagen.WORKLOADS[name]
+    say("search workload", name)
+    W, Xc = workload_host(name)
+    grid = datagen.alpha_grid(w.n_alpha)
+    if w.N * w.K > 50_000_000:
+        rows = sample_rows(w.N, count=2048)
+        W = W[rows]
+    check_search(W, Xc, grid, w.bits, w.group, oracle_idx=[0, len(grid) - 1])
+
+
+def test_full_pipeline_tiny():
+    """search -> quantize-pack -> fold -> decode, every step on the device."""
+    w = datagen.WORKLOADS[datagen.SMALL]
+    W, Xc = workload_host(w.name)
+    X = datagen.decode_input(w, 1)
+    grid = datagen.alpha_grid(w.n_alpha)
+    s_g, best_g, _ = awq.scale_search(dev(W), dev(Xc), grid, w.bits, w.group)
+    q, sc, z = awq.quantize_pack(dev(W), s_g, w.bits, w.group)
+    Y = host(awq.w4a16_matmul(awq.fold_inv_scale(dev(X), s_g), q, sc, z, w.bits, w.group))
+    s_o, best_o, _ = O.scale_search(W, Xc, grid, w.bits, w.group)
+    s_ref = O.scale_from_stats(O.act_stats(Xc), grid[best_g])
+    qo, so, zo = O.quantize_pack(W, s_ref, w.bits, w.group)
+    assert_same_bits(host(q), qo)
+    Yo = O.matmul(O.fold_inv_scale(X, s_ref), qo, so, zo, w.bits, w.group, w.K)
+    assert_rows_close(Y, Yo)

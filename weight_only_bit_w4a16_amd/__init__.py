@@ -1,0 +1,190 @@
+"""AWQ W4A16 hot path for MI355X: a thin binding over libawq's C ABI.
+
+The functions below only marshal arguments (dtype, device, contiguity and
+shape checks, output allocation, the current HIP stream) and call the
+library; every step of the computation runs in libawq's HIP kernels. There
+is no CPU fallback: if the library is missing or no GPU is visible the calls
+raise.
+
+Notation follows the pages: W [N, K] (row = output channel), activations
+[tokens, K], s [K] per input channel, delta/z per group of `group` codes
+along K.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._lib import AwqError, check, lib  # noqa: F401
+
+__all__ = [
+    "AwqError", "lib", "packed_words_per_row", "act_stats", "scale_candidates",
+    "quantize_pack", "fold_inv_scale", "w4a16_matmul", "scale_search",
+    "scale_search_workspace_bytes", "KERNEL_AUTO", "KERNEL_DECODE", "KERNEL_DECODE_EXACT",
+    "KERNEL_PREFILL",
+]
+
+KERNEL_AUTO, KERNEL_DECODE, KERNEL_DECODE_EXACT, KERNEL_PREFILL = 0, 1, 2, 3
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _group(K, group):
+    return K if group == -1 else group
+
+
+def packed_words_per_row(K: int, bits: int = 4, group: int = 128) -> int:
+    n = lib().awq_packed_words_per_row(K, bits, group)
+    if n == 0:
+        raise ValueError(f"unsupported (K={K}, bits={bits}, group={group})")
+    return int(n)
+
+
+def act_stats(xcal, stream=None):
+    """m[k] = mean_t |xcal[t, k]| (float64 [K])."""
+    torch = _torch()
+    _need(xcal, "xcal", torch.float16, 2)
+    T, K = xcal.shape
+    m = torch.empty(K, dtype=torch.float64, device=xcal.device)
+    check(lib().awq_act_stats(_ptr(xcal), T, K, _ptr(m), _stream(stream)), "awq_act_stats")
+    return m
+
+
+def scale_candidates(m, alpha, stream=None):
+    """s[a, k] = float32(m[k] ** alpha[a]) (float32 [n_alpha, K])."""
+    torch = _torch()
+    _need(m, "m", torch.float64, 1)
+    _need(alpha, "alpha", torch.float32, 1)
+    s = torch.empty((alpha.numel(), m.numel()), dtype=torch.float32, device=m.device)
+    check(lib().awq_scale_candidates(_ptr(m), m.numel(), _ptr(alpha), alpha.numel(), _ptr(s),
+                                     _stream(stream)), "awq_scale_candidates")
+    return s
+
+
+def quantize_pack(W, s=None, bits: int = 4, group: int = 128, out=None, stream=None):
+    """Round-to-nearest quantize-and-pack of W diag(s).
+
+    Returns (qpacked uint32-as-int32 [N, words_per_row], scales float32
+    [N, K/group], zeros uint8 [N, K/group]).
+    """
+    torch = _torch()
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    if s is not None:
+        _need(s, "s", torch.float32, 1)
+        if s.numel() != K:
+            raise ValueError("s must have K entries")
+    g = _group(K, group)
+    wpr = packed_words_per_row(K, bits, group)
+    if out is None:
+        q = torch.empty((N, wpr), dtype=torch.int32, device=W.device)
+        sc = torch.empty((N, K // g), dtype=torch.float32, device=W.device)
+        z = torch.empty((N, K // g), dtype=torch.uint8, device=W.device)
+    else:
+        q, sc, z = out
+    check(lib().awq_quantize_pack(_ptr(W), _ptr(s), N, K, bits, group, _ptr(q), _ptr(sc), _ptr(z),
+                                  _stream(stream)), "awq_quantize_pack")
+    return q, sc, z
+
+
+def fold_inv_scale(X, s, out=None, stream=None):
+    """X' = fp16(float32(X) / s) (fp16 [M, K])."""
+    torch = _torch()
+    _need(X, "X", torch.float16, 2)
+    _need(s, "s", torch.float32, 1)
+    M, K = X.shape
+    y = torch.empty_like(X) if out is None else out
+    check(lib().awq_fold_inv_scale(_ptr(X), _ptr(s), M, K, _ptr(y), _stream(stream)),
+          "awq_fold_inv_scale")
+    return y
+
+
+def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, out=None,
+                 kernel: int = KERNEL_AUTO, stream=None):
+    """Y = X' dequant(Q)^T (fp16 [M, N]) with X' already divided by s."""
+    torch = _torch()
+    _need(Xp, "Xp", torch.float16, 2)
+    _need(qpacked, "qpacked", torch.int32, 2)
+    _need(scales, "scales", torch.float32, 2)
+    _need(zeros, "zeros", torch.uint8, 2)
+    M, K = Xp.shape
+    N = qpacked.shape[0]
+    g = _group(K, group)
+    if qpacked.shape[1] != packed_words_per_row(K, bits, group):
+        raise ValueError("qpacked has the wrong row length for (K, bits, group)")
+    if tuple(scales.shape) != (N, K // g) or tuple(zeros.shape) != (N, K // g):
+        raise ValueError("scales/zeros must be [N, K/group]")
+    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
+    st = _stream(stream)
+    if kernel == KERNEL_AUTO:
+        r = lib().awq_w4a16_matmul(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M, N, K,
+                                   bits, group, _ptr(y), st)
+    else:
+        r = lib().awq_w4a16_matmul_kernel(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M,
+                                          N, K, bits, group, _ptr(y), kernel, st)
+    check(r, "awq_w4a16_matmul")
+    return y
+
+
+def scale_search_workspace_bytes(N, K, T, n_alpha, bits=4, group=128) -> int:
+    return int(lib().awq_scale_search_workspace_bytes(N, K, T, n_alpha, bits, group))
+
+
+def scale_search(W, xcal, alpha_grid=None, bits: int = 4, group: int = 128, workspace=None,
+                 stream=None):
+    """Grid search over alpha for s = mean|x| ** alpha.
+
+    Returns (s float32 [K] on the device, best index, losses float64 numpy).
+    Synchronizes the stream.
+    """
+    torch = _torch()
+    _need(W, "W", torch.float16, 2)
+    _need(xcal, "xcal", torch.float16, 2)
+    N, K = W.shape
+    T = xcal.shape[0]
+    if xcal.shape[1] != K:
+        raise ValueError("xcal must be [T, K]")
+    if alpha_grid is None:
+        alpha_grid = (np.arange(20, dtype=np.float64) / 20).astype(np.float32)
+    a = np.ascontiguousarray(np.asarray(alpha_grid, dtype=np.float32))
+    need = scale_search_workspace_bytes(N, K, T, len(a), bits, group)
+    if need == 0:
+        raise ValueError("unsupported scale_search sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
+    s = torch.empty(K, dtype=torch.float32, device=W.device)
+    losses = np.zeros(len(a), dtype=np.float64)
+    best = ctypes.c_int(-1)
+    check(lib().awq_scale_search(
+        _ptr(W), _ptr(xcal), N, K, T, a.ctypes.data_as(ctypes.c_void_p), len(a), bits, group,
+        _ptr(s), losses.ctypes.data_as(ctypes.c_void_p), ctypes.byref(best), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "awq_scale_search")
+    return s, int(best.value), losses

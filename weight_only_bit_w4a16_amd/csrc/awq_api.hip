@@ -1,0 +1,230 @@
+// C-ABI layer of libawq: argument validation (before any HIP call), device
+// check, dispatch to the kernel launchers, error mapping. Stateless.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/awq.h"
+#include "awq_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// normalise the group argument (-1 means the whole row); 0 if unsupported
+int resolve_group(int K, int group) {
+  if (group == -1) group = K;
+  if (group != 128 && group != 256 && group != 512) return 0;
+  if (K <= 0 || K % group != 0) return 0;
+  return group;
+}
+
+awq_status device_ready() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return AWQ_ERR_NO_DEVICE;
+  }
+  return AWQ_OK;
+}
+
+awq_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return AWQ_OK;
+  if (e == hipErrorNotSupported) return AWQ_ERR_UNSUPPORTED;
+  return AWQ_ERR_HIP;
+}
+
+awq_status check_group(int K, int bits, int group, int* g_out) {
+  if (bits != 3 && bits != 4) return AWQ_ERR_UNSUPPORTED;
+  if (K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (group == 0 || group < -1) return AWQ_ERR_INVALID_ARG;
+  if (group > 0 && K % group != 0) return AWQ_ERR_INVALID_ARG;
+  const int g = resolve_group(K, group);
+  if (g == 0) return AWQ_ERR_UNSUPPORTED;
+  *g_out = g;
+  return AWQ_OK;
+}
+
+awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                       const uint8_t* zeros, int M, int N, int K, int bits, int group, uint16_t* Y,
+                       void* stream, int kernel) {
+  if (!X || !qpacked || !scales || !zeros || !Y) return AWQ_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(qpacked) || !aligned16(scales) || !aligned16(zeros) ||
+      !aligned16(Y))
+    return AWQ_ERR_INVALID_ARG;
+  if (kernel < 0 || kernel > 3) return AWQ_ERR_INVALID_ARG;
+  int g = 0;
+  awq_status st = check_group(K, bits, group, &g);
+  if (st != AWQ_OK) return st;
+  if ((long long)M * K > (1LL << 31) || (long long)N * K > (1LL << 34)) return AWQ_ERR_UNSUPPORTED;
+  if ((kernel == 1 || kernel == 2) && (M > 16 || (bits == 3 && M > awq::kGemvW3MaxM)))
+    return AWQ_ERR_UNSUPPORTED;
+  if (kernel == 2 && bits == 3) return AWQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != AWQ_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const __half* x = reinterpret_cast<const __half*>(X);
+  __half* y = reinterpret_cast<__half*>(Y);
+  const bool decode =
+      kernel == 1 || kernel == 2 ||
+      (kernel == 0 && (bits == 4 ? M <= 16 : M <= awq::kGemvW3MaxM));
+  hipError_t e;
+  if (decode) {
+    if (bits == 4)
+      e = awq::launch_gemv_w4(x, qpacked, scales, zeros, M, N, K, g, y, s, kernel == 2 ? 1 : 0);
+    else
+      e = awq::launch_gemv_w3(x, qpacked, scales, zeros, M, N, K, g, y, s);
+  } else {
+    e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s);
+  }
+  return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERR_INVALID_ARG: return "AWQ_ERR_INVALID_ARG";
+    case AWQ_ERR_UNSUPPORTED: return "AWQ_ERR_UNSUPPORTED";
+    case AWQ_ERR_NO_DEVICE: return "AWQ_ERR_NO_DEVICE";
+    case AWQ_ERR_HIP: return "AWQ_ERR_HIP";
+    case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE";
+    default: return "AWQ_ERR_UNKNOWN";
+  }
+}
+
+int awq_version(void) { return 100; }
+
+size_t awq_packed_words_per_row(int K, int bits, int group) {
+  int g = 0;
+  if (check_group(K, bits, group, &g) != AWQ_OK) return 0;
+  return (size_t)awq::words_per_row(K, bits, g);
+}
+
+awq_status awq_act_stats(const uint16_t* Xcal, int T, int K, double* m, void* stream) {
+  if (!Xcal || !m) return AWQ_ERR_INVALID_ARG;
+  if (T <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (T >= 8192) return AWQ_ERR_UNSUPPORTED;
+  if (!aligned16(Xcal) || !aligned16(m)) return AWQ_ERR_INVALID_ARG;
+  awq_status st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_act_stats(reinterpret_cast<const __half*>(Xcal), T, K, m,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_scale_candidates(const double* m, int K, const float* alpha, int n_alpha, float* s,
+                                void* stream) {
+  if (!m || !alpha || !s) return AWQ_ERR_INVALID_ARG;
+  if (K <= 0 || n_alpha <= 0) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(m) || !aligned16(alpha) || !aligned16(s)) return AWQ_ERR_INVALID_ARG;
+  awq_status st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_scale_candidates(m, K, alpha, n_alpha, s,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_quantize_pack(const uint16_t* W, const float* s, int N, int K, int bits, int group,
+                             uint32_t* qpacked, float* scales, uint8_t* zeros, void* stream) {
+  if (!W || !qpacked || !scales || !zeros) return AWQ_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(qpacked) || !aligned16(scales) || !aligned16(zeros) ||
+      (s && !aligned16(s)))
+    return AWQ_ERR_INVALID_ARG;
+  int g = 0;
+  awq_status st = check_group(K, bits, group, &g);
+  if (st != AWQ_OK) return st;
+  if ((long long)N * K > (1LL << 34)) return AWQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_quant_pack(reinterpret_cast<const __half*>(W), s, N, K, bits, g,
+                                         qpacked, scales, zeros,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_fold_inv_scale(const uint16_t* X, const float* s, int M, int K, uint16_t* Xout,
+                              void* stream) {
+  if (!X || !s || !Xout) return AWQ_ERR_INVALID_ARG;
+  if (M <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (K % 8 != 0) return AWQ_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(s) || !aligned16(Xout)) return AWQ_ERR_INVALID_ARG;
+  awq_status st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_fold(reinterpret_cast<const __half*>(X), s, M, K,
+                                   reinterpret_cast<__half*>(Xout),
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_w4a16_matmul(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                            const uint8_t* zeros, int M, int N, int K, int bits, int group,
+                            uint16_t* Y, void* stream) {
+  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, 0);
+}
+
+awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                                   const uint8_t* zeros, int M, int N, int K, int bits, int group,
+                                   uint16_t* Y, int kernel, void* stream) {
+  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, kernel);
+}
+
+size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group) {
+  int g = 0;
+  if (N <= 0 || T <= 0 || T >= 8192 || n_alpha <= 0) return 0;
+  if (check_group(K, bits, group, &g) != AWQ_OK) return 0;
+  return awq::search_workspace_bytes(N, K, T, n_alpha, bits, g);
+}
+
+awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
+                            const float* alpha_grid, int n_alpha, int bits, int group, float* s_out,
+                            double* loss_out, int* best_index, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!W || !Xcalib || !alpha_grid || !s_out) return AWQ_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0 || T <= 0 || n_alpha <= 0) return AWQ_ERR_INVALID_ARG;
+  if (T >= 8192) return AWQ_ERR_UNSUPPORTED;
+  if (!aligned16(W) || !aligned16(Xcalib) || !aligned16(s_out)) return AWQ_ERR_INVALID_ARG;
+  for (int i = 0; i < n_alpha; ++i)
+    if (!(alpha_grid[i] >= 0.0f && alpha_grid[i] <= 1.0f)) return AWQ_ERR_INVALID_ARG;
+  int g = 0;
+  awq_status st = check_group(K, bits, group, &g);
+  if (st != AWQ_OK) return st;
+  const size_t need = awq::search_workspace_bytes(N, K, T, n_alpha, bits, g);
+  if (need == 0) return AWQ_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return AWQ_ERR_WORKSPACE;
+  st = device_ready();
+  if (st != AWQ_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // workspace head: alpha grid (float32), losses (float64), best index (int)
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* alpha_dev = reinterpret_cast<float*>(ws);
+  const size_t a_bytes = ((size_t)n_alpha * 4 + 255) & ~(size_t)255;
+  double* loss_dev = reinterpret_cast<double*>(ws + a_bytes);
+  const size_t l_bytes = ((size_t)n_alpha * 8 + 255) & ~(size_t)255;
+  int* best_dev = reinterpret_cast<int*>(ws + a_bytes + l_bytes);
+  void* rest = ws + a_bytes + l_bytes + 256;
+
+  hipError_t e = hipMemcpyAsync(alpha_dev, alpha_grid, (size_t)n_alpha * 4, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return AWQ_ERR_HIP;
+  e = awq::launch_search(reinterpret_cast<const __half*>(W), reinterpret_cast<const __half*>(Xcalib),
+                         N, K, T, alpha_dev, n_alpha, bits, g, rest, loss_dev, best_dev, s_out, s);
+  if (e != hipSuccess) return from_hip(e);
+  double* host_loss = loss_out;
+  int host_best = 0;
+  if (host_loss) {
+    e = hipMemcpyAsync(host_loss, loss_dev, (size_t)n_alpha * 8, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return AWQ_ERR_HIP;
+  }
+  e = hipMemcpyAsync(&host_best, best_dev, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return AWQ_ERR_HIP;
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return AWQ_ERR_HIP;
+  if (best_index) *best_index = host_best;
+  return AWQ_OK;
+}
+
+}  // extern "C"

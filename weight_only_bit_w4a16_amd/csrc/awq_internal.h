@@ -1,0 +1,48 @@
+// Internal launch interface between the C-ABI layer (awq_api.hip) and the
+// kernel translation units. Every launcher enqueues on `st` and returns the
+// launch status; shapes have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+// words of one packed group: int4 -> group/8, int3 -> ceil(group/10)
+inline int words_per_group(int bits, int group) { return bits == 4 ? group / 8 : (group + 9) / 10; }
+inline int words_per_row(int K, int bits, int group) {
+  int w = (K / group) * words_per_group(bits, group);
+  return (w + 3) & ~3;
+}
+
+hipError_t launch_act_stats(const __half* X, int T, int K, double* m, hipStream_t st);
+hipError_t launch_scale_candidates(const double* m, int K, const float* alpha, int n_alpha,
+                                   float* s, hipStream_t st);
+hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int bits, int group,
+                             uint32_t* q, float* scales, uint8_t* zeros, hipStream_t st);
+hipError_t launch_fold(const __half* X, const float* s, int M, int K, __half* Y, hipStream_t st);
+
+// decode, int4, M <= 16. variant 0 picks the fastest kernel for the shape;
+// variant 1 forces the exact-dequant kernel (kept selectable for tests).
+hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scales,
+                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st, int variant);
+// decode, int3, M <= 4
+hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scales,
+                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st);
+constexpr int kGemvW3MaxM = 0;  // int3 decode runs on the prefill kernel
+// prefill (any M)
+hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
+                       const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
+                       hipStream_t st);
+
+// scale search pieces
+size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);
+hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
+                         const float* alpha_dev, int n_alpha, int bits, int group, void* ws,
+                         double* loss_dev, int* best_dev, float* s_out, hipStream_t st);
+
+}  // namespace awq

@@ -1,0 +1,59 @@
+// Device helpers shared by the HIP kernels of libawq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp16 bit pattern of 1024.0: OR-ing a code c << e (e + bits <= 10) into its
+// mantissa gives the fp16 value 1024 + c * 2^e exactly.
+constexpr uint32_t kMagic2 = 0x64006400u;
+
+// Grid of one quantization group (asymmetric round-to-nearest, the range
+// always containing 0, "number of levels" read as 2^b - 1 steps). All
+// operations are single IEEE float32 roundings: the library is compiled with
+// -ffp-contract=off and float division is correctly rounded.
+struct GroupGrid {
+  float delta;
+  int z;
+};
+
+__device__ __forceinline__ GroupGrid group_grid(float wmin, float wmax, int qmax) {
+  const float lo = fminf(wmin, 0.0f);
+  const float hi = fmaxf(wmax, 0.0f);
+  const float r = hi - lo;
+  GroupGrid g;
+  if (r == 0.0f) {
+    g.delta = 1.0f;
+    g.z = 0;
+  } else {
+    g.delta = r / (float)qmax;
+    g.z = (int)rintf(-lo / g.delta);
+  }
+  return g;
+}
+
+// q = clamp(rint(w' / delta) + z, 0, qmax): the zero point is added after
+// rounding, as an integer.
+__device__ __forceinline__ int quant_code(float wp, GroupGrid g, int qmax) {
+  const int q = (int)rintf(wp / g.delta) + g.z;
+  return q < 0 ? 0 : (q > qmax ? qmax : q);
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+}  // namespace awq

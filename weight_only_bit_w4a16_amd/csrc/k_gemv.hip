@@ -1,0 +1,554 @@
+// Decode kernels (M <= 16 activation rows): stream the packed weights once
+// from HBM with 128-bit nontemporal loads, dequantize in registers and
+// contract on the fp16 matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// Work split. A workgroup (4 wavefronts) owns 16 output rows n; its 4
+// wavefronts split K into 4 contiguous ranges of 128-code chunks and their
+// partial sums are added in LDS in a fixed order (no atomics: the result is
+// bitwise reproducible). Inside a wavefront, lane l = nl + 16*jj owns row
+// n0 + nl and, for every chunk, the 32 consecutive codes 32*jj .. 32*jj+31
+// (one 16-byte load). The four 16x16x32 MFMAs of a chunk therefore cover
+// exactly one 128-code chunk of 16 rows, which never straddles a
+// quantization group (group is a multiple of 128), so the group step is
+// applied once per chunk to the fp32 MFMA result.
+//
+// Unpacking. For a packed word w with codes c0..c7 (c_i at bits 4i):
+//   (w & 0x000F000F) | 0x64006400 = fp16 pair (1024 + c0, 1024 + c4)
+//   (w & 0x00F000F0) | 0x64006400 = fp16 pair (1024 + 16 c1, 1024 + 16 c5)
+// and the same on w >> 8 for (c2, c6), (c3, c7): 5 integer ops per 8 codes.
+// The activation operand is permuted once per call to the same code order
+// (the contraction is a sum, so any common permutation of k is exact).
+#include "awq_internal.h"
+#include "device_common.h"
+
+namespace awq {
+
+namespace {
+
+__device__ __forceinline__ half8 as_h8(u32x4 v) { return __builtin_bit_cast(half8, v); }
+
+__device__ __forceinline__ floatx4 mfma16(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
+}
+
+// A operands in the code order of the unpacked weights, from the 32 fp16 activations
+// x[0..31] of one lane's span held as 16 dwords d[i] = (x[2i], x[2i+1]).
+// Operand (h, blk) dword p pairs x[8t + 2*sub + h] with x[8t + 2*sub + 4 + h],
+// t = 2*blk + p/2, sub = p%2; h = 0 even slots, h = 1 odd slots.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+__device__ __forceinline__ void permute_x32(const uint32_t* d, u32x4& e1, u32x4& e2, u32x4& o1,
+                                            u32x4& o2) {
+  e1 = u32x4{pair_lo(d[0], d[2]), pair_lo(d[1], d[3]), pair_lo(d[4], d[6]), pair_lo(d[5], d[7])};
+  e2 = u32x4{pair_lo(d[8], d[10]), pair_lo(d[9], d[11]), pair_lo(d[12], d[14]),
+             pair_lo(d[13], d[15])};
+  o1 = u32x4{pair_hi(d[0], d[2]), pair_hi(d[1], d[3]), pair_hi(d[4], d[6]), pair_hi(d[5], d[7])};
+  o2 = u32x4{pair_hi(d[8], d[10]), pair_hi(d[9], d[11]), pair_hi(d[12], d[14]),
+             pair_hi(d[13], d[15])};
+}
+
+__device__ __forceinline__ void load_x32(const uint16_t* p, uint32_t* d) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = q[i];
+    d[4 * i] = v[0];
+    d[4 * i + 1] = v[1];
+    d[4 * i + 2] = v[2];
+    d[4 * i + 3] = v[3];
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The decode kernel. Two forms of the per-chunk arithmetic:
+//
+// OFFSET (M <= 4): the MFMAs multiply the raw fp16 values 1024 + c (even
+// slots) and 1024 + 16 c (odd slots) with the activations; per chunk
+//   sum_k x_k (c_k - z) = D_E + D_O / 16 - C - z * S,
+//   C = 1024 * sum_even x + 64 * sum_odd x,  S = sum x,
+// with C and S computed once per call, so no per-code zero-point
+// subtraction is needed. The permuted activations, C and S live in LDS.
+//
+// EXACT (any M <= 16): every code becomes the exact fp16 integer c - z
+// before the MFMA (one packed add or fma per 2 codes); the activation
+// operands are read from global memory (L2-resident) and permuted in
+// registers.
+//
+// Schedule. The grid is sized so that every workgroup is resident at once;
+// workgroup b owns row blocks [b*rbw, b*rbw + rbw). Each wavefront walks its
+// K range for each of those row blocks as one flat sequence of chunks, with
+// a ring of PF 16-byte weight loads in flight that runs across row-block
+// boundaries. The loop body has no divergent control flow, so the compiler
+// can count outstanding loads exactly instead of draining them. A row block's
+// partial sums go to LDS; after one barrier the 4 wavefront partials are
+// added in a fixed order and stored.
+// ---------------------------------------------------------------------------
+enum { kOffset = 0, kExact = 1 };
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
+
+template <int MODE, int MP, int PF>
+__global__ __launch_bounds__(256) void gemv_w4_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
+    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
+    int rbw) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int R = MODE == kOffset ? (MP < 4 ? MP : 4) : 4;
+  const int nch = K >> 7;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
+  const int c0 = (wave * nch) >> 2;
+  const int c1 = ((wave + 1) * nch) >> 2;
+  const int nc = c1 - c0;
+  const int nl = lane & 15;
+  const int jj = lane >> 4;
+  const int nrb = (N + 15) >> 4;
+  const int rb0 = blockIdx.x * rbw;
+  const int nj = min(rbw, nrb - rb0);
+  const int ngr = nch >> gshift;
+  const int wpr = K >> 3;
+  const int xr = min(nl, (MODE == kOffset ? MP : M) - 1);  // A-operand row of this lane
+
+  const size_t xp_bytes = MODE == kOffset ? (size_t)nch * 256 * MP : 0;
+  const size_t cs_bytes = MODE == kOffset ? (size_t)nch * MP * 8 : 0;
+  u32x4* xp = reinterpret_cast<u32x4*>(smem);
+  float2* cs = reinterpret_cast<float2*>(smem + xp_bytes);
+  float* part = reinterpret_cast<float*>(smem + xp_bytes + cs_bytes);  // [rbw][4][64][R]
+
+  const uint32_t* qlane = Q + 4 * jj;
+  const int F = nj * nc;
+
+  // ---- weight prefetch ring -------------------------------------------------
+  u32x4 wb[PF];
+  float db[PF];
+  uint32_t zb[PF];
+  int pj = 0, pc = c0;  // position of the next prefetch
+  auto issue = [&](int slot) {
+    const int j = min(pj, nj - 1);
+    const int c = pj < nj ? pc : c1 - 1;
+    const int n = min((rb0 + j) * 16 + nl, N - 1);
+    wb[slot] = ld_nt(reinterpret_cast<const u32x4*>(qlane + (size_t)n * wpr + c * 16));
+    db[slot] = S[(size_t)n * ngr + (c >> gshift)];
+    zb[slot] = Z[(size_t)n * ngr + (c >> gshift)];
+    if (++pc == c1) {
+      pc = c0;
+      ++pj;
+    }
+  };
+  if (F > 0) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) issue(i);
+  }
+
+  if constexpr (MODE == kOffset) {
+    // permuted activations, C and S of this wavefront's chunks: one lane per
+    // (chunk, row, jj); the 4 jj lanes of a (chunk, row) form a quad
+    const int items = nc * M * 4;
+    for (int t = lane; t < items; t += 64) {
+      const int tj = t & 3;
+      const int rest = t >> 2;
+      const int tm = rest % M;
+      const int tc = c0 + rest / M;
+      uint32_t d[16];
+      load_x32(X + (size_t)tm * K + tc * 128 + 32 * tj, d);
+      u32x4 e1, e2, o1, o2;
+      permute_x32(d, e1, e2, o1, o2);
+      u32x4* dst = xp + ((size_t)(tc * 4 + tj) * 4) * MP + tm;
+      dst[0] = e1;
+      dst[MP] = e2;
+      dst[2 * MP] = o1;
+      dst[3 * MP] = o2;
+      float se = 0.f, so = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        se += h2f((uint16_t)(d[i] & 0xffffu));
+        so += h2f((uint16_t)(d[i] >> 16));
+      }
+      se += __shfl_xor(se, 1);
+      so += __shfl_xor(so, 1);
+      se += __shfl_xor(se, 2);
+      so += __shfl_xor(so, 2);
+      if (tj == 0) cs[tc * MP + tm] = make_float2(1024.f * se + 64.f * so, se + so);
+    }
+    __syncthreads();
+  }
+
+  const uint32_t magic = kMagic2;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint16_t* xlane = X + (size_t)xr * K + 32 * jj;
+  floatx4 y = zero4;
+  int cj = 0, cc = c0;  // position of the chunk being consumed
+  for (int f0 = 0; f0 < F; f0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const bool valid = f0 + i < F;
+      const u32x4 w = wb[i];
+      const float d = valid ? db[i] : 0.f;
+      const uint32_t z = zb[i];
+      issue(i);
+      const int c = valid ? cc : c1 - 1;
+      u32x4 a0, a1, a2, a3;
+      if constexpr (MODE == kOffset) {
+        const u32x4* p = xp + ((size_t)(c * 4 + jj) * 4) * MP + xr;
+        a0 = p[0];
+        a1 = p[MP];
+        a2 = p[2 * MP];
+        a3 = p[3 * MP];
+      } else {
+        uint32_t dx[16];
+        load_x32(xlane + c * 128, dx);
+        permute_x32(dx, a0, a1, a2, a3);
+      }
+      uint32_t e[8], o[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t x = w[t];
+        const uint32_t x8 = x >> 8;
+        e[2 * t] = and_or(x, 0x000F000Fu, magic);      // (c0, c4)
+        o[2 * t] = and_or(x, 0x00F000F0u, magic);      // (16 c1, 16 c5)
+        e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);  // (c2, c6)
+        o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);  // (16 c3, 16 c7)
+      }
+      if constexpr (MODE == kOffset) {
+        const floatx4 de = mfma16(a1, u32x4{e[4], e[5], e[6], e[7]},
+                                  mfma16(a0, u32x4{e[0], e[1], e[2], e[3]}, zero4));
+        const floatx4 dd = mfma16(a3, u32x4{o[4], o[5], o[6], o[7]},
+                                  mfma16(a2, u32x4{o[0], o[1], o[2], o[3]}, zero4));
+        const float zf = (float)z;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float2 cv = cs[c * MP + min(4 * jj + r, MP - 1)];
+          float t = __builtin_fmaf(dd[r], 0.0625f, de[r]) - cv.x;
+          t = __builtin_fmaf(-zf, cv.y, t);
+          y[r] = __builtin_fmaf(d, t, y[r]);
+        }
+      } else {
+        // exact c - z: even slots (1024 + c) - (1024 + z), odd slots
+        // (1024 + 16 c) / 16 - (64 + z)
+        const h2 ze = __builtin_bit_cast(h2, (0xE400u + z) * 0x00010001u);
+        const h2 zo = __builtin_bit_cast(h2, (0xD400u + 16u * z) * 0x00010001u);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          e[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, e[q]) + ze);
+          o[q] = __builtin_bit_cast(
+              uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, o[q]), sixteenth, zo));
+        }
+        floatx4 acc = mfma16(a0, u32x4{e[0], e[1], e[2], e[3]}, zero4);
+        acc = mfma16(a1, u32x4{e[4], e[5], e[6], e[7]}, acc);
+        acc = mfma16(a2, u32x4{o[0], o[1], o[2], o[3]}, acc);
+        acc = mfma16(a3, u32x4{o[4], o[5], o[6], o[7]}, acc);
+#pragma unroll
+        for (int r = 0; r < R; ++r) y[r] = __builtin_fmaf(d, acc[r], y[r]);
+      }
+      if (valid && cc == c1 - 1) {  // row block done: park the partial in LDS
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[((cj * 4 + wave) * 64 + lane) * R + r] = y[r];
+        y = zero4;
+      }
+      if (++cc == c1) {
+        cc = c0;
+        ++cj;
+      }
+    }
+  }
+  if (nc == 0) {
+    for (int j = 0; j < nj; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[((j * 4 + wave) * 64 + lane) * R + r] = 0.f;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nj * 64 * R; idx += 256) {
+    const int j = idx / (64 * R);
+    const int l = (idx / R) & 63;
+    const int r = idx % R;
+    const float* pp = part + (size_t)j * 4 * 64 * R + l * R + r;
+    const float v = ((pp[0] + pp[64 * R]) + pp[2 * 64 * R]) + pp[3 * 64 * R];
+    const int m = 4 * (l >> 4) + r;
+    const int n = (rb0 + j) * 16 + (l & 15);
+    if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(v));
+  }
+}
+
+namespace {
+int log2i(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+}  // namespace
+
+
+// ---------------------------------------------------------------------------
+// M = 1: one row per wavefront at a time, read as contiguous 1 KB pieces.
+//
+// A 1 KB piece of a packed row holds 16 quantization groups (2048 codes).
+// Lane l = j + 16*jj reads the 16 bytes at 64*j + 16*jj of the piece, i.e.
+// quarter jj of group j, so one dwordx4 instruction covers the piece
+// contiguously. In the 16x16x32 MFMA the 16 B-columns are then the 16 groups
+// of the piece and the 16 A-rows are the activations of those same 16
+// groups (lane (m, jj) holds the activations of quarter jj of group m), so
+// the diagonal entry D[j][j] is the dot product of group j with its
+// activations; the off-diagonal entries are not used. It sits in lane
+// j + 16*(j/4), register j%4.
+//
+// Offset form: the B operands are the raw fp16 values 1024 + c (even code
+// slots) and 1024 + 16 c (odd slots); the odd-slot activations are stored
+// pre-multiplied by 1/16 (exact unless they fall below the fp16 normal
+// range), so all four MFMAs of a piece accumulate into one D and, per group,
+//   sum_k x'_k c_k - z * S = D - (C + z * S),
+//   C = 1024 * sum_k x'_k,  S = sum_k x''_k,
+// where x' is the stored operand and x'' = x' (even) or 16 x' (odd).
+// The activation operands of all pieces depend only on k: they are prepared
+// once per workgroup in LDS and shared by its 4 wavefronts, which stream
+// different rows.
+// ---------------------------------------------------------------------------
+template <int SP, int RPF, bool FULL>
+__global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
+    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int gshift) {
+  __shared__ u32x4 xs[SP][4][64];  // [piece][operand][lane]
+  __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wave;
+  const int NW = gridDim.x * 4;
+  const int j = lane & 15;
+  const int jj = lane >> 4;
+  const int nch = K >> 7;  // groups of 128 codes per row; SP = ceil(nch / 16)
+  const int ngr = nch >> gshift;
+  const int wpr = K >> 3;
+  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int rdiag = j & 3;
+  const bool diag = jj == (j >> 2);
+
+  // this lane's group in every piece; without FULL the last piece may be
+  // partial: its missing groups read a valid group and get weight 0
+  int goff[SP];
+  bool gval[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    gval[s] = FULL || 16 * s + j < nch;
+    goff[s] = FULL ? 16 * s + j : min(16 * s + j, nch - 1);
+  }
+
+  // operand prep: thread (piece s, lane l) of the workgroup permutes the
+  // activations of quarter l/16 of group 16 s + l%16
+  for (int t = threadIdx.x; t < SP * 64; t += 256) {
+    const int ps = t >> 6, pl = t & 63;
+    const int g = min(16 * ps + (pl & 15), nch - 1);
+    uint32_t d[16];
+    load_x32(X + g * 128 + 32 * (pl >> 4), d);
+    // odd slots: x / 16 rounded to fp16
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float od = h2f((uint16_t)(d[i] >> 16)) * 0.0625f;
+      d[i] = (d[i] & 0xffffu) | ((uint32_t)__half_as_ushort(__float2half_rn(od)) << 16);
+    }
+    u32x4 o0, o1, o2, o3;
+    permute_x32(d, o0, o1, o2, o3);
+    xs[ps][0][pl] = o0;
+    xs[ps][1][pl] = o1;
+    xs[ps][2][pl] = o2;
+    xs[ps][3][pl] = o3;
+    float se = 0.f, so = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      se += h2f((uint16_t)(d[i] & 0xffffu));
+      so += h2f((uint16_t)(d[i] >> 16));
+    }
+    se += __shfl_xor(se, 16);
+    so += __shfl_xor(so, 16);
+    se += __shfl_xor(se, 32);
+    so += __shfl_xor(so, 32);
+    if (pl < 16) xcs[ps][pl] = make_float2(1024.f * (se + so), se + 16.f * so);
+  }
+  __syncthreads();
+  float cC[SP], cS[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    const float2 v = xcs[s][j];
+    cC[s] = v.x;
+    cS[s] = v.y;
+  }
+
+  // Ring of RPF rows x SP pieces. There are no prologue loads: the loop
+  // starts RPF rows early with an empty ring, so every load of the ring is
+  // issued at the end of an iteration and consumed one iteration later. (With
+  // prologue loads the compiler merges the two loads feeding the loop phi
+  // into one load at the top of the loop, which then waits for its data.)
+  u32x4 wb[RPF][SP];
+  float db[RPF][SP];
+  uint32_t zb[RPF][SP];
+#pragma unroll
+  for (int r = 0; r < RPF; ++r)
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      wb[r][s] = u32x4{0, 0, 0, 0};
+      db[r][s] = 0.f;
+      zb[r][s] = 0u;
+    }
+  const int last = max(cnt - 1, 0);
+  const uint32_t magic = kMagic2;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* qlane = Q + 16 * j + 4 * jj;
+  float outv = 0.f;
+  for (int i0 = -RPF; i0 < cnt; i0 += RPF) {
+#pragma unroll
+    for (int r = 0; r < RPF; ++r) {
+      const int row = i0 + r;
+      const size_t nn = (size_t)min(gw + min(row + RPF, last) * NW, N - 1);  // refill target
+      // keep the rows in program order, so that each row waits only for its
+      // own slots and the other RPF - 1 rows' loads stay in flight
+      __builtin_amdgcn_sched_barrier(0);
+      if (row >= 0) {  // uniform
+        const bool vrow = row < cnt;
+        float y = 0.f;
+#pragma unroll
+        for (int s = 0; s < SP; ++s) {
+          const u32x4 w = wb[r][s];
+          const float d = (vrow && gval[s]) ? db[r][s] : 0.f;
+          const float zs = __builtin_fmaf((float)zb[r][s], cS[s], cC[s]);
+          uint32_t e[8], o[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t x = w[t];
+            const uint32_t x8 = x >> 8;
+            e[2 * t] = and_or(x, 0x000F000Fu, magic);
+            o[2 * t] = and_or(x, 0x00F000F0u, magic);
+            e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
+            o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
+          }
+          floatx4 acc = mfma16(xs[s][0][lane], u32x4{e[0], e[1], e[2], e[3]}, zero4);
+          acc = mfma16(xs[s][1][lane], u32x4{e[4], e[5], e[6], e[7]}, acc);
+          acc = mfma16(xs[s][2][lane], u32x4{o[0], o[1], o[2], o[3]}, acc);
+          acc = mfma16(xs[s][3][lane], u32x4{o[4], o[5], o[6], o[7]}, acc);
+          float v = acc[0];
+          v = rdiag == 1 ? acc[1] : v;
+          v = rdiag == 2 ? acc[2] : v;
+          v = rdiag == 3 ? acc[3] : v;
+          y = __builtin_fmaf(d, v - zs, y);
+        }
+        // row done: the 16 diagonal lanes are quads 0 (lanes 0-3), 5, 10 and
+        // 15 (lanes 60-63); add within quads with DPP, then the 4 quads
+        float v = diag ? y : 0.f;
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+        const float sum =
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
+        outv = (row & 63) == lane ? sum : outv;
+      }
+      // refill the slots with the same pieces of the row RPF ahead
+      const uint32_t* qn = qlane + nn * wpr;
+      const float* sn = S + nn * ngr;
+      const uint8_t* zn = Z + nn * ngr;
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        wb[r][s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
+        db[r][s] = sn[goff[s] >> gshift];
+        zb[r][s] = zn[goff[s] >> gshift];
+      }
+      // A no-op (wavefront-scope) fence after the loads: a memory-writing
+      // instruction between the loads and the loop back edge keeps the
+      // compiler from merging them with the other loads that feed the ring.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    }
+  }
+  if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
+}
+
+constexpr int kGemvPF = 8;
+constexpr int kGemvMaxRbw = 8;
+
+hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scales,
+                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st, int variant) {
+  const int gshift = log2i(group / 128);
+  const int nrb = (N + 15) / 16;
+  const int nch = K / 128;
+  // all workgroups resident at once: ~3 per CU at this register budget
+  const int cap = 3 * cu_count();
+  int rbw = (nrb + cap - 1) / cap;
+  if (rbw > kGemvMaxRbw) rbw = kGemvMaxRbw;
+  const dim3 grid((nrb + rbw - 1) / rbw), block(256);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  if (variant == 0 && M == 1) {
+    const int sp = (nch + 15) / 16;
+    // wavefronts: all resident at ~2 per SIMD, and at most 64 rows each
+    const int nw = max(cu_count() * 8, (N + 63) / 64);
+    const dim3 g1((unsigned)((min(N, nw) + 3) / 4));
+    const bool full = nch % 16 == 0;
+#define AWQ_M1(SM, RP)                                                                          \
+  do {                                                                                          \
+    if (full)                                                                                   \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true>), g1, block, 0, st, x, q, scales,     \
+                         zeros, y, N, K, gshift);                                               \
+    else                                                                                        \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false>), g1, block, 0, st, x, q, scales,    \
+                         zeros, y, N, K, gshift);                                               \
+  } while (0)
+    switch (sp) {
+      case 1: AWQ_M1(1, 4); break;
+      case 2: AWQ_M1(2, 2); break;
+      case 3: AWQ_M1(3, 2); break;
+      case 4: AWQ_M1(4, 1); break;
+      case 5: AWQ_M1(5, 1); break;
+      case 6: AWQ_M1(6, 1); break;
+      default: break;
+    }
+#undef AWQ_M1
+    if (sp <= 6) return hipGetLastError();
+  }
+  if (variant == 0 && M <= 4) {
+    const int mp = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const int r = mp < 4 ? mp : 4;
+    const size_t lds = (size_t)nch * 256 * mp + (size_t)nch * mp * 8 + (size_t)rbw * 4 * 64 * r * 4;
+    if (lds <= 64 * 1024) {
+#define AWQ_GV(MPV)                                                                            \
+  hipLaunchKernelGGL((gemv_w4_kernel<kOffset, MPV, kGemvPF>), grid, block, lds, st, x, q, scales, \
+                     zeros, y, M, N, K, gshift, rbw)
+      if (mp == 1) AWQ_GV(1);
+      else if (mp == 2) AWQ_GV(2);
+      else AWQ_GV(4);
+#undef AWQ_GV
+      return hipGetLastError();
+    }
+  }
+  const size_t lds = (size_t)rbw * 4 * 64 * 4 * 4;
+  hipLaunchKernelGGL((gemv_w4_kernel<kExact, 16, kGemvPF>), grid, block, lds, st, x, q, scales,
+                     zeros, y, M, N, K, gshift, rbw);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -1,0 +1,207 @@
+// Quantize-and-pack, activation statistic, scale candidates and the fold of
+// diag(s)^-1 into the activation. These are the HBM-bound "offline" kernels
+// that feed the W4A16 product.
+#include "awq_internal.h"
+#include "device_common.h"
+
+namespace awq {
+
+// ---------------------------------------------------------------------------
+// Round-to-nearest quantize-and-pack.
+// One thread owns 8 consecutive codes of one group; the TPG = group/8
+// threads of a group sit in one wavefront and reduce min/max with shuffles.
+// int4: each thread writes its own packed word. int3: each thread folds its
+// 8 codes into 24 bits; thread w of the group gathers the 24-bit blocks that
+// cover codes 10w..10w+9 from its neighbours and writes word w.
+// ---------------------------------------------------------------------------
+template <int BITS, int TPG>
+__global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ W,
+                                                         const float* __restrict__ s, int K,
+                                                         uint32_t* __restrict__ Q,
+                                                         float* __restrict__ scales,
+                                                         uint8_t* __restrict__ zeros, int wpr,
+                                                         long total_groups) {
+  constexpr int G = TPG * 8;
+  constexpr int QMAX = (1 << BITS) - 1;
+  const int ng = K / G;
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long gi_raw = gid / TPG;
+  const int j = (int)(gid % TPG);
+  const bool active = gi_raw < total_groups;
+  // inactive threads work on a valid group so every lane joins the shuffles
+  const long gi = active ? gi_raw : total_groups - 1;
+  const long n = gi / ng;
+  const int g = (int)(gi % ng);
+  const int k0 = g * G + 8 * j;
+
+  const uint4 raw = *reinterpret_cast<const uint4*>(W + n * K + k0);
+  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+  float wp[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wp[2 * i] = h2f((uint16_t)(rw[i] & 0xffffu));
+    wp[2 * i + 1] = h2f((uint16_t)(rw[i] >> 16));
+  }
+  if (s != nullptr) {
+    const float4 s0 = *reinterpret_cast<const float4*>(s + k0);
+    const float4 s1 = *reinterpret_cast<const float4*>(s + k0 + 4);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wp[i] = wp[i] * sv[i];
+  }
+  float mn = wp[0], mx = wp[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fminf(mn, wp[i]);
+    mx = fmaxf(mx, wp[i]);
+  }
+#pragma unroll
+  for (int off = 1; off < TPG; off <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, TPG));
+    mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
+  }
+  const GroupGrid gg = group_grid(mn, mx, QMAX);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed |= (uint32_t)quant_code(wp[i], gg, QMAX) << (BITS * i);
+
+  uint32_t* qrow = Q + n * wpr;
+  if (BITS == 4) {
+    if (active) qrow[g * (G / 8) + j] = packed;
+  } else {
+    constexpr int WPG = (G + 9) / 10;
+    // word w holds codes 10w .. 10w+9, which lie in the 8-code blocks t1, t1+1
+    const int w = j;
+    const int t1 = (10 * w) >> 3;
+    const uint32_t lo24 = __shfl(packed, t1 < TPG ? t1 : TPG - 1, TPG);
+    const uint32_t hi24 = __shfl(packed, t1 + 1 < TPG ? t1 + 1 : TPG - 1, TPG);
+    const uint64_t both = (uint64_t)lo24 | ((uint64_t)(t1 + 1 < TPG ? hi24 : 0u) << 24);
+    const int first = 10 * w - 8 * t1;          // code offset inside block t1
+    const int left = G - 10 * w;  // codes of this group from slot 0 of word w on
+    const int count = left < 0 ? 0 : (left < 10 ? left : 10);
+    uint32_t word = (uint32_t)(both >> (3 * first));
+    word &= count >= 10 ? 0x3fffffffu : ((1u << (3 * count)) - 1u);
+    if (active) {
+      if (w < WPG) {
+        qrow[g * WPG + w] = word;
+      } else if (g == ng - 1 && g * WPG + w < wpr) {
+        qrow[g * WPG + w] = 0u;  // row padding to 16 bytes
+      }
+    }
+  }
+  if (active && j == 0) {
+    scales[n * ng + g] = gg.delta;
+    zeros[n * ng + g] = (uint8_t)gg.z;
+  }
+}
+
+hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int bits, int group,
+                             uint32_t* q, float* scales, uint8_t* zeros, hipStream_t st) {
+  const int wpr = words_per_row(K, bits, group);
+  const long total = (long)N * (K / group);
+  const long threads = total * (group / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const uint16_t* w = reinterpret_cast<const uint16_t*>(W);
+#define AWQ_QP(B, T)                                                                        \
+  hipLaunchKernelGGL((quant_pack_kernel<B, T>), grid, dim3(256), 0, st, w, s, K, q, scales, \
+                     zeros, wpr, total)
+  if (bits == 4) {
+    if (group == 128) AWQ_QP(4, 16);
+    else if (group == 256) AWQ_QP(4, 32);
+    else AWQ_QP(4, 64);
+  } else {
+    if (group == 128) AWQ_QP(3, 16);
+    else if (group == 256) AWQ_QP(3, 32);
+    else AWQ_QP(3, 64);
+  }
+#undef AWQ_QP
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// X' = fp16(float32(X) / s), 8 elements per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fold_kernel(const uint16_t* __restrict__ X,
+                                                   const float* __restrict__ s, int K, long total8,
+                                                   uint16_t* __restrict__ Y) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total8) return;
+  const long e = i * 8;
+  const int k = (int)(e % K);
+  const uint4 raw = *reinterpret_cast<const uint4*>(X + e);
+  const float4 s0 = *reinterpret_cast<const float4*>(s + k);
+  const float4 s1 = *reinterpret_cast<const float4*>(s + k + 4);
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = h2f((uint16_t)(rw[p] & 0xffffu)) / sv[2 * p];
+    const float b = h2f((uint16_t)(rw[p] >> 16)) / sv[2 * p + 1];
+    out[p] = (uint32_t)__half_as_ushort(__float2half_rn(a)) |
+             ((uint32_t)__half_as_ushort(__float2half_rn(b)) << 16);
+  }
+  *reinterpret_cast<uint4*>(Y + e) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+hipError_t launch_fold(const __half* X, const float* s, int M, int K, __half* Y, hipStream_t st) {
+  const long total8 = (long)M * K / 8;
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(X), s, K, total8,
+                     reinterpret_cast<uint16_t*>(Y));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// m[k] = sum_t |x[t,k]| / T in float64. The fp16 sum is exact in float64
+// for T < 8192, so the split over 4 token slices does not change the result.
+// Block = 64 columns x 4 token slices.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void act_stats_kernel(const uint16_t* __restrict__ X, int T,
+                                                        int K, double* __restrict__ m) {
+  __shared__ double part[4][64];
+  const int c = threadIdx.x & 63;
+  const int slice = threadIdx.x >> 6;
+  const int k = blockIdx.x * 64 + c;
+  double acc = 0.0;
+  if (k < K) {
+    for (int t = slice; t < T; t += 4) acc += fabs((double)h2f(X[(long)t * K + k]));
+  }
+  part[slice][c] = acc;
+  __syncthreads();
+  if (slice == 0 && k < K) {
+    const double sum = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    m[k] = sum / (double)T;
+  }
+}
+
+hipError_t launch_act_stats(const __half* X, int T, int K, double* m, hipStream_t st) {
+  hipLaunchKernelGGL(act_stats_kernel, dim3((K + 63) / 64), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(X), T, K, m);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// s[a, k] = float32(pow(m[k], alpha[a])) with pow in float64; 1 where m == 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void scale_candidates_kernel(const double* __restrict__ m, int K,
+                                                               const float* __restrict__ alpha,
+                                                               int n_alpha,
+                                                               float* __restrict__ s) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)K * n_alpha) return;
+  const int a = (int)(i / K);
+  const int k = (int)(i % K);
+  const double mk = m[k];
+  s[i] = mk > 0.0 ? (float)pow(mk, (double)alpha[a]) : 1.0f;
+}
+
+hipError_t launch_scale_candidates(const double* m, int K, const float* alpha, int n_alpha,
+                                   float* s, hipStream_t st) {
+  const long total = (long)K * n_alpha;
+  hipLaunchKernelGGL(scale_candidates_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     st, m, K, alpha, n_alpha, s);
+  return hipGetLastError();
+}
+
+}  // namespace awq
