@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ W4A16 hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input for
+the LLaMA-70B-shaped MLP slice (K=8192 in, N=28672 out, int4, group 128):
+
+  scale search (activation statistic, 20 scale candidates, fake-quant error
+  and layer-output loss per candidate, argmin) on 512 calibration tokens
+  -> quantize-and-pack W diag(s) -> fold diag(s)^-1 into X (M=1 and M=2048)
+  -> prefill W4A16 GEMM at M=2048 -> decode W4A16 GEMV at M=1.
+
+The decode GEMV runs on R independent copies of the packed weights
+(R * 126.7 MB > the 256 MB Infinity Cache) so every call streams from HBM.
+`value` is the decode GEMV's effective HBM bandwidth: algorithmic bytes per
+call (packed codes + fp32 scales + uint8 zeros + X' + Y) divided by the mean
+kernel time, taken with HIP events on the stream the kernels run on around a
+batch of back-to-back calls (per-call event times are reported beside it).
+The prefill GEMM is reported as TFLOP/s against the fp16 MFMA peak.
+
+Prints one JSON line. `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+FP16_MFMA_PEAK_TF = 2500.0  # MI355X dense fp16 matrix, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="approximate budget for the oracle's timed sample")
+    return p.parse_args()
+
+
+def cpu_baseline(w, W, Xc, s_np, budget_s):
+    """The oracle, as it stands, on the host cores: the decode product on a
+    sample of output rows (same unit as `value`), plus the pack step."""
+    import numpy as np
+    from oracle import awq_oracle as O
+    import datagen
+
+    cores = len(os.sched_getaffinity(0))
+    X1 = O.fold_inv_scale(datagen.decode_input(w, 1), s_np)
+    rows = 256
+    t0 = time.perf_counter()
+    qp, sc, z = O.quantize_pack(W[:rows], s_np, w.bits, w.group)
+    t_pack = time.perf_counter() - t0
+    wpr = qp.shape[1]
+    # grow the sample until it takes about the budget
+    done_rows, t_mm = 0, 0.0
+    chunk = rows
+    while t_mm < budget_s and done_rows < w.N:
+        lo = done_rows
+        chunk = min(chunk, w.N - lo)
+        qpc, scc, zc = O.quantize_pack(W[lo:lo + chunk], s_np, w.bits, w.group)
+        t0 = time.perf_counter()
+        O.matmul(X1, qpc, scc, zc, w.bits, w.group, w.K)
+        t_mm += time.perf_counter() - t0
+        done_rows += chunk
+        chunk = min(chunk * 2, 4096)
+    per_row_bytes = wpr * 4 + (w.K // w.group) * 5 + 2  # codes + scales + zeros + y
+    byt = done_rows * per_row_bytes + 2 * w.K
+    return {
+        "value": round(byt / t_mm / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"oracle.matmul (float64, numpy BLAS) at M=1 over {done_rows} of {w.N} "
+                   f"output rows of {w.name}; oracle.quantize_pack of {rows} rows took "
+                   f"{t_pack:.2f} s ({rows * w.K * 2 / t_pack / 1e9:.3f} GB/s of fp16 W)"),
+        "threads_env": os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this hot path runs on one GPU; --gpus must be 1 "
+              "(multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import weight_only_bit_w4a16_amd as awq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = datagen.WORKLOADS[args.workload or datagen.HEADLINE]
+    M_dec = 1
+    M_pre = w.prefill_M[0] if w.prefill_M else 2048
+
+    # ---- synthetic inputs (seeded), resident in HBM before timing ----------
+    W_np = datagen.weight(w)
+    Xc_np = datagen.calibration(w)
+    X1_np = datagen.decode_input(w, M_dec)
+    Xp_np = datagen.decode_input(w, M_pre)
+    W = torch.from_numpy(W_np).to(dev)
+    Xc = torch.from_numpy(Xc_np).to(dev)
+    X1 = torch.from_numpy(X1_np).to(dev)
+    Xp = torch.from_numpy(Xp_np).to(dev)
+    grid = datagen.alpha_grid(w.n_alpha)
+    ws = torch.empty(awq.scale_search_workspace_bytes(w.N, w.K, w.T, len(grid), w.bits, w.group),
+                     dtype=torch.uint8, device=dev)
+    wpr = awq.packed_words_per_row(w.K, w.bits, w.group)
+    ng = w.K // w.group
+    packed_bytes = w.N * wpr * 4 + w.N * ng * 5
+    R = max(2, int(np.ceil(512 * 2**20 / packed_bytes)))
+    copies = [(torch.empty((w.N, wpr), dtype=torch.int32, device=dev),
+               torch.empty((w.N, ng), dtype=torch.float32, device=dev),
+               torch.empty((w.N, ng), dtype=torch.uint8, device=dev)) for _ in range(R)]
+    X1f = torch.empty_like(X1)
+    Xpf = torch.empty_like(Xp)
+    Y1 = torch.empty((M_dec, w.N), dtype=torch.float16, device=dev)
+    Yp = torch.empty((M_pre, w.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    rec = {"search": [], "pack": [], "fold": [], "prefill": [], "decode": [], "decode_batch": []}
+
+    def step(i, timed):
+        e = {k: (ev(), ev()) for k in ("search", "pack", "fold", "prefill")}
+        e["search"][0].record(stream)
+        s, best, _ = awq.scale_search(W, Xc, grid, w.bits, w.group, workspace=ws)
+        e["search"][1].record(stream)
+        dst = copies[i % R]
+        e["pack"][0].record(stream)
+        awq.quantize_pack(W, s, w.bits, w.group, out=dst)
+        e["pack"][1].record(stream)
+        e["fold"][0].record(stream)
+        awq.fold_inv_scale(X1, s, out=X1f)
+        awq.fold_inv_scale(Xp, s, out=Xpf)
+        e["fold"][1].record(stream)
+        e["prefill"][0].record(stream)
+        awq.w4a16_matmul(Xpf, *dst, w.bits, w.group, out=Yp)
+        e["prefill"][1].record(stream)
+        # decode on every copy but the one just written (cold in the caches):
+        # one event pair per call, and one around the back-to-back batch
+        dec = []
+        ba, bb = ev(), ev()
+        ba.record(stream)
+        for r in range(1, R):
+            q = copies[(i + r) % R]
+            a, b = ev(), ev()
+            a.record(stream)
+            awq.w4a16_matmul(X1f, *q, w.bits, w.group, out=Y1)
+            b.record(stream)
+            dec.append((a, b))
+        bb.record(stream)
+        if timed:
+            for k in e:
+                rec[k].append(e[k])
+            rec["decode"].extend(dec)
+            rec["decode_batch"].append((ba, bb))
+        return best
+
+    # fill every copy once, then warm up
+    s0, _, _ = awq.scale_search(W, Xc, grid, w.bits, w.group, workspace=ws)
+    for dst in copies:
+        awq.quantize_pack(W, s0, w.bits, w.group, out=dst)
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        best = step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def mean_ms(k):
+        v = [a.elapsed_time(b) for a, b in rec[k]]
+        return float(np.mean(v)), float(np.min(v))
+
+    dec_call_ms, dec_min = mean_ms("decode")
+    dec_ms = mean_ms("decode_batch")[0] / (R - 1)
+    pre_ms, pre_min = mean_ms("prefill")
+    search_ms, _ = mean_ms("search")
+    pack_ms, _ = mean_ms("pack")
+    fold_ms, _ = mean_ms("fold")
+
+    dec_bytes = packed_bytes + 2 * M_dec * w.K + 2 * M_dec * w.N
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    pre_flops = 2.0 * M_pre * w.N * w.K
+    pre_tfs = pre_flops / (pre_ms * 1e-3) / 1e12
+    pack_bytes = w.N * w.K * 2 + packed_bytes + w.K * 4
+    search_flops = 2.0 * 2 * w.T * w.N * w.K * len(grid)  # hi and lo parts
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "decode_gemv_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            t = json.load(f)
+        if t.get("workload") == w.name and t.get("kernel_source_sha") == kernel_sha():
+            traffic = t.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": "W4A16 GEMV effective HBM GB/s (% peak) at M=1; prefill GEMM TFLOP/s (% MFMA)",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% outlier channels x50)",
+        "config": {
+            "workload": w.name, "K": w.K, "N": w.N, "bits": w.bits, "group": w.group,
+            "decode_M": M_dec, "prefill_M": M_pre, "calib_tokens": w.T, "alpha_grid": len(grid),
+            "weight_copies_rotated": R,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "decode GEMV (M=1)", "bytes_per_launch": dec_bytes,
+            "mean_us": round(dec_ms * 1e3, 2), "per_call_event_mean_us": round(dec_call_ms * 1e3, 2),
+            "per_call_event_min_us": round(dec_min * 1e3, 2),
+        },
+        "roofline_prefill": {
+            "bound": "mfma", "achieved": round(pre_tfs, 1), "peak": FP16_MFMA_PEAK_TF,
+            "unit": "TFLOP/s", "frac": round(pre_tfs / FP16_MFMA_PEAK_TF, 4),
+            "kernel": f"prefill GEMM (M={M_pre})", "flops_per_launch": pre_flops,
+            "mean_us": round(pre_ms * 1e3, 1),
+        },
+        "rows": {
+            "scale_search_ms": round(search_ms, 3),
+            "scale_search_tflops": round(search_flops / (search_ms * 1e-3) / 1e12, 1),
+            "best_alpha_index": int(best),
+            "quantize_pack_us": round(pack_ms * 1e3, 1),
+            "quantize_pack_gbs": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),
+            "fold_us": round(fold_ms * 1e3, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, W_np, Xc_np, s0.cpu().numpy(), args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def kernel_sha():
+    import hashlib
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "weight_only_bit_w4a16_amd", "csrc", "k_gemv.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

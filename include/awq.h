@@ -161,9 +161,10 @@ size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bi
  * [n_alpha] (values in [0, 1]); s_out: dev float32 [K]; loss_out: host
  * float64 [n_alpha] (may be NULL); best_index: host int (may be NULL);
  * workspace: dev, at least awq_scale_search_workspace_bytes(...) bytes.
- * The losses are computed with float32 products of fp16-rounded error
- * terms and float64 sums; they agree with an exact evaluation to about
- * 1e-5 relative. Synchronizes `stream` before returning. */
+ * The error terms are split into fp16 hi and lo parts and contracted on the
+ * fp16 matrix cores with float32 accumulation, tile sums in float64; the
+ * losses agree with an exact evaluation to about 1e-6 relative.
+ * Synchronizes `stream` before returning. */
 awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
                             const float* alpha_grid, int n_alpha, int bits, int group, float* s_out,
                             double* loss_out, int* best_index, void* workspace,

@@ -114,7 +114,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict_
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   const int m0 = (t % mt) * BM;
   const int n0 = (t / mt) * BN;
-  const int nsteps = K >> 7;
+  // fp16 B (the search) holds each error term as a hi and a lo fp16 part,
+  // [N][2K] with chunk c = (hi of k-chunk c/2 | lo of k-chunk c/2): 2 steps
+  // per 128-wide k-chunk, both against the same activation chunk
+  const int nsteps = BMODE == 0 ? 2 * (K >> 7) : K >> 7;
 
   if (BMODE == 3) {
     // zero the slots 130..143 of every row once; they are never written again
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict_
 
   Stage<BMODE> st;
   auto load_step = [&](int ks) {
-    const int k0 = ks << 7;
+    const int k0 = BMODE == 0 ? (ks >> 1) << 7 : ks << 7;
     if constexpr (BMODE == 0 || BMODE == 4) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict_
         const int id = tid + NT * i;
         const int r = id >> 4, c8 = id & 15;
         const int n = min(n0 + r, N - 1);
-        st.b[i] = *reinterpret_cast<const u32x4*>(B + (size_t)n * K + k0 + 8 * c8);
+        st.b[i] = *reinterpret_cast<const u32x4*>(B + (size_t)n * 2 * K + (ks << 7) + 8 * c8);
       }
     } else if constexpr (BMODE == 4) {
       const uint32_t* Q = static_cast<const uint32_t*>(Bsrc);
@@ -357,7 +360,8 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   return hipGetLastError();
 }
 
-// sum over the tile grid of ||A B^T||^2 partials, one double per workgroup
+// ||A (Bhi + Blo)^T||^2 as one float64 partial per workgroup tile; A is
+// [M, K] fp16, B is [N, 2K] fp16 holding hi/lo parts per 128-wide k chunk
 hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K,
                              double* partial, hipStream_t st) {
   const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));

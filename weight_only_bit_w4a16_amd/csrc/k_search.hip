@@ -2,7 +2,8 @@
 //
 // For every alpha of the grid:
 //   s      = scale candidates (float32, one per input channel)
-//   D      = W - Q(W diag(s)) diag(s)^-1        (fake-quant error, fp16 [N, K])
+//   D      = W - Q(W diag(s)) diag(s)^-1        (fake-quant error, as hi + lo
+//                                                 fp16 parts, [N, 2K])
 //   loss   = || Xcal D^T ||_F^2                  (fp16 MFMA contraction,
 //                                                 float32 tile sums, float64
 //                                                 across tiles)
@@ -61,20 +62,32 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
     mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
   }
   const GroupGrid gg = group_grid(mn, mx, QMAX);
-  uint32_t out[4];
+  // D = hi + lo with hi = fp16(D), lo = fp16(D - hi): about 22 significant
+  // bits, so the fp16 contraction of both parts is accurate to ~1e-6
+  uint32_t hi[4], lo[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    uint32_t h[2];
+    uint32_t h[2], l[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int i = 2 * p + e;
       const int q = quant_code(wp[i], gg, QMAX);
       const float back = ((float)(q - gg.z) * gg.delta) / sv[i];
-      h[e] = __half_as_ushort(__float2half_rn(w[i] - back));
+      const float dv = w[i] - back;
+      const __half dh = __float2half_rn(dv);
+      h[e] = __half_as_ushort(dh);
+      l[e] = __half_as_ushort(__float2half_rn(dv - __half2float(dh)));
     }
-    out[p] = h[0] | (h[1] << 16);
+    hi[p] = h[0] | (h[1] << 16);
+    lo[p] = l[0] | (l[1] << 16);
   }
-  if (active) *reinterpret_cast<uint4*>(D + n * K + k0) = make_uint4(out[0], out[1], out[2], out[3]);
+  if (active) {
+    // row n of D is [2K]: k-chunk c (128 wide) -> hi at 256c, lo at 256c + 128
+    const int c = k0 >> 7, off = k0 & 127;
+    uint16_t* row = D + n * 2 * K + 256 * c + off;
+    *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(row + 128) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
 }
 
 // loss[a] = sum of the tile partials of alpha a, in a fixed order
@@ -116,7 +129,7 @@ Layout layout(int N, int K, int T, int n_alpha) {
   L.m = 0;
   L.s_all = L.m + align256((size_t)K * 8);
   L.d = L.s_all + align256((size_t)n_alpha * K * 4);
-  L.partial = L.d + align256((size_t)N * K * 2);
+  L.partial = L.d + align256((size_t)N * K * 4);  // hi and lo fp16 parts
   L.total = L.partial + align256((size_t)n_alpha * sqnorm_abt_tiles(T, N) * 8);
   return L;
 }
