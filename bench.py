@@ -14,7 +14,8 @@ The decode GEMV runs on R independent copies of the packed weights
 `value` is the decode GEMV's effective HBM bandwidth: algorithmic bytes per
 call (packed codes + fp32 scales + uint8 zeros + X' + Y) divided by the mean
 kernel time, taken with HIP events on the stream the kernels run on around a
-batch of back-to-back calls (per-call event times are reported beside it).
+batch of back-to-back calls (per-call event times, which add the event
+overhead to every call, are reported beside it).
 The prefill GEMM is reported as TFLOP/s against the fp16 MFMA peak.
 
 Prints one JSON line. `--gpus N` with N > 1 exits: this path runs on one GPU.
@@ -150,24 +151,27 @@ def main():
         e["prefill"][0].record(stream)
         awq.w4a16_matmul(Xpf, *dst, w.bits, w.group, out=Yp)
         e["prefill"][1].record(stream)
-        # decode on every copy but the one just written (cold in the caches):
-        # one event pair per call, and one around the back-to-back batch
+        # decode on every copy but the one just written (cold in the caches),
+        # back to back between one event pair; odd steps also time each call
         dec = []
         ba, bb = ev(), ev()
         ba.record(stream)
         for r in range(1, R):
             q = copies[(i + r) % R]
-            a, b = ev(), ev()
-            a.record(stream)
+            if i % 2:
+                a, b = ev(), ev()
+                a.record(stream)
             awq.w4a16_matmul(X1f, *q, w.bits, w.group, out=Y1)
-            b.record(stream)
-            dec.append((a, b))
+            if i % 2:
+                b.record(stream)
+                dec.append((a, b))
         bb.record(stream)
         if timed:
             for k in e:
                 rec[k].append(e[k])
             rec["decode"].extend(dec)
-            rec["decode_batch"].append((ba, bb))
+            if i % 2 == 0:
+                rec["decode_batch"].append((ba, bb))
         return best
 
     # fill every copy once, then warm up

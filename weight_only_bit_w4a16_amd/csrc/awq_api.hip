@@ -77,6 +77,12 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const float* 
       e = awq::launch_gemv_w4(x, qpacked, scales, zeros, M, N, K, g, y, s, kernel == 2 ? 1 : 0);
     else
       e = awq::launch_gemv_w3(x, qpacked, scales, zeros, M, N, K, g, y, s);
+    // a shape the decode kernel does not cover (its LDS budget) runs on the
+    // prefill kernel when the caller let the library choose
+    if (e == hipErrorNotSupported && kernel == 0) {
+      (void)hipGetLastError();
+      e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s);
+    }
   } else {
     e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s);
   }

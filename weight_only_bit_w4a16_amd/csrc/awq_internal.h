@@ -33,7 +33,7 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
 hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scales,
                           const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
                           hipStream_t st);
-constexpr int kGemvW3MaxM = 0;  // int3 decode runs on the prefill kernel
+constexpr int kGemvW3MaxM = 4;
 // prefill (any M)
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
                        const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
