@@ -14,8 +14,8 @@ The decode GEMV runs on R independent copies of the packed weights
 `value` is the decode GEMV's effective HBM bandwidth: algorithmic bytes per
 call (packed codes + fp32 scales + uint8 zeros + X' + Y) divided by the mean
 kernel time, taken with HIP events on the stream the kernels run on around a
-batch of back-to-back calls (per-call event times, which add the event
-overhead to every call, are reported beside it).
+replayed HIP graph of back-to-back calls (per-call event times, which add the
+event and launch overhead to every call, are reported beside it).
 The prefill GEMM is reported as TFLOP/s against the fp16 MFMA peak.
 
 Prints one JSON line. `--gpus N` with N > 1 exits: this path runs on one GPU.
@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 256 MiB device copy first (a kernel of known "
+                        "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="approximate budget for the oracle's timed sample")
     return p.parse_args()
@@ -151,18 +154,20 @@ def main():
         e["prefill"][0].record(stream)
         awq.w4a16_matmul(Xpf, *dst, w.bits, w.group, out=Yp)
         e["prefill"][1].record(stream)
-        # decode on every copy but the one just written (cold in the caches),
-        # back to back between one event pair; odd steps also time each call
+        # decode on every copy but the one just written (cold in the caches):
+        # even steps replay a captured graph of the R-1 calls between one
+        # event pair, odd steps launch them one by one with an event pair each
         dec = []
         ba, bb = ev(), ev()
         ba.record(stream)
-        for r in range(1, R):
-            q = copies[(i + r) % R]
-            if i % 2:
+        if i % 2 == 0:
+            graphs[i % R].replay()
+        else:
+            for r in range(1, R):
+                q = copies[(i + r) % R]
                 a, b = ev(), ev()
                 a.record(stream)
-            awq.w4a16_matmul(X1f, *q, w.bits, w.group, out=Y1)
-            if i % 2:
+                awq.w4a16_matmul(X1f, *q, w.bits, w.group, out=Y1)
                 b.record(stream)
                 dec.append((a, b))
         bb.record(stream)
@@ -174,10 +179,36 @@ def main():
                 rec["decode_batch"].append((ba, bb))
         return best
 
+    if args.copy_calibration:
+        a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     # fill every copy once, then warm up
     s0, _, _ = awq.scale_search(W, Xc, grid, w.bits, w.group, workspace=ws)
     for dst in copies:
         awq.quantize_pack(W, s0, w.bits, w.group, out=dst)
+    awq.fold_inv_scale(X1, s0, out=X1f)
+    # graph g decodes every copy but copy g (the one step g rewrites)
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            awq.w4a16_matmul(X1f, *copies[0], w.bits, w.group, out=Y1)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for g in range(R):
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            for r in range(1, R):
+                awq.w4a16_matmul(X1f, *copies[(g + r) % R], w.bits, w.group, out=Y1)
+        graphs.append(cg)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
@@ -189,6 +220,8 @@ def main():
 
     def mean_ms(k):
         v = [a.elapsed_time(b) for a, b in rec[k]]
+        if not v:
+            return float("nan"), float("nan")
         return float(np.mean(v)), float(np.min(v))
 
     dec_call_ms, dec_min = mean_ms("decode")
@@ -205,13 +238,7 @@ def main():
     pack_bytes = w.N * w.K * 2 + packed_bytes + w.K * 4
     search_flops = 2.0 * 2 * w.T * w.N * w.K * len(grid)  # hi and lo parts
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "decode_gemv_traffic.json")
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            t = json.load(f)
-        if t.get("workload") == w.name and t.get("kernel_source_sha") == kernel_sha():
-            traffic = t.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(w.name)
 
     out = {
         "metric": "W4A16 GEMV effective HBM GB/s (% peak) at M=1; prefill GEMM TFLOP/s (% MFMA)",
@@ -235,8 +262,9 @@ def main():
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "decode GEMV (M=1)", "bytes_per_launch": dec_bytes,
-            "mean_us": round(dec_ms * 1e3, 2), "per_call_event_mean_us": round(dec_call_ms * 1e3, 2),
-            "per_call_event_min_us": round(dec_min * 1e3, 2),
+            "mean_us": round(dec_ms * 1e3, 2),
+            "per_call_event_mean_us": None if dec_call_ms != dec_call_ms else round(dec_call_ms * 1e3, 2),
+            "per_call_event_min_us": None if dec_min != dec_min else round(dec_min * 1e3, 2),
         },
         "roofline_prefill": {
             "bound": "mfma", "achieved": round(pre_tfs, 1), "peak": FP16_MFMA_PEAK_TF,
@@ -256,6 +284,26 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, W_np, Xc_np, s0.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the summary is for another workload or an older kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_gemv_m1_llama70b_mlp_8192x28672_int4_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("workload") != workload or kv.get("kernel_source_sha") != kernel_sha():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def kernel_sha():
