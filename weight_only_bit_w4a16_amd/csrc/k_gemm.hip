@@ -1,13 +1,19 @@
 // Prefill / batched W4A16 (and W3A16) product on the fp16 matrix cores, and
 // the fp16 "A * B^T" contraction the scale search uses.
 //
-// One workgroup (4 wavefronts, 2 x 2) computes a 128 x 128 tile of
-// Y = A B^T, A = X' [M, K] fp16 and B = dequant(Q) [N, K]. The K loop runs
-// one 128-code group per step: the packed words, group steps and zero points
-// of the next step are loaded into registers while the matrix cores work on
-// the current step; then the tile is dequantized to fp16 (q - z) * delta in
-// LDS and the activation tile is copied next to it. Each wavefront computes
-// 64 x 64 with v_mfma_f32_32x32x16_f16.
+// A workgroup of WGM x WGN wavefronts computes a BM x BN tile of Y = A B^T,
+// A = X' [M, K] fp16, B = dequant(Q) [N, K]; each wavefront computes a
+// (BM/WGM) x (BN/WGN) sub-tile with v_mfma_f32_32x32x16_f16. The K loop is
+// software pipelined over two LDS buffers with one barrier per step: while
+// the matrix cores work on step k from one buffer, two register stages hold
+// steps k+1 and k+2 (loads in flight); after the MFMAs, step k+1 is
+// dequantized into the other buffer and the loads for step k+3 are issued.
+//
+// K steps: 64 codes (half a group) for int4 and fp16 B, one whole 128-code
+// group for int3 (an int3 group is 13 words; 64 codes would split a word).
+// B tiles are dequantized to fp16 (q - z) * fp16(delta). For int4 a group
+// spans two steps: the scale and zero point are loaded with the even step
+// only and reused for the odd one.
 //
 // Code order in LDS. The packed words are unpacked with the fp16 magic-number
 // trick, which yields codes in pairs that are not adjacent in k; the
@@ -16,8 +22,8 @@
 //   int4, per 8-code word:  c0 c4 c2 c6 c1 c5 c3 c7
 //   int3, per 10-code word: c0 c6 c1 c7 c3 c8 c4 c9 c2 c5
 // (an int3 group is 13 words = 130 slots, of which the last 2 hold no code;
-// their activation slots are zero). fp16 B tiles (the search) keep natural
-// order.
+// their activation slots are zero; slots 130..143 pad the step to 9 x 16).
+// fp16 B tiles (the search) keep natural order.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -27,82 +33,87 @@ namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128;
-constexpr int NT = 256;
-
-template <int BMODE>
-struct Cfg;
-template <>
-struct Cfg<0> {  // fp16 B, natural order
-  static constexpr int SLOTS = 128, STRIDE = 136;
-};
-template <>
-struct Cfg<4> {
-  static constexpr int SLOTS = 128, STRIDE = 136;
-};
-template <>
-struct Cfg<3> {
-  static constexpr int SLOTS = 144, STRIDE = 152;  // 130 used + zero pad to 9 x 16
-};
-
 __device__ __forceinline__ floatx16 mfma32(u32x4 a, u32x4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
                                                 __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t plo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+// low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
+__device__ __forceinline__ uint32_t plo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
 __device__ __forceinline__ uint32_t phi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 __device__ __forceinline__ uint32_t hbits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 hv(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-// ---- per-step register staging -------------------------------------------
+template <int BMODE, int BM, int BN, int NT>
+struct Cfg {
+  static constexpr int BK = BMODE == 3 ? 128 : 64;     // codes per step
+  static constexpr int SLOTS = BMODE == 3 ? 144 : 64;  // LDS k slots per step
+  static constexpr int STR = SLOTS + 8;                // LDS row stride (halves)
+  static constexpr int ACH = BM * BK / 8 / NT;         // 16-byte A chunks per thread
+  static constexpr int BCH = BN * BK / 8 / NT;         // 16-byte fp16 B chunks per thread
+  static constexpr int BW = BN * 8 / NT;               // int4 B words per thread
+  static constexpr int AIT = (BM * 13 + NT - 1) / NT;  // int3 A items per thread
+  static constexpr int BIT = (BN * 13 + NT - 1) / NT;  // int3 B items per thread
+};
 
-template <int BMODE>
+// register staging of one K step
+template <int BMODE, int BM, int BN, int NT>
 struct Stage;
+template <int BM, int BN, int NT>
+struct Stage<0, BM, BN, NT> {
+  u32x4 a[Cfg<0, BM, BN, NT>::ACH], b[Cfg<0, BM, BN, NT>::BCH];
+};
+template <int BM, int BN, int NT>
+struct Stage<4, BM, BN, NT> {
+  u32x4 a[Cfg<4, BM, BN, NT>::ACH];
+  uint32_t b[Cfg<4, BM, BN, NT>::BW];
+  float d;           // scale of the step's group (even steps only)
+  uint32_t zw, zsh;  // zero point = (zw >> zsh) & 0xff (even steps only)
+};
+template <int BM, int BN, int NT>
+struct Stage<3, BM, BN, NT> {
+  uint32_t a[Cfg<3, BM, BN, NT>::AIT][5];
+  uint32_t b[Cfg<3, BM, BN, NT>::BIT];
+  float d[Cfg<3, BM, BN, NT>::BIT];
+  uint32_t zw[Cfg<3, BM, BN, NT>::BIT], zsh[Cfg<3, BM, BN, NT>::BIT];
+};
 
-// fp16 A and B, natural order: 8 x 16 B per thread for each operand
-template <>
-struct Stage<0> {
-  u32x4 a[8], b[8];
-};
-// int4: A 8 x 16 B, B 2 x 16 B (8 words of one row) + delta + z
-template <>
-struct Stage<4> {
-  u32x4 a[8];
-  u32x4 b[2];
-  float d;
-  uint32_t z;
-};
-// int3: A 7 items x 5 dwords, B 7 words + delta/z per item
-template <>
-struct Stage<3> {
-  uint32_t a[7][5];
-  uint32_t b[7];
-  float d[7];
-  uint32_t z[7];
+// int4 dequantization constants of one (row, group): fp16 delta and the
+// offsets -(1024 + z), -(64 + z) that turn magic-number halves into c - z
+struct Dq {
+  h2 dh, ze, zo;
 };
 
 }  // namespace
 
-template <int BMODE, int EPI>
-__global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict__ A,
-                                                     const void* __restrict__ Bsrc,
-                                                     const float* __restrict__ S,
-                                                     const uint8_t* __restrict__ Z, int M, int N,
-                                                     int K, int wpr, int gshift,
-                                                     uint16_t* __restrict__ Y,
-                                                     double* __restrict__ partial) {
-  using C = Cfg<BMODE>;
-  constexpr int STR = C::STRIDE;
-  __shared__ __align__(16) uint16_t lds_a[BM * STR];
-  __shared__ __align__(16) uint16_t lds_b[BN * STR];
+// ZW: zero points are read as the aligned 32-bit word holding them (the
+// zero-point array is a whole number of words); otherwise byte by byte.
+// Word loads keep the loop-carried value 32 bits wide, so no byte
+// extension is scheduled ahead of the MFMAs (it would wait on the newest
+// loads).
+template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
+    const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const float* __restrict__ S,
+    const uint8_t* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
+    uint16_t* __restrict__ Y, double* __restrict__ partial) {
+  constexpr int NT = 64 * WGM * WGN;
+  using C = Cfg<BMODE, BM, BN, NT>;
+  using St = Stage<BMODE, BM, BN, NT>;
+  constexpr int STR = C::STR;
+  constexpr int BK = C::BK;
+  constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;  // 32x32 tiles per wavefront
+  static_assert(TM >= 1 && TN >= 1 && BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile");
+  __shared__ __align__(16) uint16_t lds_a[2][BM * STR];
+  __shared__ __align__(16) uint16_t lds_b[2][BN * STR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // tile order: when the tile count splits evenly over the 8 XCDs, give each
   // XCD a contiguous run of tiles that walk M for a fixed N tile, so the
@@ -115,150 +126,196 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict_
   const int m0 = (t % mt) * BM;
   const int n0 = (t / mt) * BN;
   // fp16 B (the search) holds each error term as a hi and a lo fp16 part,
-  // [N][2K] with chunk c = (hi of k-chunk c/2 | lo of k-chunk c/2): 2 steps
-  // per 128-wide k-chunk, both against the same activation chunk
-  const int nsteps = BMODE == 0 ? 2 * (K >> 7) : K >> 7;
+  // [N][2K]: 256-wide block c = (hi of k 128c..128c+127 | lo of the same k),
+  // so a 64-wide step s reads activations 128*(s/4) + 64*(s%2)
+  const int nsteps = BMODE == 0 ? 2 * (K / BK) : K / BK;
+  const int ng = K >> (7 + gshift);  // quantization groups per row
 
   if (BMODE == 3) {
-    // zero the slots 130..143 of every row once; they are never written again
-    for (int i = tid; i < BM * 14; i += NT) {
-      lds_a[(i / 14) * STR + 130 + i % 14] = 0;
-      lds_b[(i / 14) * STR + 130 + i % 14] = 0;
+    // zero the slots 130..143 of every row of both buffers once; they are
+    // never written again
+    for (int i = tid; i < 2 * (BM + BN) * 14; i += NT) {
+      const int buf = i / ((BM + BN) * 14);
+      const int rr = (i / 14) % (BM + BN), c = i % 14;
+      if (rr < BM)
+        lds_a[buf][rr * STR + 130 + c] = 0;
+      else
+        lds_b[buf][(rr - BM) * STR + 130 + c] = 0;
     }
   }
 
-  Stage<BMODE> st;
-  auto load_step = [&](int ks) {
-    const int k0 = BMODE == 0 ? (ks >> 1) << 7 : ks << 7;
+  auto load_zero = [&](size_t idx, uint32_t& zw, uint32_t& zsh) {
+    if constexpr (ZW) {
+      zw = reinterpret_cast<const uint32_t*>(Z)[idx >> 2];
+      zsh = 8u * (uint32_t)(idx & 3);
+    } else {
+      zw = Z[idx];
+      zsh = 0u;
+    }
+  };
+  // load step ks into st; for int4, SZ says whether this (even) step also
+  // loads its group's scale and zero point
+  auto load_step = [&](St& st, int ks, auto SZ) {
     if constexpr (BMODE == 0 || BMODE == 4) {
+      const int ka = BMODE == 0 ? 128 * (ks >> 2) + 64 * (ks & 1) : BK * ks;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < C::ACH; ++i) {
         const int id = tid + NT * i;
-        const int r = id >> 4, c8 = id & 15;
-        const int m = m0 + r;
-        if (m < M)
-          st.a[i] = *reinterpret_cast<const u32x4*>(A + (size_t)m * K + k0 + 8 * c8);
-        else
-          st.a[i] = u32x4{0, 0, 0, 0};
+        const int r = id / (BK / 8), c8 = id % (BK / 8);
+        // rows past M read row M - 1: they only feed outputs never stored
+        const int m = min(m0 + r, M - 1);
+        st.a[i] = *reinterpret_cast<const u32x4*>(A + (size_t)m * K + ka + 8 * c8);
       }
     }
     if constexpr (BMODE == 0) {
       const uint16_t* B = static_cast<const uint16_t*>(Bsrc);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < C::BCH; ++i) {
         const int id = tid + NT * i;
-        const int r = id >> 4, c8 = id & 15;
+        const int r = id / (BK / 8), c8 = id % (BK / 8);
         const int n = min(n0 + r, N - 1);
-        st.b[i] = *reinterpret_cast<const u32x4*>(B + (size_t)n * 2 * K + (ks << 7) + 8 * c8);
+        st.b[i] = *reinterpret_cast<const u32x4*>(B + (size_t)n * 2 * K + BK * ks + 8 * c8);
       }
     } else if constexpr (BMODE == 4) {
+      // BW consecutive words of one row (8 words = 64 codes per row and step)
       const uint32_t* Q = static_cast<const uint32_t*>(Bsrc);
-      const int r = tid >> 1, h = tid & 1;
+      const int r = (tid * C::BW) / 8, w0 = (tid * C::BW) % 8;
       const int n = min(n0 + r, N - 1);
-      const uint32_t* p = Q + (size_t)n * wpr + ks * 16 + 8 * h;
-      st.b[0] = ld_nt(reinterpret_cast<const u32x4*>(p));
-      st.b[1] = ld_nt(reinterpret_cast<const u32x4*>(p + 4));
-      const int ng = nsteps >> gshift;
-      st.d = S[(size_t)n * ng + (ks >> gshift)];
-      st.z = Z[(size_t)n * ng + (ks >> gshift)];
-    } else {  // int3: items (row, word) over 128 rows x 13 words
+      const uint32_t* p = Q + (size_t)n * wpr + 8 * ks + w0;
+      if constexpr (SZ.value) {
+        const int g = (ks * BK) >> (7 + gshift);
+        st.d = S[(size_t)n * ng + g];
+        load_zero((size_t)n * ng + g, st.zw, st.zsh);
+      }
+      if constexpr (C::BW == 4) {
+        const u32x4 v = ld_nt(reinterpret_cast<const u32x4*>(p));
+        st.b[0] = v[0];
+        st.b[1] = v[1];
+        st.b[2] = v[2];
+        st.b[3] = v[3];
+      } else if constexpr (C::BW == 2) {
+        const uint64_t v = ld_nt(reinterpret_cast<const uint64_t*>(p));
+        st.b[0] = (uint32_t)v;
+        st.b[1] = (uint32_t)(v >> 32);
+      } else {
+#pragma unroll
+        for (int q = 0; q < C::BW; ++q) st.b[q] = ld_nt(p + q);
+      }
+    } else {  // int3: items (row, word) over BM or BN rows x 13 words
       const uint32_t* Q = static_cast<const uint32_t*>(Bsrc);
+      const int k0 = BK * ks;
 #pragma unroll
-      for (int i = 0; i < 7; ++i) {
-        const int id = tid + NT * i;
-        if (id < BM * 13) {
-          const int r = id / 13, j = id % 13;
-          const int m = m0 + r;
-          const int kx = k0 + 10 * j;
-          if (m < M) {
-            const uint32_t* px = reinterpret_cast<const uint32_t*>(A + (size_t)m * K + kx);
+      for (int i = 0; i < C::AIT; ++i) {
+        const int id = min(tid + NT * i, BM * 13 - 1);
+        const int r = id / 13, j = id % 13;
+        const int m = min(m0 + r, M - 1);
+        const uint32_t* px = reinterpret_cast<const uint32_t*>(A + (size_t)m * K + k0 + 10 * j);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) st.a[i][q] = px[q];
-            st.a[i][4] = j < 12 ? px[4] : 0u;  // codes 128, 129 do not exist
-          } else {
+        for (int q = 0; q < 4; ++q) st.a[i][q] = px[q];
+        // codes 128, 129 do not exist: word 12 re-reads codes 120, 121 and
+        // the store zeroes them
+        st.a[i][4] = px[j < 12 ? 4 : 0];
+      }
 #pragma unroll
-            for (int q = 0; q < 5; ++q) st.a[i][q] = 0u;
-          }
-          const int n = min(n0 + r, N - 1);
-          st.b[i] = ld_nt(Q + (size_t)n * wpr + ks * 13 + j);
-          st.d[i] = S[(size_t)n * nsteps + ks];
-          st.z[i] = Z[(size_t)n * nsteps + ks];
-        }
+      for (int i = 0; i < C::BIT; ++i) {
+        const int id = min(tid + NT * i, BN * 13 - 1);
+        const int r = id / 13, j = id % 13;
+        const int n = min(n0 + r, N - 1);
+        st.b[i] = ld_nt(Q + (size_t)n * wpr + ks * 13 + j);
+        st.d[i] = S[(size_t)n * ng + ks];
+        load_zero((size_t)n * ng + ks, st.zw[i], st.zsh[i]);
       }
     }
   };
 
-  auto store_step = [&]() {
+  Dq dq;  // int4: constants of the group of the last even step stored
+  auto store_step = [&](const St& st, int buf, auto SZ) {
+    uint16_t* la = lds_a[buf];
+    uint16_t* lb = lds_b[buf];
     if constexpr (BMODE == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < C::ACH; ++i) {
         const int id = tid + NT * i;
-        const int r = id >> 4, c8 = id & 15;
-        *reinterpret_cast<u32x4*>(&lds_a[r * STR + 8 * c8]) = st.a[i];
-        *reinterpret_cast<u32x4*>(&lds_b[r * STR + 8 * c8]) = st.b[i];
+        const int r = id / (BK / 8), c8 = id % (BK / 8);
+        *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = st.a[i];
+      }
+#pragma unroll
+      for (int i = 0; i < C::BCH; ++i) {
+        const int id = tid + NT * i;
+        const int r = id / (BK / 8), c8 = id % (BK / 8);
+        *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * c8]) = st.b[i];
       }
     } else if constexpr (BMODE == 4) {
+      if constexpr (SZ.value) {
+        const uint32_t z = (st.zw >> st.zsh) & 0xffu;
+        dq.dh = h2{(_Float16)st.d, (_Float16)st.d};
+        dq.ze = hv((0xE400u + z) * 0x00010001u);       // -(1024 + z)
+        dq.zo = hv((0xD400u + 16u * z) * 0x00010001u);  // -(64 + z)
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < C::ACH; ++i) {
         const int id = tid + NT * i;
-        const int r = id >> 4, c8 = id & 15;
+        const int r = id / (BK / 8), c8 = id % (BK / 8);
         const u32x4 d = st.a[i];
         const u32x4 p = {plo(d[0], d[2]), plo(d[1], d[3]), phi(d[0], d[2]), phi(d[1], d[3])};
-        *reinterpret_cast<u32x4*>(&lds_a[r * STR + 8 * c8]) = p;
+        *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = p;
       }
-      const int r = tid >> 1, h = tid & 1;
-      const h2 dh = {(_Float16)st.d, (_Float16)st.d};
-      const h2 ze = hv((0xE400u + st.z) * 0x00010001u);       // -(1024 + z)
-      const h2 zo = hv((0xD400u + 16u * st.z) * 0x00010001u);  // -(64 + z)
+      const int r = (tid * C::BW) / 8, w0 = (tid * C::BW) % 8;
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w = st.b[v][q];
-          const uint32_t w8 = w >> 8;
-          const h2 e0 = (hv((w & 0x000F000Fu) | kMagic2) + ze) * dh;
-          const h2 e1 = (hv((w8 & 0x000F000Fu) | kMagic2) + ze) * dh;
-          const h2 o0 = __builtin_elementwise_fma(hv((w & 0x00F000F0u) | kMagic2), sixteenth, zo) * dh;
-          const h2 o1 = __builtin_elementwise_fma(hv((w8 & 0x00F000F0u) | kMagic2), sixteenth, zo) * dh;
-          const int word = 8 * h + 4 * v + q;
-          *reinterpret_cast<u32x4*>(&lds_b[r * STR + 8 * word]) =
-              u32x4{hbits(e0), hbits(e1), hbits(o0), hbits(o1)};
-        }
+      for (int q = 0; q < C::BW; ++q) {
+        const uint32_t w = st.b[q];
+        const uint32_t w8 = w >> 8;
+        const h2 e0 = (hv((w & 0x000F000Fu) | kMagic2) + dq.ze) * dq.dh;
+        const h2 e1 = (hv((w8 & 0x000F000Fu) | kMagic2) + dq.ze) * dq.dh;
+        const h2 o0 =
+            __builtin_elementwise_fma(hv((w & 0x00F000F0u) | kMagic2), sixteenth, dq.zo) * dq.dh;
+        const h2 o1 =
+            __builtin_elementwise_fma(hv((w8 & 0x00F000F0u) | kMagic2), sixteenth, dq.zo) * dq.dh;
+        *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * (w0 + q)]) =
+            u32x4{hbits(e0), hbits(e1), hbits(o0), hbits(o1)};
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 7; ++i) {
+      for (int i = 0; i < C::AIT; ++i) {
         const int id = tid + NT * i;
         if (id < BM * 13) {
           const int r = id / 13, j = id % 13;
-          const uint32_t* d = st.a[i];
+          uint32_t d[5];
+#pragma unroll
+          for (int q = 0; q < 5; ++q) d[q] = st.a[i][q];
+          if (j == 12) d[4] = 0u;
           // (x0,x6) (x1,x7) (x3,x8) (x4,x9) (x2,x5) from d_i = (x[2i], x[2i+1])
-          uint32_t* pa = reinterpret_cast<uint32_t*>(&lds_a[r * STR + 10 * j]);
+          uint32_t* pa = reinterpret_cast<uint32_t*>(&la[r * STR + 10 * j]);
           pa[0] = plo(d[0], d[3]);
           pa[1] = phi(d[0], d[3]);
-          pa[2] = (d[1] >> 16) | (d[4] << 16);
-          pa[3] = (d[2] & 0xffffu) | (d[4] & 0xffff0000u);
-          pa[4] = (d[1] & 0xffffu) | (d[2] & 0xffff0000u);
-          // codes: magic pairs with per-half power-of-two weights, made exact
-          // integers c - z by one packed fma each, then scaled by delta
+          pa[2] = __builtin_amdgcn_perm(d[4], d[1], 0x05040302u);  // (d1.hi, d4.lo)
+          pa[3] = __builtin_amdgcn_perm(d[4], d[2], 0x07060100u);  // (d2.lo, d4.hi)
+          pa[4] = __builtin_amdgcn_perm(d[2], d[1], 0x07060100u);  // (d1.lo, d2.hi)
+        }
+      }
+      // codes: magic pairs with per-half power-of-two weights, made exact
+      // integers c - z by one packed fma each, then scaled by delta
+      const h2 mul[5] = {{(_Float16)1.f, (_Float16)0.25f},
+                         {(_Float16)0.125f, (_Float16)0.03125f},
+                         {(_Float16)0.5f, (_Float16)1.f},
+                         {(_Float16)0.0625f, (_Float16)0.125f},
+                         {(_Float16)0.0078125f, (_Float16)1.f}};
+      const float offl[5] = {1024.f, 128.f, 512.f, 64.f, 8.f};
+      const float offh[5] = {256.f, 32.f, 1024.f, 128.f, 1024.f};
+#pragma unroll
+      for (int i = 0; i < C::BIT; ++i) {
+        const int id = tid + NT * i;
+        if (id < BN * 13) {
+          const int r = id / 13, j = id % 13;
           const uint32_t w = st.b[i];
           const uint32_t t8 = w >> 8, u1 = w << 1;
-          const uint32_t z = st.z[i];
+          const float zf = (float)((st.zw[i] >> st.zsh[i]) & 0xffu);
           const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
           const uint32_t raw[5] = {(w & 0x001C0007u) | kMagic2, (w & 0x00E00038u) | kMagic2,
                                    (t8 & 0x0007000Eu) | kMagic2, (t8 & 0x00380070u) | kMagic2,
                                    (u1 & 0x00070380u) | kMagic2};
-          // per pair: (lo weight, hi weight) = (1,4) (8,32) (2,1) (16,8) (128,1)
-          const h2 mul[5] = {{(_Float16)1.f, (_Float16)0.25f},
-                             {(_Float16)0.125f, (_Float16)0.03125f},
-                             {(_Float16)0.5f, (_Float16)1.f},
-                             {(_Float16)0.0625f, (_Float16)0.125f},
-                             {(_Float16)0.0078125f, (_Float16)1.f}};
-          const float offl[5] = {1024.f, 128.f, 512.f, 64.f, 8.f};
-          const float offh[5] = {256.f, 32.f, 1024.f, 128.f, 1024.f};
-          uint32_t* pb = reinterpret_cast<uint32_t*>(&lds_b[r * STR + 10 * j]);
-          const float zf = (float)z;
+          uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * j]);
 #pragma unroll
           for (int p = 0; p < 5; ++p) {
             const h2 add = {(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
@@ -269,65 +326,94 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict_
     }
   };
 
-  floatx16 acc[2][2];
+  floatx16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int lr = lane & 31;
   const int lk = (lane >> 5) * 8;
-  load_step(0);
-  for (int ks = 0; ks < nsteps; ++ks) {
-    __syncthreads();  // previous step's MFMA reads are done
-    store_step();
-    __syncthreads();
-    if (ks + 1 < nsteps) load_step(ks + 1);
+  const int arow = (BM / WGM) * wm + lr;
+  const int brow = (BN / WGN) * wn + lr;
+
+  auto compute = [&](int buf) {
+    const uint16_t* la = lds_a[buf];
+    const uint16_t* lb = lds_b[buf];
     constexpr int NKS = C::SLOTS / 16;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
       const int ko = kk * 16 + lk;
-      u32x4 fa[2], fb[2];
+      u32x4 fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(&lds_a[(64 * wm + 32 * i + lr) * STR + ko]);
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(&la[(arow + 32 * i) * STR + ko]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(&lds_b[(64 * wn + 32 * j + lr) * STR + ko]);
+      for (int j = 0; j < TN; ++j)
+        fb[j] = *reinterpret_cast<const u32x4*>(&lb[(brow + 32 * j) * STR + ko]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
     }
+  };
+
+  // Two register stages in flight: while step ks is computed from LDS,
+  // stage sa holds step ks + 1 (stored after the MFMAs) and sb step ks + 2.
+  // sa always carries even steps, sb odd ones. Loads past the last step
+  // re-read the last step (branch-free; the extra stores land in the buffer
+  // no later step reads).
+  using Even = std::integral_constant<bool, BMODE == 4>;
+  using Odd = std::integral_constant<bool, false>;
+  St sa, sb;
+  const int last = nsteps - 1;
+  load_step(sa, 0, Even{});
+  load_step(sb, min(1, last), Odd{});
+  store_step(sa, 0, Even{});
+  load_step(sa, min(2, last), Even{});
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 1 < nsteps; ks += 2) {
+    compute(0);
+    store_step(sb, 1, Odd{});
+    load_step(sb, min(ks + 3, last), Odd{});
+    __syncthreads();
+    compute(1);
+    store_step(sa, 0, Even{});
+    load_step(sa, min(ks + 4, last), Even{});
+    __syncthreads();
   }
+  if (ks < nsteps) compute(0);
 
   // D layout of the 32x32 MFMA: lane l holds column l % 32, rows
   // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15
   if constexpr (EPI == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 64 * wn + 32 * j + lr;
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + (BN / WGN) * wn + 32 * j + lr;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int m =
+              m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][v]));
         }
       }
   } else {
-    __shared__ double wsum[4];
+    __shared__ double wsum[WGM * WGN];
     float sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 64 * wn + 32 * j + lr;
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + (BN / WGN) * wn + 32 * j + lr;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int m =
+              m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const float e = acc[i][j][v];
           if (m < M && n < N) sq = __builtin_fmaf(e, e, sq);
         }
@@ -337,9 +423,26 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(const uint16_t* __restrict_
     for (int off = 32; off >= 1; off >>= 1) ds += __shfl_xor(ds, off);
     if (lane == 0) wsum[wave] = ds;
     __syncthreads();
-    if (tid == 0) partial[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    if (tid == 0) {
+      double s = 0.0;
+      for (int w = 0; w < WGM * WGN; ++w) s += wsum[w];
+      partial[blockIdx.x] = s;
+    }
   }
 }
+
+namespace {
+int cu_n() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  return v;
+}
+unsigned tiles_of(int M, int N, int bm, int bn) {
+  return (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
+}
+}  // namespace
 
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
                        const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
@@ -348,15 +451,33 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   int gshift = 0;
   while ((128 << gshift) < group) ++gshift;
   const int wpr = words_per_row(K, bits, group);
-  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
-  if (bits == 4)
-    hipLaunchKernelGGL((gemm_kernel<4, 0>), dim3(tiles), dim3(NT), 0, st, x, q, scales, zeros, M,
-                       N, K, wpr, gshift, y, nullptr);
-  else
-    hipLaunchKernelGGL((gemm_kernel<3, 0>), dim3(tiles), dim3(NT), 0, st, x, q, scales, zeros, M,
-                       N, K, wpr, gshift, y, nullptr);
+  const unsigned cus = (unsigned)cu_n();
+  const bool zw = ((size_t)N * (size_t)(K / group)) % 4 == 0;
+#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN)                                                      \
+  do {                                                                                          \
+    if (zw)                                                                                     \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true>),                       \
+                         dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
+                         zeros, M, N, K, wpr, gshift, y, nullptr);                              \
+    else                                                                                        \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false>),                      \
+                         dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
+                         zeros, M, N, K, wpr, gshift, y, nullptr);                              \
+  } while (0)
+  if (bits == 4) {
+    // the largest tile that still gives every compute unit work
+    if (tiles_of(M, N, 256, 256) >= cus)
+      AWQ_GEMM(4, 256, 256, 2, 4);
+    else if (tiles_of(M, N, 128, 128) >= cus)
+      AWQ_GEMM(4, 128, 128, 2, 2);
+    else
+      AWQ_GEMM(4, 64, 64, 2, 2);
+  } else {
+    AWQ_GEMM(3, 64, 64, 2, 2);
+  }
+#undef AWQ_GEMM
   return hipGetLastError();
 }
 
@@ -364,14 +485,11 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
 // [M, K] fp16, B is [N, 2K] fp16 holding hi/lo parts per 128-wide k chunk
 hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K,
                              double* partial, hipStream_t st) {
-  const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_kernel<0, 1>), dim3(tiles), dim3(NT), 0, st, A, B, nullptr, nullptr, M,
-                     N, K, 0, 0, nullptr, partial);
+  hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false>), dim3(tiles_of(M, N, 128, 128)),
+                     dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial);
   return hipGetLastError();
 }
 
-unsigned sqnorm_abt_tiles(int M, int N) {
-  return (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-}
+unsigned sqnorm_abt_tiles(int M, int N) { return tiles_of(M, N, 128, 128); }
 
 }  // namespace awq
