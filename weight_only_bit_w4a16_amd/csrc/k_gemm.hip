@@ -45,6 +45,12 @@ __device__ __forceinline__ uint32_t plo(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t phi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
+// v_and_or_b32: (a & m) | o in one instruction (the mask stays scalar)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
 __device__ __forceinline__ uint32_t hbits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 hv(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
@@ -228,72 +234,69 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     }
   };
 
+  // dequantize / permute one register stage into LDS buffer buf, item by
+  // item, so the work can be spread between the MFMAs of the current step
+  constexpr int NA = BMODE == 3 ? C::AIT : C::ACH;                         // A items
+  constexpr int NB = BMODE == 3 ? C::BIT : (BMODE == 4 ? C::BW : C::BCH);  // B items
   Dq dq;  // int4: constants of the group of the last even step stored
-  auto store_step = [&](const St& st, int buf, auto SZ) {
+  auto set_dq = [&](const St& st) {
+    if constexpr (BMODE == 4) {
+      const uint32_t z = (st.zw >> st.zsh) & 0xffu;
+      dq.dh = h2{(_Float16)st.d, (_Float16)st.d};
+      dq.ze = hv((0xE400u + z) * 0x00010001u);       // -(1024 + z)
+      dq.zo = hv((0xD400u + 16u * z) * 0x00010001u);  // -(64 + z)
+    }
+  };
+  auto store_a = [&](const St& st, int buf, int i) {
     uint16_t* la = lds_a[buf];
+    if constexpr (BMODE == 0) {
+      const int id = tid + NT * i;
+      const int r = id / (BK / 8), c8 = id % (BK / 8);
+      *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = st.a[i];
+    } else if constexpr (BMODE == 4) {
+      const int id = tid + NT * i;
+      const int r = id / (BK / 8), c8 = id % (BK / 8);
+      const u32x4 d = st.a[i];
+      const u32x4 p = {plo(d[0], d[2]), plo(d[1], d[3]), phi(d[0], d[2]), phi(d[1], d[3])};
+      *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = p;
+    } else {
+      const int id = tid + NT * i;
+      if (id < BM * 13) {
+        const int r = id / 13, j = id % 13;
+        uint32_t d[5];
+#pragma unroll
+        for (int q = 0; q < 5; ++q) d[q] = st.a[i][q];
+        if (j == 12) d[4] = 0u;
+        // (x0,x6) (x1,x7) (x3,x8) (x4,x9) (x2,x5) from d_i = (x[2i], x[2i+1])
+        uint32_t* pa = reinterpret_cast<uint32_t*>(&la[r * STR + 10 * j]);
+        pa[0] = plo(d[0], d[3]);
+        pa[1] = phi(d[0], d[3]);
+        pa[2] = __builtin_amdgcn_perm(d[4], d[1], 0x05040302u);  // (d1.hi, d4.lo)
+        pa[3] = __builtin_amdgcn_perm(d[4], d[2], 0x07060100u);  // (d2.lo, d4.hi)
+        pa[4] = __builtin_amdgcn_perm(d[2], d[1], 0x07060100u);  // (d1.lo, d2.hi)
+      }
+    }
+  };
+  auto store_b = [&](const St& st, int buf, int i) {
     uint16_t* lb = lds_b[buf];
     if constexpr (BMODE == 0) {
-#pragma unroll
-      for (int i = 0; i < C::ACH; ++i) {
-        const int id = tid + NT * i;
-        const int r = id / (BK / 8), c8 = id % (BK / 8);
-        *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = st.a[i];
-      }
-#pragma unroll
-      for (int i = 0; i < C::BCH; ++i) {
-        const int id = tid + NT * i;
-        const int r = id / (BK / 8), c8 = id % (BK / 8);
-        *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * c8]) = st.b[i];
-      }
+      const int id = tid + NT * i;
+      const int r = id / (BK / 8), c8 = id % (BK / 8);
+      *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * c8]) = st.b[i];
     } else if constexpr (BMODE == 4) {
-      if constexpr (SZ.value) {
-        const uint32_t z = (st.zw >> st.zsh) & 0xffu;
-        dq.dh = h2{(_Float16)st.d, (_Float16)st.d};
-        dq.ze = hv((0xE400u + z) * 0x00010001u);       // -(1024 + z)
-        dq.zo = hv((0xD400u + 16u * z) * 0x00010001u);  // -(64 + z)
-      }
-#pragma unroll
-      for (int i = 0; i < C::ACH; ++i) {
-        const int id = tid + NT * i;
-        const int r = id / (BK / 8), c8 = id % (BK / 8);
-        const u32x4 d = st.a[i];
-        const u32x4 p = {plo(d[0], d[2]), plo(d[1], d[3]), phi(d[0], d[2]), phi(d[1], d[3])};
-        *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = p;
-      }
       const int r = (tid * C::BW) / 8, w0 = (tid * C::BW) % 8;
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-#pragma unroll
-      for (int q = 0; q < C::BW; ++q) {
-        const uint32_t w = st.b[q];
-        const uint32_t w8 = w >> 8;
-        const h2 e0 = (hv((w & 0x000F000Fu) | kMagic2) + dq.ze) * dq.dh;
-        const h2 e1 = (hv((w8 & 0x000F000Fu) | kMagic2) + dq.ze) * dq.dh;
-        const h2 o0 =
-            __builtin_elementwise_fma(hv((w & 0x00F000F0u) | kMagic2), sixteenth, dq.zo) * dq.dh;
-        const h2 o1 =
-            __builtin_elementwise_fma(hv((w8 & 0x00F000F0u) | kMagic2), sixteenth, dq.zo) * dq.dh;
-        *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * (w0 + q)]) =
-            u32x4{hbits(e0), hbits(e1), hbits(o0), hbits(o1)};
-      }
+      const uint32_t w = st.b[i];
+      const uint32_t w8 = w >> 8;
+      const h2 e0 = (hv(and_or(w, 0x000F000Fu, kMagic2)) + dq.ze) * dq.dh;
+      const h2 e1 = (hv(and_or(w8, 0x000F000Fu, kMagic2)) + dq.ze) * dq.dh;
+      const h2 o0 =
+          __builtin_elementwise_fma(hv(and_or(w, 0x00F000F0u, kMagic2)), sixteenth, dq.zo) * dq.dh;
+      const h2 o1 =
+          __builtin_elementwise_fma(hv(and_or(w8, 0x00F000F0u, kMagic2)), sixteenth, dq.zo) * dq.dh;
+      *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * (w0 + i)]) =
+          u32x4{hbits(e0), hbits(e1), hbits(o0), hbits(o1)};
     } else {
-#pragma unroll
-      for (int i = 0; i < C::AIT; ++i) {
-        const int id = tid + NT * i;
-        if (id < BM * 13) {
-          const int r = id / 13, j = id % 13;
-          uint32_t d[5];
-#pragma unroll
-          for (int q = 0; q < 5; ++q) d[q] = st.a[i][q];
-          if (j == 12) d[4] = 0u;
-          // (x0,x6) (x1,x7) (x3,x8) (x4,x9) (x2,x5) from d_i = (x[2i], x[2i+1])
-          uint32_t* pa = reinterpret_cast<uint32_t*>(&la[r * STR + 10 * j]);
-          pa[0] = plo(d[0], d[3]);
-          pa[1] = phi(d[0], d[3]);
-          pa[2] = __builtin_amdgcn_perm(d[4], d[1], 0x05040302u);  // (d1.hi, d4.lo)
-          pa[3] = __builtin_amdgcn_perm(d[4], d[2], 0x07060100u);  // (d2.lo, d4.hi)
-          pa[4] = __builtin_amdgcn_perm(d[2], d[1], 0x07060100u);  // (d1.lo, d2.hi)
-        }
-      }
       // codes: magic pairs with per-half power-of-two weights, made exact
       // integers c - z by one packed fma each, then scaled by delta
       const h2 mul[5] = {{(_Float16)1.f, (_Float16)0.25f},
@@ -303,27 +306,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
                          {(_Float16)0.0078125f, (_Float16)1.f}};
       const float offl[5] = {1024.f, 128.f, 512.f, 64.f, 8.f};
       const float offh[5] = {256.f, 32.f, 1024.f, 128.f, 1024.f};
+      const int id = tid + NT * i;
+      if (id < BN * 13) {
+        const int r = id / 13, j = id % 13;
+        const uint32_t w = st.b[i];
+        const uint32_t t8 = w >> 8, u1 = w << 1;
+        const float zf = (float)((st.zw[i] >> st.zsh[i]) & 0xffu);
+        const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
+        const uint32_t raw[5] = {(w & 0x001C0007u) | kMagic2, (w & 0x00E00038u) | kMagic2,
+                                 (t8 & 0x0007000Eu) | kMagic2, (t8 & 0x00380070u) | kMagic2,
+                                 (u1 & 0x00070380u) | kMagic2};
+        uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * j]);
 #pragma unroll
-      for (int i = 0; i < C::BIT; ++i) {
-        const int id = tid + NT * i;
-        if (id < BN * 13) {
-          const int r = id / 13, j = id % 13;
-          const uint32_t w = st.b[i];
-          const uint32_t t8 = w >> 8, u1 = w << 1;
-          const float zf = (float)((st.zw[i] >> st.zsh[i]) & 0xffu);
-          const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
-          const uint32_t raw[5] = {(w & 0x001C0007u) | kMagic2, (w & 0x00E00038u) | kMagic2,
-                                   (t8 & 0x0007000Eu) | kMagic2, (t8 & 0x00380070u) | kMagic2,
-                                   (u1 & 0x00070380u) | kMagic2};
-          uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * j]);
-#pragma unroll
-          for (int p = 0; p < 5; ++p) {
-            const h2 add = {(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
-            pb[p] = hbits(__builtin_elementwise_fma(hv(raw[p]), mul[p], add) * dh);
-          }
+        for (int p = 0; p < 5; ++p) {
+          const h2 add = {(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
+          pb[p] = hbits(__builtin_elementwise_fma(hv(raw[p]), mul[p], add) * dh);
         }
       }
     }
+  };
+  auto store_all = [&](const St& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) store_a(st, buf, i);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) store_b(st, buf, i);
   };
 
   floatx16 acc[TM][TN];
@@ -339,29 +345,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   const int arow = (BM / WGM) * wm + lr;
   const int brow = (BN / WGN) * wn + lr;
 
-  auto compute = [&](int buf) {
-    const uint16_t* la = lds_a[buf];
-    const uint16_t* lb = lds_b[buf];
-    constexpr int NKS = C::SLOTS / 16;
+  auto mma = [&](const uint16_t* la, const uint16_t* lb, int kk) {
+    const int ko = kk * 16 + lk;
+    u32x4 fa[TM], fb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[i] = *reinterpret_cast<const u32x4*>(&la[(arow + 32 * i) * STR + ko]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[j] = *reinterpret_cast<const u32x4*>(&lb[(brow + 32 * j) * STR + ko]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+  };
+  constexpr int NKS = C::SLOTS / 16;
+  // one pipeline step: MFMAs on buffer cur, with the stores of stage sst
+  // into the other buffer spread over the sub-steps, then the loads of
+  // stage lst
+  auto step = [&](int cur, const St& sst, St& lst, int lks, auto SZ) {
+    if constexpr (SZ.value) set_dq(sst);
+    const uint16_t* la = lds_a[cur];
+    const uint16_t* lb = lds_b[cur];
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      const int ko = kk * 16 + lk;
-      u32x4 fa[TM], fb[TN];
+      mma(la, lb, kk);
+      if (kk < NKS - 1) {
+        if (kk < NA) store_a(sst, cur ^ 1, kk);
+        if (kk < NB) store_b(sst, cur ^ 1, kk);
+      } else {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(&la[(arow + 32 * i) * STR + ko]);
+        for (int i = kk; i < NA; ++i) store_a(sst, cur ^ 1, i);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(&lb[(brow + 32 * j) * STR + ko]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+        for (int i = kk; i < NB; ++i) store_b(sst, cur ^ 1, i);
+      }
     }
+    load_step(lst, lks, SZ);
+    __syncthreads();
   };
 
   // Two register stages in flight: while step ks is computed from LDS,
-  // stage sa holds step ks + 1 (stored after the MFMAs) and sb step ks + 2.
+  // stage sa holds step ks + 1 (stored during the MFMAs) and sb step ks + 2.
   // sa always carries even steps, sb odd ones. Loads past the last step
   // re-read the last step (branch-free; the extra stores land in the buffer
   // no later step reads).
@@ -371,21 +395,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   const int last = nsteps - 1;
   load_step(sa, 0, Even{});
   load_step(sb, min(1, last), Odd{});
-  store_step(sa, 0, Even{});
+  set_dq(sa);
+  store_all(sa, 0);
   load_step(sa, min(2, last), Even{});
   __syncthreads();
   int ks = 0;
   for (; ks + 1 < nsteps; ks += 2) {
-    compute(0);
-    store_step(sb, 1, Odd{});
-    load_step(sb, min(ks + 3, last), Odd{});
-    __syncthreads();
-    compute(1);
-    store_step(sa, 0, Even{});
-    load_step(sa, min(ks + 4, last), Even{});
-    __syncthreads();
+    step(0, sb, sb, min(ks + 3, last), Odd{});
+    step(1, sa, sa, min(ks + 4, last), Even{});
   }
-  if (ks < nsteps) compute(0);
+  if (ks < nsteps) {
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) mma(lds_a[0], lds_b[0], kk);
+  }
 
   // D layout of the 32x32 MFMA: lane l holds column l % 32, rows
   // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15
