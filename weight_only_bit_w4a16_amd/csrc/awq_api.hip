@@ -75,8 +75,14 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const float* 
   if (decode) {
     if (bits == 4)
       e = awq::launch_gemv_w4(x, qpacked, scales, zeros, M, N, K, g, y, s, kernel == 2 ? 1 : 0);
+    else if (M == 1 && kernel == 0)
+      e = awq::launch_gemv_w3_m1(x, qpacked, scales, zeros, N, K, g, y, s);
     else
+      e = hipErrorNotSupported;
+    if (bits == 3 && e == hipErrorNotSupported) {
+      (void)hipGetLastError();
       e = awq::launch_gemv_w3(x, qpacked, scales, zeros, M, N, K, g, y, s);
+    }
     // a shape the decode kernel does not cover (its LDS budget) runs on the
     // prefill kernel when the caller let the library choose
     if (e == hipErrorNotSupported && kernel == 0) {

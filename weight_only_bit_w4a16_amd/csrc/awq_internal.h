@@ -34,6 +34,10 @@ hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scale
                           const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
                           hipStream_t st);
 constexpr int kGemvW3MaxM = 4;
+// decode, int3, M = 1, group 128 (K up to 96 groups)
+hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* scales,
+                             const uint8_t* zeros, int N, int K, int group, __half* Y,
+                             hipStream_t st);
 // prefill (any M)
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
                        const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,

@@ -487,6 +487,231 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
   if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
 }
 
+// ---------------------------------------------------------------------------
+// Decode, int3, M = 1, group 128. The same streaming scheme as the int4
+// kernel above: a wavefront reads one row at a time in pieces of 16 groups
+// (16 x 13 words = 832 contiguous bytes) and contracts each piece with
+// diagonal 16x16x32 MFMAs. Lane j + 16 jj loads the 4 words of group j that
+// start at word {0, 4, 7, 9}[jj] (dword-aligned 16-byte loads) and uses all
+// 4 (jj = 0), the first 3 (jj = 1, 2) or the last 3 (jj = 3), so the
+// group's 13 words are used once and no load leaves the group.
+//
+// Unpacking. A word holds codes c0..c9 at bits 3i. Five AND-ORs with the
+// fp16 magic number give five pairs (1024 + wl c_a, 1024 + wh c_b):
+//   w & 0x001C0007 -> (c0, c6) weights (1, 4)
+//   w & 0x00E00038 -> (c1, c7)         (8, 32)
+//   (w >> 8) & 0x0007000E -> (c3, c8)  (2, 1)
+//   (w >> 8) & 0x00380070 -> (c4, c9)  (16, 8)
+//   (w << 1) & 0x00070380 -> (c2, c5)  (128, 1)
+// The activation operand holds x / weight for each slot (exact: powers of
+// two), so the MFMA gives 1024 * sum(A) + sum(c x); the first term C and
+// the zero-point term z * S are removed per group as in the int4 kernel.
+// Slots of unused words and of the two codes past the group's 128 (word 12,
+// c8 and c9) have A = 0.
+namespace {
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+constexpr int kW3Lo[5] = {0, 1, 3, 4, 2};
+constexpr int kW3Hi[5] = {6, 7, 8, 9, 5};
+constexpr float kW3InvLo[5] = {1.f, 0.125f, 0.5f, 0.0625f, 0.0078125f};
+constexpr float kW3InvHi[5] = {0.25f, 0.03125f, 1.f, 0.125f, 1.f};
+__device__ __forceinline__ int w3_first_word(int jj) { return jj == 0 ? 0 : (jj == 1 ? 4 : (jj == 2 ? 7 : 9)); }
+}  // namespace
+
+template <int SP, int RPF, bool FULL>
+__global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
+    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int wpr) {
+  __shared__ u32x4 xs[SP][5][64];  // [piece][operand][lane]
+  __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wave;
+  const int NW = gridDim.x * 4;
+  const int j = lane & 15;
+  const int jj = lane >> 4;
+  const int nch = K >> 7;  // groups per row; SP = ceil(nch / 16)
+  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int rdiag = j & 3;
+  const bool diag = jj == (j >> 2);
+  const int woff = w3_first_word(jj);
+
+  int goff[SP];
+  bool gval[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    gval[s] = FULL || 16 * s + j < nch;
+    goff[s] = FULL ? 16 * s + j : min(16 * s + j, nch - 1);
+  }
+
+  // operand prep: thread (piece s, lane l) builds lane l's 40 activation
+  // slots of group 16 s + l%16
+  for (int t = threadIdx.x; t < SP * 64; t += 256) {
+    const int ps = t >> 6, pl = t & 63;
+    const int pq = pl >> 4;
+    const int g = min(16 * ps + (pl & 15), nch - 1);
+    const int pw = w3_first_word(pq);
+    const int wlo = pq == 3 ? 1 : 0, whi = pq == 1 || pq == 2 ? 3 : 4;  // used words [wlo, whi)
+    // dwords 5 pw .. 5 pw + 19 of the group's 64 (codes 10 pw .. 10 pw + 39)
+    const uint32_t* xg = reinterpret_cast<const uint32_t*>(X + (size_t)g * 128);
+    uint32_t d[20];
+#pragma unroll
+    for (int i = 0; i < 20; ++i) {
+      const int di = 5 * pw + i;
+      const uint32_t v = xg[min(di, 63)];
+      d[i] = di < 64 ? v : 0u;
+    }
+    uint32_t av[20];
+    float cs = 0.f, ss = 0.f;
+#pragma unroll
+    for (int P = 0; P < 20; ++P) {
+      const int w = P / 5, p = P % 5;
+      const bool use = w >= wlo && w < whi;
+      const int cl = 10 * w + kW3Lo[p], ch = 10 * w + kW3Hi[p];
+      const float xl = h2f((uint16_t)(d[cl >> 1] >> (16 * (cl & 1))));
+      const float xh = h2f((uint16_t)(d[ch >> 1] >> (16 * (ch & 1))));
+      // a code past the group's 128 only occurs for word 12 (c8, c9)
+      const bool lo_ok = use && 10 * (pw + w) + kW3Lo[p] < 128;
+      const bool hi_ok = use && 10 * (pw + w) + kW3Hi[p] < 128;
+      const __half al = __float2half_rn(lo_ok ? xl * kW3InvLo[p] : 0.f);
+      const __half ah = __float2half_rn(hi_ok ? xh * kW3InvHi[p] : 0.f);
+      av[P] = (uint32_t)__half_as_ushort(al) | ((uint32_t)__half_as_ushort(ah) << 16);
+      const float fl = __half2float(al), fh = __half2float(ah);
+      cs += fl + fh;
+      ss += fl * (1.f / kW3InvLo[p]) + fh * (1.f / kW3InvHi[p]);
+    }
+#pragma unroll
+    for (int o = 0; o < 5; ++o)
+      xs[ps][o][pl] = u32x4{av[4 * o], av[4 * o + 1], av[4 * o + 2], av[4 * o + 3]};
+    cs += __shfl_xor(cs, 16);
+    ss += __shfl_xor(ss, 16);
+    cs += __shfl_xor(cs, 32);
+    ss += __shfl_xor(ss, 32);
+    if (pl < 16) xcs[ps][pl] = make_float2(1024.f * cs, ss);
+  }
+  __syncthreads();
+  float cC[SP], cS[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    const float2 v = xcs[s][j];
+    cC[s] = v.x;
+    cS[s] = v.y;
+  }
+
+  // ring of RPF rows x SP pieces, filled without prologue loads (see the
+  // int4 kernel)
+  u32x4 wb[RPF][SP];
+  float db[RPF][SP];
+  uint32_t zb[RPF][SP];
+#pragma unroll
+  for (int r = 0; r < RPF; ++r)
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      wb[r][s] = u32x4{0, 0, 0, 0};
+      db[r][s] = 0.f;
+      zb[r][s] = 0u;
+    }
+  const int last = max(cnt - 1, 0);
+  const uint32_t magic = kMagic2;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* qlane = Q + woff;
+  float outv = 0.f;
+  for (int i0 = -RPF; i0 < cnt; i0 += RPF) {
+#pragma unroll
+    for (int r = 0; r < RPF; ++r) {
+      const int row = i0 + r;
+      const size_t nn = (size_t)min(gw + min(row + RPF, last) * NW, N - 1);  // refill target
+      __builtin_amdgcn_sched_barrier(0);
+      if (row >= 0) {  // uniform
+        const bool vrow = row < cnt;
+        float y = 0.f;
+#pragma unroll
+        for (int s = 0; s < SP; ++s) {
+          const u32x4 w = wb[r][s];
+          const float dd = (vrow && gval[s]) ? db[r][s] : 0.f;
+          const float zs = __builtin_fmaf((float)zb[r][s], cS[s], cC[s]);
+          uint32_t pr[20];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x = w[q];
+            const uint32_t t8 = x >> 8, u1 = x << 1;
+            pr[5 * q + 0] = and_or(x, 0x001C0007u, magic);
+            pr[5 * q + 1] = and_or(x, 0x00E00038u, magic);
+            pr[5 * q + 2] = and_or(t8, 0x0007000Eu, magic);
+            pr[5 * q + 3] = and_or(t8, 0x00380070u, magic);
+            pr[5 * q + 4] = and_or(u1, 0x00070380u, magic);
+          }
+          floatx4 acc = mfma16(xs[s][0][lane], u32x4{pr[0], pr[1], pr[2], pr[3]}, zero4);
+          acc = mfma16(xs[s][1][lane], u32x4{pr[4], pr[5], pr[6], pr[7]}, acc);
+          acc = mfma16(xs[s][2][lane], u32x4{pr[8], pr[9], pr[10], pr[11]}, acc);
+          acc = mfma16(xs[s][3][lane], u32x4{pr[12], pr[13], pr[14], pr[15]}, acc);
+          acc = mfma16(xs[s][4][lane], u32x4{pr[16], pr[17], pr[18], pr[19]}, acc);
+          float v = acc[0];
+          v = rdiag == 1 ? acc[1] : v;
+          v = rdiag == 2 ? acc[2] : v;
+          v = rdiag == 3 ? acc[3] : v;
+          y = __builtin_fmaf(dd, v - zs, y);
+        }
+        float v = diag ? y : 0.f;
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+        const float sum =
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
+        outv = (row & 63) == lane ? sum : outv;
+      }
+      const uint32_t* qn = qlane + nn * wpr;
+      const float* sn = S + nn * nch;
+      const uint8_t* zn = Z + nn * nch;
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
+        wb[r][s] = u32x4{v[0], v[1], v[2], v[3]};
+        db[r][s] = sn[goff[s]];
+        zb[r][s] = zn[goff[s]];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    }
+  }
+  if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
+}
+
+hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* scales,
+                             const uint8_t* zeros, int N, int K, int group, __half* Y,
+                             hipStream_t st) {
+  const int nch = K / 128;
+  const int sp = (nch + 15) / 16;
+  if (group != 128 || sp > 6) return hipErrorNotSupported;
+  const int wpr = words_per_row(K, 3, group);
+  const int nw = max(cu_count() * 8, (N + 63) / 64);
+  const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  const bool full = nch % 16 == 0;
+#define AWQ_W3(SM, RP)                                                                          \
+  do {                                                                                          \
+    if (full)                                                                                   \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true>), g1, block, 0, st, x, q, scales,     \
+                         zeros, y, N, K, wpr);                                                  \
+    else                                                                                        \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false>), g1, block, 0, st, x, q, scales,    \
+                         zeros, y, N, K, wpr);                                                  \
+  } while (0)
+  switch (sp) {
+    case 1: AWQ_W3(1, 4); break;
+    case 2: AWQ_W3(2, 2); break;
+    case 3: AWQ_W3(3, 2); break;
+    case 4: AWQ_W3(4, 1); break;
+    case 5: AWQ_W3(5, 1); break;
+    default: AWQ_W3(6, 1); break;
+  }
+#undef AWQ_W3
+  return hipGetLastError();
+}
+
 constexpr int kGemvPF = 8;
 constexpr int kGemvMaxRbw = 8;
 
