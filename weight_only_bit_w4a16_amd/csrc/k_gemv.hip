@@ -358,44 +358,62 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
   }
 
   // operand prep: thread (piece s, lane l) of the workgroup permutes the
-  // activations of quarter l/16 of group 16 s + l%16
-  for (int t = threadIdx.x; t < SP * 64; t += 256) {
-    const int ps = t >> 6, pl = t & 63;
-    const int g = min(16 * ps + (pl & 15), nch - 1);
-    uint32_t d[16];
-    load_x32(X + g * 128 + 32 * (pl >> 4), d);
-    // odd slots: x / 16 rounded to fp16
+  // activations of quarter l/16 of group 16 s + l%16. The activations are
+  // loaded first; for long rows (SP >= 3) the prep runs after the first ring
+  // loads are issued, so it overlaps their memory latency.
+  constexpr bool kLatePrep = SP >= 3;
+  constexpr int XI = (SP * 64 + 255) / 256;  // prep items per thread
+  uint32_t xd[XI][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float od = h2f((uint16_t)(d[i] >> 16)) * 0.0625f;
-      d[i] = (d[i] & 0xffffu) | ((uint32_t)__half_as_ushort(__float2half_rn(od)) << 16);
-    }
-    u32x4 o0, o1, o2, o3;
-    permute_x32(d, o0, o1, o2, o3);
-    xs[ps][0][pl] = o0;
-    xs[ps][1][pl] = o1;
-    xs[ps][2][pl] = o2;
-    xs[ps][3][pl] = o3;
-    float se = 0.f, so = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      se += h2f((uint16_t)(d[i] & 0xffffu));
-      so += h2f((uint16_t)(d[i] >> 16));
-    }
-    se += __shfl_xor(se, 16);
-    so += __shfl_xor(so, 16);
-    se += __shfl_xor(se, 32);
-    so += __shfl_xor(so, 32);
-    if (pl < 16) xcs[ps][pl] = make_float2(1024.f * (se + so), se + 16.f * so);
+  for (int u = 0; u < XI; ++u) {
+    const int t = min((int)threadIdx.x + 256 * u, SP * 64 - 1);
+    const int g = min(16 * (t >> 6) + (t & 15), nch - 1);
+    load_x32(X + g * 128 + 32 * ((t & 63) >> 4), xd[u]);
   }
-  __syncthreads();
   float cC[SP], cS[SP];
+  auto prep = [&]() {
 #pragma unroll
-  for (int s = 0; s < SP; ++s) {
-    const float2 v = xcs[s][j];
-    cC[s] = v.x;
-    cS[s] = v.y;
-  }
+    for (int u = 0; u < XI; ++u) {
+      const int t = (int)threadIdx.x + 256 * u;
+      const int ps = t >> 6, pl = t & 63;
+      uint32_t d[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) d[i] = xd[u][i];
+      // odd slots: x / 16 rounded to fp16
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float od = h2f((uint16_t)(d[i] >> 16)) * 0.0625f;
+        d[i] = (d[i] & 0xffffu) | ((uint32_t)__half_as_ushort(__float2half_rn(od)) << 16);
+      }
+      u32x4 o0, o1, o2, o3;
+      permute_x32(d, o0, o1, o2, o3);
+      float se = 0.f, so = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        se += h2f((uint16_t)(d[i] & 0xffffu));
+        so += h2f((uint16_t)(d[i] >> 16));
+      }
+      se += __shfl_xor(se, 16);
+      so += __shfl_xor(so, 16);
+      se += __shfl_xor(se, 32);
+      so += __shfl_xor(so, 32);
+      if (t < SP * 64) {  // wave-uniform: SP * 64 is a multiple of 64
+        xs[ps][0][pl] = o0;
+        xs[ps][1][pl] = o1;
+        xs[ps][2][pl] = o2;
+        xs[ps][3][pl] = o3;
+        if (pl < 16) xcs[ps][pl] = make_float2(1024.f * (se + so), se + 16.f * so);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      const float2 v = xcs[s][j];
+      cC[s] = v.x;
+      cS[s] = v.y;
+    }
+  };
+  if constexpr (!kLatePrep) prep();
 
   // Ring of RPF rows x SP pieces. There are no prologue loads: the loop
   // starts RPF rows early with an empty ring, so every load of the ring is
@@ -472,17 +490,23 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
       const uint32_t* qn = qlane + nn * wpr;
       const float* sn = S + nn * ngr;
       const uint8_t* zn = Z + nn * ngr;
+      // rows past this wavefront's last need no loads (uniform branch)
+      if (row + RPF < cnt) {
 #pragma unroll
-      for (int s = 0; s < SP; ++s) {
-        wb[r][s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
-        db[r][s] = sn[goff[s] >> gshift];
-        zb[r][s] = zn[goff[s] >> gshift];
+        for (int s = 0; s < SP; ++s) {
+          wb[r][s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
+          db[r][s] = sn[goff[s] >> gshift];
+          zb[r][s] = zn[goff[s] >> gshift];
+        }
       }
       // A no-op (wavefront-scope) fence after the loads: a memory-writing
       // instruction between the loads and the loop back edge keeps the
       // compiler from merging them with the other loads that feed the ring.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     }
+    // uniform: the first pass only fills the ring
+    if constexpr (kLatePrep)
+      if (i0 < 0) prep();
   }
   if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
 }
@@ -544,58 +568,71 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
   }
 
   // operand prep: thread (piece s, lane l) builds lane l's 40 activation
-  // slots of group 16 s + l%16
-  for (int t = threadIdx.x; t < SP * 64; t += 256) {
-    const int ps = t >> 6, pl = t & 63;
-    const int pq = pl >> 4;
-    const int g = min(16 * ps + (pl & 15), nch - 1);
-    const int pw = w3_first_word(pq);
-    const int wlo = pq == 3 ? 1 : 0, whi = pq == 1 || pq == 2 ? 3 : 4;  // used words [wlo, whi)
+  // slots of group 16 s + l%16. As in the int4 kernel the activations are
+  // loaded first and, for long rows, prepared while the first ring loads are
+  // in flight.
+  constexpr bool kLatePrep = SP >= 3;
+  constexpr int XI = (SP * 64 + 255) / 256;  // prep items per thread
+  uint32_t xd[XI][20];
+#pragma unroll
+  for (int u = 0; u < XI; ++u) {
+    const int t = min((int)threadIdx.x + 256 * u, SP * 64 - 1);
+    const int pl = t & 63;
+    const int g = min(16 * (t >> 6) + (pl & 15), nch - 1);
+    const int pw = w3_first_word(pl >> 4);
     // dwords 5 pw .. 5 pw + 19 of the group's 64 (codes 10 pw .. 10 pw + 39)
     const uint32_t* xg = reinterpret_cast<const uint32_t*>(X + (size_t)g * 128);
-    uint32_t d[20];
 #pragma unroll
-    for (int i = 0; i < 20; ++i) {
-      const int di = 5 * pw + i;
-      const uint32_t v = xg[min(di, 63)];
-      d[i] = di < 64 ? v : 0u;
-    }
-    uint32_t av[20];
-    float cs = 0.f, ss = 0.f;
-#pragma unroll
-    for (int P = 0; P < 20; ++P) {
-      const int w = P / 5, p = P % 5;
-      const bool use = w >= wlo && w < whi;
-      const int cl = 10 * w + kW3Lo[p], ch = 10 * w + kW3Hi[p];
-      const float xl = h2f((uint16_t)(d[cl >> 1] >> (16 * (cl & 1))));
-      const float xh = h2f((uint16_t)(d[ch >> 1] >> (16 * (ch & 1))));
-      // a code past the group's 128 only occurs for word 12 (c8, c9)
-      const bool lo_ok = use && 10 * (pw + w) + kW3Lo[p] < 128;
-      const bool hi_ok = use && 10 * (pw + w) + kW3Hi[p] < 128;
-      const __half al = __float2half_rn(lo_ok ? xl * kW3InvLo[p] : 0.f);
-      const __half ah = __float2half_rn(hi_ok ? xh * kW3InvHi[p] : 0.f);
-      av[P] = (uint32_t)__half_as_ushort(al) | ((uint32_t)__half_as_ushort(ah) << 16);
-      const float fl = __half2float(al), fh = __half2float(ah);
-      cs += fl + fh;
-      ss += fl * (1.f / kW3InvLo[p]) + fh * (1.f / kW3InvHi[p]);
-    }
-#pragma unroll
-    for (int o = 0; o < 5; ++o)
-      xs[ps][o][pl] = u32x4{av[4 * o], av[4 * o + 1], av[4 * o + 2], av[4 * o + 3]};
-    cs += __shfl_xor(cs, 16);
-    ss += __shfl_xor(ss, 16);
-    cs += __shfl_xor(cs, 32);
-    ss += __shfl_xor(ss, 32);
-    if (pl < 16) xcs[ps][pl] = make_float2(1024.f * cs, ss);
+    for (int i = 0; i < 20; ++i) xd[u][i] = xg[min(5 * pw + i, 63)];
   }
-  __syncthreads();
   float cC[SP], cS[SP];
+  auto prep = [&]() {
 #pragma unroll
-  for (int s = 0; s < SP; ++s) {
-    const float2 v = xcs[s][j];
-    cC[s] = v.x;
-    cS[s] = v.y;
-  }
+    for (int u = 0; u < XI; ++u) {
+      const int t = (int)threadIdx.x + 256 * u;
+      const int ps = t >> 6, pl = t & 63;
+      const int pq = pl >> 4;
+      const int pw = w3_first_word(pq);
+      const int wlo = pq == 3 ? 1 : 0, whi = pq == 1 || pq == 2 ? 3 : 4;  // used words [wlo, whi)
+      uint32_t av[20];
+      float cs = 0.f, ss = 0.f;
+#pragma unroll
+      for (int P = 0; P < 20; ++P) {
+        const int w = P / 5, p = P % 5;
+        const bool use = w >= wlo && w < whi;
+        const int cl = 10 * w + kW3Lo[p], ch = 10 * w + kW3Hi[p];
+        const float xl = h2f((uint16_t)(xd[u][cl >> 1] >> (16 * (cl & 1))));
+        const float xh = h2f((uint16_t)(xd[u][ch >> 1] >> (16 * (ch & 1))));
+        // a code past the group's 128 only occurs for word 12 (c8, c9)
+        const bool lo_ok = use && 10 * (pw + w) + kW3Lo[p] < 128;
+        const bool hi_ok = use && 10 * (pw + w) + kW3Hi[p] < 128;
+        const __half al = __float2half_rn(lo_ok ? xl * kW3InvLo[p] : 0.f);
+        const __half ah = __float2half_rn(hi_ok ? xh * kW3InvHi[p] : 0.f);
+        av[P] = (uint32_t)__half_as_ushort(al) | ((uint32_t)__half_as_ushort(ah) << 16);
+        const float fl = __half2float(al), fh = __half2float(ah);
+        cs += fl + fh;
+        ss += fl * (1.f / kW3InvLo[p]) + fh * (1.f / kW3InvHi[p]);
+      }
+      cs += __shfl_xor(cs, 16);
+      ss += __shfl_xor(ss, 16);
+      cs += __shfl_xor(cs, 32);
+      ss += __shfl_xor(ss, 32);
+      if (t < SP * 64) {  // wave-uniform: SP * 64 is a multiple of 64
+#pragma unroll
+        for (int o = 0; o < 5; ++o)
+          xs[ps][o][pl] = u32x4{av[4 * o], av[4 * o + 1], av[4 * o + 2], av[4 * o + 3]};
+        if (pl < 16) xcs[ps][pl] = make_float2(1024.f * cs, ss);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SP; ++s) {
+      const float2 v = xcs[s][j];
+      cC[s] = v.x;
+      cS[s] = v.y;
+    }
+  };
+  if constexpr (!kLatePrep) prep();
 
   // ring of RPF rows x SP pieces, filled without prologue loads (see the
   // int4 kernel)
@@ -666,15 +703,20 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
       const uint32_t* qn = qlane + nn * wpr;
       const float* sn = S + nn * nch;
       const uint8_t* zn = Z + nn * nch;
+      // rows past this wavefront's last need no loads (uniform branch)
+      if (row + RPF < cnt) {
 #pragma unroll
-      for (int s = 0; s < SP; ++s) {
-        const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
-        wb[r][s] = u32x4{v[0], v[1], v[2], v[3]};
-        db[r][s] = sn[goff[s]];
-        zb[r][s] = zn[goff[s]];
+        for (int s = 0; s < SP; ++s) {
+          const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
+          wb[r][s] = u32x4{v[0], v[1], v[2], v[3]};
+          db[r][s] = sn[goff[s]];
+          zb[r][s] = zn[goff[s]];
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     }
+    if constexpr (kLatePrep)
+      if (i0 < 0) prep();
   }
   if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
 }
