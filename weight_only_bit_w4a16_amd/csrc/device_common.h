@@ -22,6 +22,7 @@ constexpr uint32_t kMagic2 = 0x64006400u;
 // -ffp-contract=off and float division is correctly rounded.
 struct GroupGrid {
   float delta;
+  float rdelta;  // approximate 1 / delta (v_rcp_f32), used only to pick codes fast
   int z;
 };
 
@@ -37,13 +38,20 @@ __device__ __forceinline__ GroupGrid group_grid(float wmin, float wmax, int qmax
     g.delta = r / (float)qmax;
     g.z = (int)rintf(-lo / g.delta);
   }
+  g.rdelta = __builtin_amdgcn_rcpf(g.delta);
   return g;
 }
 
-// q = clamp(rint(w' / delta) + z, 0, qmax): the zero point is added after
-// rounding, as an integer.
+// q = clamp(rint(wp / delta) + z, 0, qmax) with wp / delta the correctly
+// rounded fp32 quotient. |wp / delta| <= qmax, and wp * rdelta is within
+// 2 ulp of the exact quotient, so it rounds to the same integer unless it
+// lies within a few ulp of a half-integer; only those (rare) lanes pay for
+// the IEEE division.
 __device__ __forceinline__ int quant_code(float wp, GroupGrid g, int qmax) {
-  const int q = (int)rintf(wp / g.delta) + g.z;
+  const float t = wp * g.rdelta;
+  float qf = rintf(t);
+  if (__builtin_fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 0x1p-16f) qf = rintf(wp / g.delta);
+  const int q = (int)qf + g.z;
   return q < 0 ? 0 : (q > qmax ? qmax : q);
 }
 

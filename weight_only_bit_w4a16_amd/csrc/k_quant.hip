@@ -16,95 +16,107 @@ namespace awq {
 // ---------------------------------------------------------------------------
 template <int BITS, int TPG>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ W,
-                                                         const float* __restrict__ s, int K,
+                                                         const float* __restrict__ s, int N, int K,
                                                          uint32_t* __restrict__ Q,
                                                          float* __restrict__ scales,
-                                                         uint8_t* __restrict__ zeros, int wpr,
-                                                         long total_groups) {
+                                                         uint8_t* __restrict__ zeros, int wpr) {
   constexpr int G = TPG * 8;
   constexpr int QMAX = (1 << BITS) - 1;
   const int ng = K / G;
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long gi_raw = gid / TPG;
-  const int j = (int)(gid % TPG);
-  const bool active = gi_raw < total_groups;
-  // inactive threads work on a valid group so every lane joins the shuffles
-  const long gi = active ? gi_raw : total_groups - 1;
-  const long n = gi / ng;
-  const int g = (int)(gi % ng);
-  const int k0 = g * G + 8 * j;
-
-  const uint4 raw = *reinterpret_cast<const uint4*>(W + n * K + k0);
-  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-  float wp[8];
+  // grid: x walks the K/8 threads of a row, y the rows (strided past 65535)
+  const int tr = blockIdx.x * 256 + threadIdx.x;
+  // threads past the row end form whole groups (K and 256 threads are
+  // multiples of the group); they work on the last group so every lane
+  // joins the shuffles, and store nothing
+  const bool active = tr < K / 8;
+  const int tt = active ? tr : K / 8 - TPG + (tr % TPG);
+  const int j = tt % TPG;
+  const int g = tt / TPG;
+  const int k0 = 8 * tt;
+  float sv[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wp[2 * i] = h2f((uint16_t)(rw[i] & 0xffffu));
-    wp[2 * i + 1] = h2f((uint16_t)(rw[i] >> 16));
-  }
+  for (int i = 0; i < 8; ++i) sv[i] = 1.0f;
   if (s != nullptr) {
     const float4 s0 = *reinterpret_cast<const float4*>(s + k0);
     const float4 s1 = *reinterpret_cast<const float4*>(s + k0 + 4);
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    sv[0] = s0.x, sv[1] = s0.y, sv[2] = s0.z, sv[3] = s0.w;
+    sv[4] = s1.x, sv[5] = s1.y, sv[6] = s1.z, sv[7] = s1.w;
+  }
+  // rows blockIdx.y, + gridDim.y, ...; the next row's load is issued before
+  // the current row is processed
+  uint4 raw = *reinterpret_cast<const uint4*>(W + (size_t)blockIdx.y * K + k0);
+  for (int nr = blockIdx.y; nr < N; nr += gridDim.y) {
+    const size_t n = (size_t)nr;
+    const int nx = min(nr + (int)gridDim.y, N - 1);
+    const uint4 next = *reinterpret_cast<const uint4*>(W + (size_t)nx * K + k0);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    raw = next;
+    float wp[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wp[2 * i] = h2f((uint16_t)(rw[i] & 0xffffu));
+      wp[2 * i + 1] = h2f((uint16_t)(rw[i] >> 16));
+    }
+    // s == 1 multiplies exactly, so plain RTN takes the same path
 #pragma unroll
     for (int i = 0; i < 8; ++i) wp[i] = wp[i] * sv[i];
-  }
-  float mn = wp[0], mx = wp[0];
+    float mn = wp[0], mx = wp[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = fminf(mn, wp[i]);
-    mx = fmaxf(mx, wp[i]);
-  }
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, wp[i]);
+      mx = fmaxf(mx, wp[i]);
+    }
 #pragma unroll
-  for (int off = 1; off < TPG; off <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, TPG));
-    mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
-  }
-  const GroupGrid gg = group_grid(mn, mx, QMAX);
-  uint32_t packed = 0;
+    for (int off = 1; off < TPG; off <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off, TPG));
+      mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
+    }
+    const GroupGrid gg = group_grid(mn, mx, QMAX);
+    uint32_t packed = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= (uint32_t)quant_code(wp[i], gg, QMAX) << (BITS * i);
+    for (int i = 0; i < 8; ++i) packed |= (uint32_t)quant_code(wp[i], gg, QMAX) << (BITS * i);
 
-  uint32_t* qrow = Q + n * wpr;
-  if (BITS == 4) {
-    if (active) qrow[g * (G / 8) + j] = packed;
-  } else {
-    constexpr int WPG = (G + 9) / 10;
-    // word w holds codes 10w .. 10w+9, which lie in the 8-code blocks t1, t1+1
-    const int w = j;
-    const int t1 = (10 * w) >> 3;
-    const uint32_t lo24 = __shfl(packed, t1 < TPG ? t1 : TPG - 1, TPG);
-    const uint32_t hi24 = __shfl(packed, t1 + 1 < TPG ? t1 + 1 : TPG - 1, TPG);
-    const uint64_t both = (uint64_t)lo24 | ((uint64_t)(t1 + 1 < TPG ? hi24 : 0u) << 24);
-    const int first = 10 * w - 8 * t1;          // code offset inside block t1
-    const int left = G - 10 * w;  // codes of this group from slot 0 of word w on
-    const int count = left < 0 ? 0 : (left < 10 ? left : 10);
-    uint32_t word = (uint32_t)(both >> (3 * first));
-    word &= count >= 10 ? 0x3fffffffu : ((1u << (3 * count)) - 1u);
-    if (active) {
-      if (w < WPG) {
-        qrow[g * WPG + w] = word;
-      } else if (g == ng - 1 && g * WPG + w < wpr) {
-        qrow[g * WPG + w] = 0u;  // row padding to 16 bytes
+    uint32_t* qrow = Q + n * wpr;
+    if (BITS == 4) {
+      if (active) qrow[g * (G / 8) + j] = packed;
+    } else {
+      constexpr int WPG = (G + 9) / 10;
+      // word w holds codes 10w .. 10w+9, which lie in the 8-code blocks t1, t1+1
+      const int w = j;
+      const int t1 = (10 * w) >> 3;
+      const uint32_t lo24 = __shfl(packed, t1 < TPG ? t1 : TPG - 1, TPG);
+      const uint32_t hi24 = __shfl(packed, t1 + 1 < TPG ? t1 + 1 : TPG - 1, TPG);
+      const uint64_t both = (uint64_t)lo24 | ((uint64_t)(t1 + 1 < TPG ? hi24 : 0u) << 24);
+      const int first = 10 * w - 8 * t1;          // code offset inside block t1
+      const int left = G - 10 * w;  // codes of this group from slot 0 of word w on
+      const int count = left < 0 ? 0 : (left < 10 ? left : 10);
+      uint32_t word = (uint32_t)(both >> (3 * first));
+      word &= count >= 10 ? 0x3fffffffu : ((1u << (3 * count)) - 1u);
+      if (active) {
+        if (w < WPG) {
+          qrow[g * WPG + w] = word;
+        } else if (g == ng - 1 && g * WPG + w < wpr) {
+          qrow[g * WPG + w] = 0u;  // row padding to 16 bytes
+        }
       }
     }
-  }
-  if (active && j == 0) {
-    scales[n * ng + g] = gg.delta;
-    zeros[n * ng + g] = (uint8_t)gg.z;
+    if (active && j == 0) {
+      scales[n * ng + g] = gg.delta;
+      zeros[n * ng + g] = (uint8_t)gg.z;
+    }
   }
 }
 
 hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int bits, int group,
                              uint32_t* q, float* scales, uint8_t* zeros, hipStream_t st) {
   const int wpr = words_per_row(K, bits, group);
-  const long total = (long)N * (K / group);
-  const long threads = total * (group / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  // about 4 rows per thread
+  const int gy = (N + 3) / 4 < 65535 ? (N + 3) / 4 : 65535;
+  const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)gy);
   const uint16_t* w = reinterpret_cast<const uint16_t*>(W);
-#define AWQ_QP(B, T)                                                                        \
-  hipLaunchKernelGGL((quant_pack_kernel<B, T>), grid, dim3(256), 0, st, w, s, K, q, scales, \
-                     zeros, wpr, total)
+#define AWQ_QP(B, T)                                                                           \
+  hipLaunchKernelGGL((quant_pack_kernel<B, T>), grid, dim3(256), 0, st, w, s, N, K, q, scales, \
+                     zeros, wpr)
   if (bits == 4) {
     if (group == 128) AWQ_QP(4, 16);
     else if (group == 256) AWQ_QP(4, 32);
@@ -119,64 +131,93 @@ hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int 
 }
 
 // ---------------------------------------------------------------------------
-// X' = fp16(float32(X) / s), 8 elements per thread.
+// X' = fp16(float32(X) / s), 8 elements per thread, the quotient correctly
+// rounded to fp32 and then to fp16. x * (1/s) with the hardware reciprocal is
+// within 2 ulp (fp32) of the correctly rounded quotient, so it rounds to the
+// same fp16 unless its 13 dropped mantissa bits lie within a few ulp of the
+// fp16 midpoint, or the result is an fp16 subnormal; those lanes divide.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fold_one(float x, float sv, float rs) {
+  float t = x * rs;
+  const uint32_t low = __float_as_uint(t) & 0x1fffu;
+  const uint32_t dist = low > 0x1000u ? low - 0x1000u : 0x1000u - low;
+  if (dist <= 8u || __builtin_fabsf(t) < 0x1p-14f) t = x / sv;
+  return (uint32_t)__half_as_ushort(__float2half_rn(t));
+}
+
 __global__ __launch_bounds__(256) void fold_kernel(const uint16_t* __restrict__ X,
-                                                   const float* __restrict__ s, int K, long total8,
+                                                   const float* __restrict__ s, int M, int K,
                                                    uint16_t* __restrict__ Y) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total8) return;
-  const long e = i * 8;
-  const int k = (int)(e % K);
-  const uint4 raw = *reinterpret_cast<const uint4*>(X + e);
+  const int k = 8 * (blockIdx.x * 256 + threadIdx.x);
+  if (k >= K) return;
   const float4 s0 = *reinterpret_cast<const float4*>(s + k);
   const float4 s1 = *reinterpret_cast<const float4*>(s + k + 4);
   const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t out[4];
+  float rs[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float a = h2f((uint16_t)(rw[p] & 0xffffu)) / sv[2 * p];
-    const float b = h2f((uint16_t)(rw[p] >> 16)) / sv[2 * p + 1];
-    out[p] = (uint32_t)__half_as_ushort(__float2half_rn(a)) |
-             ((uint32_t)__half_as_ushort(__float2half_rn(b)) << 16);
+  for (int i = 0; i < 8; ++i) rs[i] = __builtin_amdgcn_rcpf(sv[i]);
+  // rows blockIdx.y, + gridDim.y, ...; the next row's load is issued first
+  uint4 raw = *reinterpret_cast<const uint4*>(X + (size_t)blockIdx.y * K + k);
+  for (int mr = blockIdx.y; mr < M; mr += gridDim.y) {
+    const size_t e = (size_t)mr * K + k;
+    const int mx = min(mr + (int)gridDim.y, M - 1);
+    const uint4 next = *reinterpret_cast<const uint4*>(X + (size_t)mx * K + k);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    raw = next;
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      out[p] = fold_one(h2f((uint16_t)(rw[p] & 0xffffu)), sv[2 * p], rs[2 * p]) |
+               (fold_one(h2f((uint16_t)(rw[p] >> 16)), sv[2 * p + 1], rs[2 * p + 1]) << 16);
+    *reinterpret_cast<uint4*>(Y + e) = make_uint4(out[0], out[1], out[2], out[3]);
   }
-  *reinterpret_cast<uint4*>(Y + e) = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 hipError_t launch_fold(const __half* X, const float* s, int M, int K, __half* Y, hipStream_t st) {
-  const long total8 = (long)M * K / 8;
-  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint16_t*>(X), s, K, total8,
-                     reinterpret_cast<uint16_t*>(Y));
+  const int gy = (M + 3) / 4 < 65535 ? (M + 3) / 4 : 65535;  // about 4 rows per thread
+  const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)gy);
+  hipLaunchKernelGGL(fold_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(X), s,
+                     M, K, reinterpret_cast<uint16_t*>(Y));
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // m[k] = sum_t |x[t,k]| / T in float64. The fp16 sum is exact in float64
-// for T < 8192, so the split over 4 token slices does not change the result.
-// Block = 64 columns x 4 token slices.
+// for T < 8192, so the split over 16 token slices does not change the result.
+// Block = 64 columns x 16 token slices (one wavefront per slice); each
+// thread keeps 8 independent loads in flight.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void act_stats_kernel(const uint16_t* __restrict__ X, int T,
-                                                        int K, double* __restrict__ m) {
-  __shared__ double part[4][64];
+__global__ __launch_bounds__(1024) void act_stats_kernel(const uint16_t* __restrict__ X, int T,
+                                                         int K, double* __restrict__ m) {
+  __shared__ double part[16][64];
   const int c = threadIdx.x & 63;
   const int slice = threadIdx.x >> 6;
   const int k = blockIdx.x * 64 + c;
   double acc = 0.0;
   if (k < K) {
-    for (int t = slice; t < T; t += 4) acc += fabs((double)h2f(X[(long)t * K + k]));
+    const uint16_t* xc = X + k;
+    int t = slice;
+    for (; t + 16 * 7 < T; t += 16 * 8) {
+      uint16_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = xc[(size_t)(t + 16 * u) * K];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += fabs((double)h2f(v[u]));
+    }
+    for (; t < T; t += 16) acc += fabs((double)h2f(xc[(size_t)t * K]));
   }
   part[slice][c] = acc;
   __syncthreads();
   if (slice == 0 && k < K) {
-    const double sum = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += part[i][c];
     m[k] = sum / (double)T;
   }
 }
 
 hipError_t launch_act_stats(const __half* X, int T, int K, double* m, hipStream_t st) {
-  hipLaunchKernelGGL(act_stats_kernel, dim3((K + 63) / 64), dim3(256), 0, st,
+  hipLaunchKernelGGL(act_stats_kernel, dim3((K + 63) / 64), dim3(1024), 0, st,
                      reinterpret_cast<const uint16_t*>(X), T, K, m);
   return hipGetLastError();
 }

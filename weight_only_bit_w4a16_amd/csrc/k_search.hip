@@ -24,69 +24,75 @@ namespace {
 // (same group grid, same rounding), one thread per 8 codes of a group.
 template <int BITS, int TPG>
 __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* __restrict__ W,
-                                                               const float* __restrict__ s, int K,
-                                                               uint16_t* __restrict__ D,
-                                                               long total_groups) {
+                                                               const float* __restrict__ s, int N,
+                                                               int K, uint16_t* __restrict__ D) {
   constexpr int G = TPG * 8;
   constexpr int QMAX = (1 << BITS) - 1;
-  const int ng = K / G;
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long gi_raw = gid / TPG;
-  const int j = (int)(gid % TPG);
-  const bool active = gi_raw < total_groups;
-  const long gi = active ? gi_raw : total_groups - 1;
-  const long n = gi / ng;
-  const int g = (int)(gi % ng);
-  const int k0 = g * G + 8 * j;
-  const uint4 raw = *reinterpret_cast<const uint4*>(W + n * K + k0);
-  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+  // grid: x walks the K/8 threads of a row, y the rows (strided past 65535);
+  // threads past the row end work on the last group and store nothing
+  const int tr = blockIdx.x * 256 + threadIdx.x;
+  const bool active = tr < K / 8;
+  const int tt = active ? tr : K / 8 - TPG + (tr % TPG);
+  const int k0 = 8 * tt;
   const float4 s0 = *reinterpret_cast<const float4*>(s + k0);
   const float4 s1 = *reinterpret_cast<const float4*>(s + k0 + 4);
   const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-  float w[8], wp[8];
+  // rows blockIdx.y, + gridDim.y, ...; the next row's load is issued before
+  // the current row is processed
+  uint4 raw = *reinterpret_cast<const uint4*>(W + (size_t)blockIdx.y * K + k0);
+  for (int nr = blockIdx.y; nr < N; nr += gridDim.y) {
+    const size_t n = (size_t)nr;
+    const int nx = min(nr + (int)gridDim.y, N - 1);
+    const uint4 next = *reinterpret_cast<const uint4*>(W + (size_t)nx * K + k0);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    raw = next;
+    float w[8], wp[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[2 * i] = h2f((uint16_t)(rw[i] & 0xffffu));
-    w[2 * i + 1] = h2f((uint16_t)(rw[i] >> 16));
-  }
-  float mn, mx;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    wp[i] = w[i] * sv[i];
-    mn = i == 0 ? wp[i] : fminf(mn, wp[i]);
-    mx = i == 0 ? wp[i] : fmaxf(mx, wp[i]);
-  }
-#pragma unroll
-  for (int off = 1; off < TPG; off <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, TPG));
-    mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
-  }
-  const GroupGrid gg = group_grid(mn, mx, QMAX);
-  // D = hi + lo with hi = fp16(D), lo = fp16(D - hi): about 22 significant
-  // bits, so the fp16 contraction of both parts is accurate to ~1e-6
-  uint32_t hi[4], lo[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t h[2], l[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int i = 2 * p + e;
-      const int q = quant_code(wp[i], gg, QMAX);
-      const float back = ((float)(q - gg.z) * gg.delta) / sv[i];
-      const float dv = w[i] - back;
-      const __half dh = __float2half_rn(dv);
-      h[e] = __half_as_ushort(dh);
-      l[e] = __half_as_ushort(__float2half_rn(dv - __half2float(dh)));
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = h2f((uint16_t)(rw[i] & 0xffffu));
+      w[2 * i + 1] = h2f((uint16_t)(rw[i] >> 16));
     }
-    hi[p] = h[0] | (h[1] << 16);
-    lo[p] = l[0] | (l[1] << 16);
-  }
-  if (active) {
-    // row n of D is [2K]: k-chunk c (128 wide) -> hi at 256c, lo at 256c + 128
-    const int c = k0 >> 7, off = k0 & 127;
-    uint16_t* row = D + n * 2 * K + 256 * c + off;
-    *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4*>(row + 128) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    float mn, mx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wp[i] = w[i] * sv[i];
+      mn = i == 0 ? wp[i] : fminf(mn, wp[i]);
+      mx = i == 0 ? wp[i] : fmaxf(mx, wp[i]);
+    }
+#pragma unroll
+    for (int off = 1; off < TPG; off <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off, TPG));
+      mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
+    }
+    const GroupGrid gg = group_grid(mn, mx, QMAX);
+    // D = hi + lo with hi = fp16(D), lo = fp16(D - hi): about 22 significant
+    // bits, so the fp16 contraction of both parts is accurate to ~1e-6
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t h[2], l[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * p + e;
+        const int q = quant_code(wp[i], gg, QMAX);
+        // the codes are exact; the error term only feeds the loss, so the
+        // division by s uses the hardware reciprocal (within 1 ulp)
+        const float back = ((float)(q - gg.z) * gg.delta) * __builtin_amdgcn_rcpf(sv[i]);
+        const float dv = w[i] - back;
+        const __half dh = __float2half_rn(dv);
+        h[e] = __half_as_ushort(dh);
+        l[e] = __half_as_ushort(__float2half_rn(dv - __half2float(dh)));
+      }
+      hi[p] = h[0] | (h[1] << 16);
+      lo[p] = l[0] | (l[1] << 16);
+    }
+    if (active) {
+      // row n of D is [2K]: k-chunk c (128 wide) -> hi at 256c, lo at 256c + 128
+      const int c = k0 >> 7, off = k0 & 127;
+      uint16_t* row = D + n * 2 * K + 256 * c + off;
+      *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(row + 128) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
   }
 }
 
@@ -161,13 +167,12 @@ hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
   if (e != hipSuccess) return e;
   e = launch_scale_candidates(m, K, alpha_dev, n_alpha, s_all, st);
   if (e != hipSuccess) return e;
-  const long groups = (long)N * (K / group);
-  const long threads = groups * (group / 8);
-  const dim3 fgrid((unsigned)((threads + 255) / 256));
+  const int gy = (N + 3) / 4 < 65535 ? (N + 3) / 4 : 65535;  // about 4 rows per thread
+  const dim3 fgrid((unsigned)((K / 8 + 255) / 256), (unsigned)gy);
   for (int a = 0; a < n_alpha; ++a) {
     const float* s = s_all + (size_t)a * K;
 #define AWQ_FQ(B, TP) \
-  hipLaunchKernelGGL((fake_quant_error_kernel<B, TP>), fgrid, dim3(256), 0, st, w, s, K, D, groups)
+  hipLaunchKernelGGL((fake_quant_error_kernel<B, TP>), fgrid, dim3(256), 0, st, w, s, N, K, D)
     if (bits == 4) {
       if (group == 128) AWQ_FQ(4, 16);
       else if (group == 256) AWQ_FQ(4, 32);
