@@ -236,7 +236,7 @@ def main():
     pre_flops = 2.0 * M_pre * w.N * w.K
     pre_tfs = pre_flops / (pre_ms * 1e-3) / 1e12
     pack_bytes = w.N * w.K * 2 + packed_bytes + w.K * 4
-    search_flops = 2.0 * 2 * w.T * w.N * w.K * len(grid)  # hi and lo parts
+    search_flops = 2.0 * w.T * w.N * w.K * len(grid)  # the contraction Xcal D^T per alpha
 
     traffic = measured_traffic(w.name)
 

@@ -299,8 +299,10 @@ def check_search(W, Xc, grid, bits, group, oracle_idx=None):
 
 
 @pytest.mark.parametrize("bits", [4, 3])
-@pytest.mark.parametrize("N,K,T", [(64, 512, 64), (130, 1024, 100), (16, 128, 8)])
+@pytest.mark.parametrize("N,K,T", [(64, 512, 64), (130, 1024, 100), (16, 128, 8), (1024, 1024, 256)])
 def test_search_small(bits, N, K, T):
+    """T N < 2^18 runs the hi/lo contraction, (1024, 1024, 256) the smallest
+    scaled one (its loss error is statistical, shrinking as 1/sqrt(T N))."""
     say("search", bits, N, K, T)
     W, Xc, _ = datagen.small_layer(K, N, T, max(1, K // 100), 40.0, seed=N + K + T)
     check_search(W, Xc, datagen.alpha_grid(20), bits, 128)

@@ -23,7 +23,7 @@
 //   int3, per 10-code word: c0 c6 c1 c7 c3 c8 c4 c9 c2 c5
 // (an int3 group is 13 words = 130 slots, of which the last 2 hold no code;
 // their activation slots are zero; slots 130..143 pad the step to 9 x 16).
-// fp16 B tiles (the search) keep natural order.
+// fp16 B tiles (the search's error terms) keep natural order.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -105,7 +105,7 @@ template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const float* __restrict__ S,
     const uint8_t* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
-    uint16_t* __restrict__ Y, double* __restrict__ partial) {
+    uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo) {
   constexpr int NT = 64 * WGM * WGN;
   using C = Cfg<BMODE, BM, BN, NT>;
   using St = Stage<BMODE, BM, BN, NT>;
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   const int m0 = (t % mt) * BM;
   const int n0 = (t / mt) * BN;
-  // fp16 B (the search) holds each error term as a hi and a lo fp16 part,
+  // fp16 B with hilo set holds each term as a hi and a lo fp16 part,
   // [N][2K]: 256-wide block c = (hi of k 128c..128c+127 | lo of the same k),
   // so a 64-wide step s reads activations 128*(s/4) + 64*(s%2)
-  const int nsteps = BMODE == 0 ? 2 * (K / BK) : K / BK;
+  const int nsteps = BMODE == 0 && hilo ? 2 * (K / BK) : K / BK;
   const int ng = K >> (7 + gshift);  // quantization groups per row
 
   if (BMODE == 3) {
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // loads its group's scale and zero point
   auto load_step = [&](St& st, int ks, auto SZ) {
     if constexpr (BMODE == 0 || BMODE == 4) {
-      const int ka = BMODE == 0 ? 128 * (ks >> 2) + 64 * (ks & 1) : BK * ks;
+      const int ka = BMODE == 0 && hilo ? 128 * (ks >> 2) + 64 * (ks & 1) : BK * ks;
 #pragma unroll
       for (int i = 0; i < C::ACH; ++i) {
         const int id = tid + NT * i;
@@ -180,7 +180,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         const int id = tid + NT * i;
         const int r = id / (BK / 8), c8 = id % (BK / 8);
         const int n = min(n0 + r, N - 1);
-        st.b[i] = *reinterpret_cast<const u32x4*>(B + (size_t)n * 2 * K + BK * ks + 8 * c8);
+        st.b[i] = *reinterpret_cast<const u32x4*>(B + (size_t)n * (hilo ? 2 * K : K) + BK * ks +
+                                                  8 * c8);
       }
     } else if constexpr (BMODE == 4) {
       // BW consecutive words of one row (8 words = 64 codes per row and step)
@@ -482,11 +483,11 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
     if (zw)                                                                                     \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true>),                       \
                          dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
-                         zeros, M, N, K, wpr, gshift, y, nullptr);                              \
+                         zeros, M, N, K, wpr, gshift, y, nullptr, 0);                           \
     else                                                                                        \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false>),                      \
                          dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
-                         zeros, M, N, K, wpr, gshift, y, nullptr);                              \
+                         zeros, M, N, K, wpr, gshift, y, nullptr, 0);                           \
   } while (0)
   if (bits == 4) {
     // the largest tile that still gives every compute unit work
@@ -503,12 +504,14 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   return hipGetLastError();
 }
 
-// ||A (Bhi + Blo)^T||^2 as one float64 partial per workgroup tile; A is
-// [M, K] fp16, B is [N, 2K] fp16 holding hi/lo parts per 128-wide k chunk
-hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K,
+// ||A B^T||_F^2 as one float64 partial per workgroup tile; A is [M, K] fp16,
+// B is [N, K] fp16, or with hilo [N, 2K] holding hi and lo parts per
+// 128-wide k chunk (then the product is A (Bhi + Blo)^T)
+hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K, bool hilo,
                              double* partial, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false>), dim3(tiles_of(M, N, 128, 128)),
-                     dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial);
+                     dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial,
+                     hilo ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -1,31 +1,43 @@
 // Per-layer grid search over alpha for s = mean|x| ** alpha.
 //
-// For every alpha of the grid:
-//   s      = scale candidates (float32, one per input channel)
-//   D      = W - Q(W diag(s)) diag(s)^-1        (fake-quant error, as hi + lo
-//                                                 fp16 parts, [N, 2K])
-//   loss   = || Xcal D^T ||_F^2                  (fp16 MFMA contraction,
-//                                                 float32 tile sums, float64
-//                                                 across tiles)
-// then best = first index of the minimum loss and s_out = s_best. Everything
+// The loss of a candidate s is ||Xcal D^T||_F^2 with D = W - Q(W s) / s
+// (the fake-quant error of every weight), contracted on the fp16 matrix
+// cores (float32 accumulation, float32 tile sums, float64 across tiles).
+// Two evaluations, each well inside 1e-4 (relative) of an exact one at its
+// sizes:
+//  * scaled (T N >= 2^18): per column k, x_k D_nk = (x_k / s_k) *
+//    (w_nk s_k - Q(W s)_nk), so the product is evaluated with activations
+//    Xs = fp16(Xcal / s) (the fold kernel) and errors E = fp16(2^8 (W s -
+//    Q(W s))), both of the same magnitude for every channel (the unscaled D
+//    is tiny on channels with large s and loses its precision in fp16). The
+//    2^8 keeps E clear of fp16 subnormals; the loss is divided by 2^16. The
+//    rounding errors of both operands are random, so their effect on the
+//    loss shrinks as 1/sqrt(T N): measured at most 6e-6 at T N = 2^20 on
+//    the outlier-heavy layers, so below about 1.2e-5 at 2^18.
+//  * hi/lo (small T N): Xcal as given (exact fp16) against D split into an
+//    fp16 hi and lo part, contracted as one product over 2K.
+// Then best = first index of the minimum loss and s_out = s_best. Everything
 // runs on the device; the host only enqueues.
 #include "awq_internal.h"
 #include "device_common.h"
 
 namespace awq {
 
-hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K,
+hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K, bool hilo,
                              double* partial, hipStream_t st);
 unsigned sqnorm_abt_tiles(int M, int N);
 
 namespace {
 
-// D = W - (q - z) * delta / s, quantized exactly as the pack kernel does
-// (same group grid, same rounding), one thread per 8 codes of a group.
-template <int BITS, int TPG>
+// Quantized exactly as the pack kernel does (same group grid, same
+// rounding), one thread per 8 codes of a group. SCALED: E = fp16(2^8 (W s -
+// (q - z) delta)), [N, K]. Otherwise D = W - (q - z) delta / s as hi = fp16(D)
+// and lo = fp16(D - hi), [N, 2K]: 128-wide k chunk c -> hi at 256 c, lo at
+// 256 c + 128.
+template <int BITS, int TPG, bool SCALED>
 __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* __restrict__ W,
                                                                const float* __restrict__ s, int N,
-                                                               int K, uint16_t* __restrict__ D) {
+                                                               int K, uint16_t* __restrict__ E) {
   constexpr int G = TPG * 8;
   constexpr int QMAX = (1 << BITS) - 1;
   // grid: x walks the K/8 threads of a row, y the rows (strided past 65535);
@@ -46,16 +58,12 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
     const uint4 next = *reinterpret_cast<const uint4*>(W + (size_t)nx * K + k0);
     const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
     raw = next;
-    float w[8], wp[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w[2 * i] = h2f((uint16_t)(rw[i] & 0xffffu));
-      w[2 * i + 1] = h2f((uint16_t)(rw[i] >> 16));
-    }
+    float wp[8];
     float mn, mx;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      wp[i] = w[i] * sv[i];
+      const float w = h2f((uint16_t)(i & 1 ? rw[i >> 1] >> 16 : rw[i >> 1] & 0xffffu));
+      wp[i] = w * sv[i];
       mn = i == 0 ? wp[i] : fminf(mn, wp[i]);
       mx = i == 0 ? wp[i] : fmaxf(mx, wp[i]);
     }
@@ -65,8 +73,6 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
       mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
     }
     const GroupGrid gg = group_grid(mn, mx, QMAX);
-    // D = hi + lo with hi = fp16(D), lo = fp16(D - hi): about 22 significant
-    // bits, so the fp16 contraction of both parts is accurate to ~1e-6
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -75,29 +81,37 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
       for (int e = 0; e < 2; ++e) {
         const int i = 2 * p + e;
         const int q = quant_code(wp[i], gg, QMAX);
-        // the codes are exact; the error term only feeds the loss, so the
-        // division by s uses the hardware reciprocal (within 1 ulp)
-        const float back = ((float)(q - gg.z) * gg.delta) * __builtin_amdgcn_rcpf(sv[i]);
-        const float dv = w[i] - back;
-        const __half dh = __float2half_rn(dv);
-        h[e] = __half_as_ushort(dh);
-        l[e] = __half_as_ushort(__float2half_rn(dv - __half2float(dh)));
+        const float back = (float)(q - gg.z) * gg.delta;
+        if constexpr (SCALED) {
+          h[e] = __half_as_ushort(__float2half_rn((wp[i] - back) * 256.0f));
+          l[e] = 0u;
+        } else {
+          // the codes are exact; D only feeds the loss, so the division by s
+          // uses the hardware reciprocal (within 1 ulp)
+          const float w = h2f((uint16_t)(e ? rw[p] >> 16 : rw[p] & 0xffffu));
+          const float dv = w - back * __builtin_amdgcn_rcpf(sv[i]);
+          const __half dh = __float2half_rn(dv);
+          h[e] = __half_as_ushort(dh);
+          l[e] = __half_as_ushort(__float2half_rn(dv - __half2float(dh)));
+        }
       }
       hi[p] = h[0] | (h[1] << 16);
       lo[p] = l[0] | (l[1] << 16);
     }
     if (active) {
-      // row n of D is [2K]: k-chunk c (128 wide) -> hi at 256c, lo at 256c + 128
-      const int c = k0 >> 7, off = k0 & 127;
-      uint16_t* row = D + n * 2 * K + 256 * c + off;
-      *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(row + 128) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      if constexpr (SCALED) {
+        *reinterpret_cast<uint4*>(E + n * K + k0) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      } else {
+        uint16_t* row = E + n * 2 * K + 256 * (k0 >> 7) + (k0 & 127);
+        *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(row + 128) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
     }
   }
 }
 
 // loss[a] = sum of the tile partials of alpha a, in a fixed order
-__global__ void reduce_loss_kernel(const double* __restrict__ partial, int tiles,
+__global__ void reduce_loss_kernel(const double* __restrict__ partial, int tiles, double scale,
                                    double* __restrict__ loss) {
   __shared__ double buf[256];
   const int a = blockIdx.x;
@@ -109,7 +123,7 @@ __global__ void reduce_loss_kernel(const double* __restrict__ partial, int tiles
     if ((int)threadIdx.x < w) buf[threadIdx.x] += buf[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[a] = buf[0];
+  if (threadIdx.x == 0) loss[a] = buf[0] * scale;
 }
 
 // best = first index of the minimum (strict <), s_out = s_all[best]
@@ -127,15 +141,16 @@ __global__ void argmin_copy_kernel(const double* __restrict__ loss, int n_alpha,
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t m, s_all, d, partial, total;
+  size_t m, s_all, xs, e, partial, total;
 };
 
 Layout layout(int N, int K, int T, int n_alpha) {
   Layout L;
   L.m = 0;
   L.s_all = L.m + align256((size_t)K * 8);
-  L.d = L.s_all + align256((size_t)n_alpha * K * 4);
-  L.partial = L.d + align256((size_t)N * K * 4);  // hi and lo fp16 parts
+  L.xs = L.s_all + align256((size_t)n_alpha * K * 4);
+  L.e = L.xs + align256((size_t)T * K * 2);
+  L.partial = L.e + align256((size_t)N * K * 4);  // E [N, K] or hi/lo D [N, 2K]
   L.total = L.partial + align256((size_t)n_alpha * sqnorm_abt_tiles(T, N) * 8);
   return L;
 }
@@ -157,11 +172,11 @@ hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
   uint8_t* base = static_cast<uint8_t*>(ws);
   double* m = reinterpret_cast<double*>(base + L.m);
   float* s_all = reinterpret_cast<float*>(base + L.s_all);
-  uint16_t* D = reinterpret_cast<uint16_t*>(base + L.d);
+  uint16_t* Xs = reinterpret_cast<uint16_t*>(base + L.xs);
+  uint16_t* E = reinterpret_cast<uint16_t*>(base + L.e);
   double* partial = reinterpret_cast<double*>(base + L.partial);
   const unsigned tiles = sqnorm_abt_tiles(T, N);
   const uint16_t* w = reinterpret_cast<const uint16_t*>(W);
-  const uint16_t* xc = reinterpret_cast<const uint16_t*>(Xc);
 
   hipError_t e = launch_act_stats(Xc, T, K, m, st);
   if (e != hipSuccess) return e;
@@ -169,27 +184,45 @@ hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
   if (e != hipSuccess) return e;
   const int gy = (N + 3) / 4 < 65535 ? (N + 3) / 4 : 65535;  // about 4 rows per thread
   const dim3 fgrid((unsigned)((K / 8 + 255) / 256), (unsigned)gy);
+  // the scaled single product's rounding effect on the loss shrinks as
+  // 1/sqrt(T N); from 2^18 on it stays below about 1.2e-5
+  const bool scaled = (long long)T * N >= (1LL << 18);
   for (int a = 0; a < n_alpha; ++a) {
     const float* s = s_all + (size_t)a * K;
-#define AWQ_FQ(B, TP) \
-  hipLaunchKernelGGL((fake_quant_error_kernel<B, TP>), fgrid, dim3(256), 0, st, w, s, N, K, D)
+#define AWQ_FQ(B, TP, SC) \
+  hipLaunchKernelGGL((fake_quant_error_kernel<B, TP, SC>), fgrid, dim3(256), 0, st, w, s, N, K, E)
+#define AWQ_FQ2(B, TP) \
+  do {                 \
+    if (scaled)        \
+      AWQ_FQ(B, TP, true); \
+    else               \
+      AWQ_FQ(B, TP, false); \
+  } while (0)
     if (bits == 4) {
-      if (group == 128) AWQ_FQ(4, 16);
-      else if (group == 256) AWQ_FQ(4, 32);
-      else AWQ_FQ(4, 64);
+      if (group == 128) AWQ_FQ2(4, 16);
+      else if (group == 256) AWQ_FQ2(4, 32);
+      else AWQ_FQ2(4, 64);
     } else {
-      if (group == 128) AWQ_FQ(3, 16);
-      else if (group == 256) AWQ_FQ(3, 32);
-      else AWQ_FQ(3, 64);
+      if (group == 128) AWQ_FQ2(3, 16);
+      else if (group == 256) AWQ_FQ2(3, 32);
+      else AWQ_FQ2(3, 64);
     }
+#undef AWQ_FQ2
 #undef AWQ_FQ
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_sqnorm_abt(xc, D, T, N, K, partial + (size_t)a * tiles, st);
+    if (scaled) {
+      e = launch_fold(Xc, s, T, K, reinterpret_cast<__half*>(Xs), st);
+      if (e != hipSuccess) return e;
+      e = launch_sqnorm_abt(Xs, E, T, N, K, false, partial + (size_t)a * tiles, st);
+    } else {
+      e = launch_sqnorm_abt(reinterpret_cast<const uint16_t*>(Xc), E, T, N, K, true,
+                            partial + (size_t)a * tiles, st);
+    }
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(reduce_loss_kernel, dim3(n_alpha), dim3(256), 0, st, partial, (int)tiles,
-                     loss_dev);
+                     scaled ? 1.0 / 65536.0 : 1.0, loss_dev);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(argmin_copy_kernel, dim3((K + 255) / 256), dim3(256), 0, st, loss_dev,
