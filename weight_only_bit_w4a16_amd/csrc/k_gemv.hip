@@ -123,25 +123,25 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
 
   const size_t xp_bytes = MODE == kOffset ? (size_t)nch * 256 * MP : 0;
   const size_t cs_bytes = MODE == kOffset ? (size_t)nch * MP * 8 : 0;
+  const size_t part_bytes = (size_t)rbw * 4 * 64 * R * 4;
   u32x4* xp = reinterpret_cast<u32x4*>(smem);
   float2* cs = reinterpret_cast<float2*>(smem + xp_bytes);
   float* part = reinterpret_cast<float*>(smem + xp_bytes + cs_bytes);  // [rbw][4][64][R]
+  // scales and zero points of the workgroup's rows, staged once: [rbw*16][ngr]
+  float* sc = reinterpret_cast<float*>(smem + xp_bytes + cs_bytes + part_bytes);
+  uint8_t* zz = reinterpret_cast<uint8_t*>(sc + (size_t)rbw * 16 * ngr);
 
   const uint32_t* qlane = Q + 4 * jj;
   const int F = nj * nc;
 
   // ---- weight prefetch ring -------------------------------------------------
   u32x4 wb[PF];
-  float db[PF];
-  uint32_t zb[PF];
   int pj = 0, pc = c0;  // position of the next prefetch
   auto issue = [&](int slot) {
     const int j = min(pj, nj - 1);
     const int c = pj < nj ? pc : c1 - 1;
     const int n = min((rb0 + j) * 16 + nl, N - 1);
     wb[slot] = ld_nt(reinterpret_cast<const u32x4*>(qlane + (size_t)n * wpr + c * 16));
-    db[slot] = S[(size_t)n * ngr + (c >> gshift)];
-    zb[slot] = Z[(size_t)n * ngr + (c >> gshift)];
     if (++pc == c1) {
       pc = c0;
       ++pj;
@@ -150,6 +150,31 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
   if (F > 0) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) issue(i);
+  }
+
+  // scales and zero points: whole rows, coalesced (a per-chunk load of 16
+  // rows' values would touch 16 cache lines per instruction)
+  // rows, 8 values per thread in flight at a time
+  const int nsz = nj * 16 * ngr;
+  for (int base = 0; base < nsz; base += 256 * 8) {
+    float sv[8];
+    uint8_t zv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = min(base + (int)threadIdx.x + 256 * u, nsz - 1);
+      const int r = idx / ngr, g = idx - r * ngr;
+      const size_t n = (size_t)min((rb0 + (r >> 4)) * 16 + (r & 15), N - 1);
+      sv[u] = S[n * ngr + g];
+      zv[u] = Z[n * ngr + g];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + (int)threadIdx.x + 256 * u;
+      if (idx < nsz) {
+        sc[idx] = sv[u];
+        zz[idx] = zv[u];
+      }
+    }
   }
 
   if constexpr (MODE == kOffset) {
@@ -182,8 +207,8 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
       so += __shfl_xor(so, 2);
       if (tj == 0) cs[tc * MP + tm] = make_float2(1024.f * se + 64.f * so, se + so);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   const uint32_t magic = kMagic2;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -196,10 +221,11 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
     for (int i = 0; i < PF; ++i) {
       const bool valid = f0 + i < F;
       const u32x4 w = wb[i];
-      const float d = valid ? db[i] : 0.f;
-      const uint32_t z = zb[i];
       issue(i);
       const int c = valid ? cc : c1 - 1;
+      const int sidx = (min(cj, nj - 1) * 16 + nl) * ngr + (c >> gshift);
+      const float d = valid ? sc[sidx] : 0.f;
+      const uint32_t z = zz[sidx];
       u32x4 a0, a1, a2, a3;
       if constexpr (MODE == kOffset) {
         const u32x4* p = xp + ((size_t)(c * 4 + jj) * 4) * MP + xr;
@@ -755,7 +781,19 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
 }
 
 constexpr int kGemvPF = 8;
+constexpr size_t kLdsMax = 160 * 1024;  // LDS of one gfx950 compute unit
 constexpr int kGemvMaxRbw = 8;
+
+// raise a decode kernel's dynamic LDS limit once to the largest size used
+template <int MODE, int MP>
+hipError_t allow_lds(size_t lds) {
+  static size_t allowed = 0;
+  if (lds <= allowed) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute((const void*)gemv_w4_kernel<MODE, MP, kGemvPF>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) allowed = lds;
+  return e;
+}
 
 hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scales,
                           const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
@@ -797,22 +835,35 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
 #undef AWQ_M1
     if (sp <= 6) return hipGetLastError();
   }
-  if (variant == 0 && M <= 4) {
-    const int mp = M == 1 ? 1 : (M == 2 ? 2 : 4);
+  // LDS: activations in MFMA order and their C, S (offset form), the row
+  // blocks' partial sums, and the staged scales and zero points
+  const size_t sz = (size_t)rbw * 16 * (nch >> gshift) * 5;
+  if (variant == 0 && M <= 16) {
+    const int mp = M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16)));
     const int r = mp < 4 ? mp : 4;
-    const size_t lds = (size_t)nch * 256 * mp + (size_t)nch * mp * 8 + (size_t)rbw * 4 * 64 * r * 4;
-    if (lds <= 64 * 1024) {
-#define AWQ_GV(MPV)                                                                            \
-  hipLaunchKernelGGL((gemv_w4_kernel<kOffset, MPV, kGemvPF>), grid, block, lds, st, x, q, scales, \
-                     zeros, y, M, N, K, gshift, rbw)
+    const size_t lds =
+        (size_t)nch * 256 * mp + (size_t)nch * mp * 8 + (size_t)rbw * 4 * 64 * r * 4 + sz;
+    if (lds <= kLdsMax) {
+#define AWQ_GV(MPV)                                                                              \
+  do {                                                                                            \
+    const hipError_t ea = allow_lds<kOffset, MPV>(lds);                                          \
+    if (ea != hipSuccess) return ea;                                                              \
+    hipLaunchKernelGGL((gemv_w4_kernel<kOffset, MPV, kGemvPF>), grid, block, lds, st, x, q,       \
+                       scales, zeros, y, M, N, K, gshift, rbw);                                   \
+  } while (0)
       if (mp == 1) AWQ_GV(1);
       else if (mp == 2) AWQ_GV(2);
-      else AWQ_GV(4);
+      else if (mp == 4) AWQ_GV(4);
+      else if (mp == 8) AWQ_GV(8);
+      else AWQ_GV(16);
 #undef AWQ_GV
       return hipGetLastError();
     }
   }
-  const size_t lds = (size_t)rbw * 4 * 64 * 4 * 4;
+  const size_t lds = (size_t)rbw * 4 * 64 * 4 * 4 + sz;
+  if (lds > kLdsMax) return hipErrorNotSupported;
+  const hipError_t ea = allow_lds<kExact, 16>(lds);
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((gemv_w4_kernel<kExact, 16, kGemvPF>), grid, block, lds, st, x, q, scales,
                      zeros, y, M, N, K, gshift, rbw);
   return hipGetLastError();
