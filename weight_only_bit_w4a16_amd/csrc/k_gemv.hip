@@ -780,6 +780,165 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Decode, int4, 2 <= M <= 16 (gemv_w4_mx_kernel). A workgroup of WV <= 8
+// wavefronts splits K into WV slices of CPW 128-code chunks; wavefront s
+// keeps the activation operands of its slice (all token rows, MFMA A
+// layout, prepared once) in registers and streams row block after row block
+// (16 weight rows) against them, so the MFMA work does not grow with M and
+// the activations are read once per workgroup. Lane (n, q) = (l % 16, l / 16)
+// loads codes 32q .. 32q + 31 of a chunk of row n (16 bytes); the four
+// 16x16x32 MFMAs of a chunk take word t of every lane, so one chunk gives
+// the 16 rows x 16 token rows of one quantization group. Offset form as in
+// gemv_w4_kernel: even slots (1024 + c) and odd slots (1024 + 16 c) are
+// contracted separately, and C = 1024 sum(x even) + 64 sum(x odd) and
+// z * S, S = sum(x), are removed per chunk and token. Weights stream
+// through a 4-chunk register ring that runs across row blocks; the scales
+// and zero points of the next row block are staged in LDS meanwhile, and
+// the slices' partial sums of a row block are added in LDS in a fixed order.
+template <int CPW>
+__global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
+    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
+    int rbw) {
+  static_assert(CPW % 4 == 0, "the ring of 4 chunks must tile a slice");
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WV = blockDim.x >> 6;
+  const int nl = lane & 15, q = lane >> 4;
+  const int nch = K >> 7;
+  const int ngr = nch >> gshift;
+  const int wpr = K >> 3;
+  const int nrb = (N + 15) >> 4;
+  const int rb0 = blockIdx.x * rbw;
+  const int nj = min(rbw, nrb - rb0);
+  const int cbeg = wave * CPW;
+
+  float2* csx = reinterpret_cast<float2*>(smem);                  // [nch][16] (C, S)
+  float* szf = reinterpret_cast<float*>(csx + (size_t)nch * 16);  // [2][16][ngr] scales
+  float* part = szf + 2 * 16 * ngr;                               // [2][WV][4][64] partials
+  uint8_t* szb = reinterpret_cast<uint8_t*>(part + 2 * WV * 256);  // [2][16][ngr] zeros
+
+  // ---- weight ring: 4 chunks ahead, across row blocks -----------------------
+  const uint32_t* qlane = Q + 4 * q;
+  auto wload = [&](int j, int i) {  // chunk i of the slice, row block j
+    const size_t n = (size_t)min((rb0 + min(j, nj - 1)) * 16 + nl, N - 1);
+    const int c = min(cbeg + i, nch - 1);
+    return ld_nt(reinterpret_cast<const u32x4*>(qlane + n * wpr + c * 16));
+  };
+  u32x4 ring[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ring[i] = wload(0, i);
+
+  // ---- scales and zero points of row block j: loaded into registers, then
+  // stored to LDS buffer j & 1 ------------------------------------------------
+  const int szn = 16 * ngr;  // values per row block
+  constexpr int SZI = 3;     // per thread: 16 * 96 / 512 (K up to 12288)
+  float szv[SZI];
+  uint8_t zzv[SZI];
+  auto sz_load = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < SZI; ++u) {
+      const int idx = min((int)threadIdx.x + (int)blockDim.x * u, szn - 1);
+      const int r = idx / ngr, g = idx - r * ngr;
+      const size_t n = (size_t)min((rb0 + min(j, nj - 1)) * 16 + r, N - 1);
+      szv[u] = S[n * ngr + g];
+      zzv[u] = Z[n * ngr + g];
+    }
+  };
+  auto sz_store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < SZI; ++u) {
+      const int idx = (int)threadIdx.x + (int)blockDim.x * u;
+      if (idx < szn) {
+        szf[buf * szn + idx] = szv[u];
+        szb[buf * szn + idx] = zzv[u];
+      }
+    }
+  };
+  sz_load(0);
+
+  // ---- activation operands of this slice (token row nl) and C, S ----------
+  u32x4 av[CPW][4];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = cbeg + i;
+    const bool ok = c < nch && nl < M;
+    uint32_t d[16];
+    load_x32(X + (size_t)min(nl, M - 1) * K + min(c, nch - 1) * 128 + 32 * q, d);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) d[t] = ok ? d[t] : 0u;
+    permute_x32(d, av[i][0], av[i][1], av[i][2], av[i][3]);
+    float se = 0.f, so = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      se += h2f((uint16_t)(d[t] & 0xffffu));
+      so += h2f((uint16_t)(d[t] >> 16));
+    }
+    se += __shfl_xor(se, 16);
+    so += __shfl_xor(so, 16);
+    se += __shfl_xor(se, 32);
+    so += __shfl_xor(so, 32);
+    if (q == 0 && c < nch) csx[c * 16 + nl] = make_float2(1024.f * se + 64.f * so, se + so);
+  }
+  sz_store(0);
+  __syncthreads();
+
+  const uint32_t magic = kMagic2;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nj; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nj) sz_load(j + 1);  // uniform
+    floatx4 y = zero4;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const u32x4 w = ring[i & 3];
+      // refill: chunk i + 4 of this row block or the next one's
+      ring[i & 3] = i + 4 < CPW ? wload(j, i + 4) : wload(j + 1, i + 4 - CPW);
+      const int c = cbeg + i;
+      if (c < nch) {  // uniform
+        uint32_t e[8], o[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t x = w[t];
+          const uint32_t x8 = x >> 8;
+          e[2 * t] = and_or(x, 0x000F000Fu, magic);
+          o[2 * t] = and_or(x, 0x00F000F0u, magic);
+          e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
+          o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
+        }
+        const floatx4 de = mfma16(av[i][1], u32x4{e[4], e[5], e[6], e[7]},
+                                  mfma16(av[i][0], u32x4{e[0], e[1], e[2], e[3]}, zero4));
+        const floatx4 dd = mfma16(av[i][3], u32x4{o[4], o[5], o[6], o[7]},
+                                  mfma16(av[i][2], u32x4{o[0], o[1], o[2], o[3]}, zero4));
+        const int gi = nl * ngr + (c >> gshift);
+        const float dl = szf[buf * szn + gi];
+        const float zf = (float)szb[buf * szn + gi];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float2 cv = csx[c * 16 + 4 * q + r];  // token 4q + r
+          const float t = __builtin_fmaf(dd[r], 0.0625f, de[r]) - __builtin_fmaf(zf, cv.y, cv.x);
+          y[r] = __builtin_fmaf(dl, t, y[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[((buf * WV + wave) * 4 + r) * 64 + lane] = y[r];
+    if (j + 1 < nj) sz_store(buf ^ 1);
+    __syncthreads();
+    // slices' partials of row block j, added in slice order
+    for (int t = threadIdx.x; t < 256; t += blockDim.x) {
+      const int l = t & 63, r = t >> 6;
+      float v = 0.f;
+      for (int w = 0; w < WV; ++w) v += part[((buf * WV + w) * 4 + r) * 64 + l];
+      const int m = 4 * (l >> 4) + r;
+      const int n = (rb0 + j) * 16 + (l & 15);
+      if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(v));
+    }
+  }
+}
+
 constexpr int kGemvPF = 8;
 constexpr size_t kLdsMax = 160 * 1024;  // LDS of one gfx950 compute unit
 constexpr int kGemvMaxRbw = 8;
@@ -795,6 +954,35 @@ hipError_t allow_lds(size_t lds) {
   return e;
 }
 
+// 2 <= M <= 16: slices of CPW in {4, 8} chunks over at most 8 wavefronts
+// (K up to 8192; larger K does not fit the register budget)
+hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* scales,
+                             const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st) {
+  const int gshift = log2i(group / 128);
+  const int nch = K / 128;
+  const int cpw = 4 * (((nch + 7) / 8 + 3) / 4);
+  if (cpw > 8) return hipErrorNotSupported;
+  const int wv = (nch + cpw - 1) / cpw;
+  const int ngr = nch >> gshift;
+  const int nrb = (N + 15) / 16;
+  // one workgroup of 8 wavefronts fills a compute unit at this register use
+  const int resident = cu_count() * (wv <= 4 ? 8 / wv : 1);
+  const int rbw = (nrb + resident - 1) / resident;
+  const dim3 grid((unsigned)((nrb + rbw - 1) / rbw)), block((unsigned)(64 * wv));
+  const size_t lds = (size_t)nch * 16 * 8 + (size_t)2 * 16 * ngr * 4 + (size_t)2 * wv * 256 * 4 +
+                     (size_t)2 * 16 * ngr;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  if (cpw == 4)
+    hipLaunchKernelGGL((gemv_w4_mx_kernel<4>), grid, block, lds, st, x, q, scales, zeros, y, M, N,
+                       K, gshift, rbw);
+  else
+    hipLaunchKernelGGL((gemv_w4_mx_kernel<8>), grid, block, lds, st, x, q, scales, zeros, y, M, N,
+                       K, gshift, rbw);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scales,
                           const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
                           hipStream_t st, int variant) {
@@ -808,6 +996,10 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   const dim3 grid((nrb + rbw - 1) / rbw), block(256);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  if (variant == 0 && M >= 2) {
+    const hipError_t e = launch_gemv_w4_mx(X, q, scales, zeros, M, N, K, group, Y, st);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (variant == 0 && M == 1) {
     const int sp = (nch + 15) / 16;
     // wavefronts: all resident at ~2 per SIMD, and at most 64 rows each
