@@ -16,14 +16,15 @@
 // only and reused for the odd one.
 //
 // Code order in LDS. The packed words are unpacked with the fp16 magic-number
-// trick, which yields codes in pairs that are not adjacent in k; the
-// activation tile is stored with the same permutation of k, so the
-// contraction (a sum over k) is unchanged:
+// trick, which yields codes in pairs that are not adjacent in k. For int4 the
+// activation tile is stored with the same permutation of k (the contraction
+// is a sum over k, so any common order is exact):
 //   int4, per 8-code word:  c0 c4 c2 c6 c1 c5 c3 c7
-//   int3, per 10-code word: c0 c6 c1 c7 c3 c8 c4 c9 c2 c5
-// (an int3 group is 13 words = 130 slots, of which the last 2 hold no code;
-// their activation slots are zero; slots 130..143 pad the step to 9 x 16).
-// fp16 B tiles (the search's error terms) keep natural order.
+// For int3 the five pairs of a word are put back in natural order with
+// v_perm_b32, so the activation tile is a plain copy; an int3 group is 13
+// words = 130 slots, of which the last 2 hold no code (their activation slots
+// are zero), and slots 130..143 pad the step to 9 x 16. fp16 B tiles (the
+// search's error terms) keep natural order.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -32,6 +33,7 @@ namespace awq {
 namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // dword-aligned 16 B
 
 __device__ __forceinline__ floatx16 mfma32(u32x4 a, u32x4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
@@ -62,8 +64,7 @@ struct Cfg {
   static constexpr int ACH = BM * BK / 8 / NT;         // 16-byte A chunks per thread
   static constexpr int BCH = BN * BK / 8 / NT;         // 16-byte fp16 B chunks per thread
   static constexpr int BW = BN * 8 / NT;               // int4 B words per thread
-  static constexpr int AIT = (BM * 13 + NT - 1) / NT;  // int3 A items per thread
-  static constexpr int BIT = (BN * 13 + NT - 1) / NT;  // int3 B items per thread
+  static constexpr int BIT = BN * 4 / NT;              // int3 B (row, quarter) items per thread
 };
 
 // register staging of one K step
@@ -82,8 +83,8 @@ struct Stage<4, BM, BN, NT> {
 };
 template <int BM, int BN, int NT>
 struct Stage<3, BM, BN, NT> {
-  uint32_t a[Cfg<3, BM, BN, NT>::AIT][5];
-  uint32_t b[Cfg<3, BM, BN, NT>::BIT];
+  u32x4 a[Cfg<3, BM, BN, NT>::ACH];
+  u32x4 b[Cfg<3, BM, BN, NT>::BIT];  // 4 words of a group from word {0,4,7,9}[quarter]
   float d[Cfg<3, BM, BN, NT>::BIT];
   uint32_t zw[Cfg<3, BM, BN, NT>::BIT], zsh[Cfg<3, BM, BN, NT>::BIT];
 };
@@ -138,15 +139,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   const int ng = K >> (7 + gshift);  // quantization groups per row
 
   if (BMODE == 3) {
-    // zero the slots 130..143 of every row of both buffers once; they are
-    // never written again
-    for (int i = tid; i < 2 * (BM + BN) * 14; i += NT) {
-      const int buf = i / ((BM + BN) * 14);
-      const int rr = (i / 14) % (BM + BN), c = i % 14;
+    // zero the slots 128..143 of every row of both buffers once: activation
+    // slots 128..143 and weight slots 130..143 are never written again
+    // (weight slots 128, 129 take the finite phantom codes of word 12)
+    for (int i = tid; i < 2 * (BM + BN) * 16; i += NT) {
+      const int buf = i / ((BM + BN) * 16);
+      const int rr = (i / 16) % (BM + BN), c = i % 16;
       if (rr < BM)
-        lds_a[buf][rr * STR + 130 + c] = 0;
+        lds_a[buf][rr * STR + 128 + c] = 0;
       else
-        lds_b[buf][(rr - BM) * STR + 130 + c] = 0;
+        lds_b[buf][(rr - BM) * STR + 128 + c] = 0;
     }
   }
 
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // load step ks into st; for int4, SZ says whether this (even) step also
   // loads its group's scale and zero point
   auto load_step = [&](St& st, int ks, auto SZ) {
-    if constexpr (BMODE == 0 || BMODE == 4) {
+    {
       const int ka = BMODE == 0 && hilo ? 128 * (ks >> 2) + 64 * (ks & 1) : BK * ks;
 #pragma unroll
       for (int i = 0; i < C::ACH; ++i) {
@@ -208,27 +210,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 #pragma unroll
         for (int q = 0; q < C::BW; ++q) st.b[q] = ld_nt(p + q);
       }
-    } else {  // int3: items (row, word) over BM or BN rows x 13 words
+    } else {  // int3: item = (row, quarter); quarters cover words 0-3, 4-6, 7-9, 10-12
       const uint32_t* Q = static_cast<const uint32_t*>(Bsrc);
-      const int k0 = BK * ks;
-#pragma unroll
-      for (int i = 0; i < C::AIT; ++i) {
-        const int id = min(tid + NT * i, BM * 13 - 1);
-        const int r = id / 13, j = id % 13;
-        const int m = min(m0 + r, M - 1);
-        const uint32_t* px = reinterpret_cast<const uint32_t*>(A + (size_t)m * K + k0 + 10 * j);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st.a[i][q] = px[q];
-        // codes 128, 129 do not exist: word 12 re-reads codes 120, 121 and
-        // the store zeroes them
-        st.a[i][4] = px[j < 12 ? 4 : 0];
-      }
 #pragma unroll
       for (int i = 0; i < C::BIT; ++i) {
-        const int id = min(tid + NT * i, BN * 13 - 1);
-        const int r = id / 13, j = id % 13;
+        const int id = tid + NT * i;
+        const int r = id >> 2, qt = id & 3;
         const int n = min(n0 + r, N - 1);
-        st.b[i] = ld_nt(Q + (size_t)n * wpr + ks * 13 + j);
+        // dword-aligned 16-byte load that stays inside the group: quarter 3
+        // reads words 9..12 and uses the last three
+        const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
+        const u32x4a4 v =
+            ld_nt(reinterpret_cast<const u32x4a4*>(Q + (size_t)n * wpr + ks * 13 + w0));
+        st.b[i] = u32x4{v[0], v[1], v[2], v[3]};
         st.d[i] = S[(size_t)n * ng + ks];
         load_zero((size_t)n * ng + ks, st.zw[i], st.zsh[i]);
       }
@@ -237,7 +231,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 
   // dequantize / permute one register stage into LDS buffer buf, item by
   // item, so the work can be spread between the MFMAs of the current step
-  constexpr int NA = BMODE == 3 ? C::AIT : C::ACH;                         // A items
+  constexpr int NA = C::ACH;                                               // A items
   constexpr int NB = BMODE == 3 ? C::BIT : (BMODE == 4 ? C::BW : C::BCH);  // B items
   Dq dq;  // int4: constants of the group of the last even step stored
   auto set_dq = [&](const St& st) {
@@ -260,22 +254,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const u32x4 d = st.a[i];
       const u32x4 p = {plo(d[0], d[2]), plo(d[1], d[3]), phi(d[0], d[2]), phi(d[1], d[3])};
       *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = p;
-    } else {
+    } else {  // int3: natural order, a plain copy
       const int id = tid + NT * i;
-      if (id < BM * 13) {
-        const int r = id / 13, j = id % 13;
-        uint32_t d[5];
-#pragma unroll
-        for (int q = 0; q < 5; ++q) d[q] = st.a[i][q];
-        if (j == 12) d[4] = 0u;
-        // (x0,x6) (x1,x7) (x3,x8) (x4,x9) (x2,x5) from d_i = (x[2i], x[2i+1])
-        uint32_t* pa = reinterpret_cast<uint32_t*>(&la[r * STR + 10 * j]);
-        pa[0] = plo(d[0], d[3]);
-        pa[1] = phi(d[0], d[3]);
-        pa[2] = __builtin_amdgcn_perm(d[4], d[1], 0x05040302u);  // (d1.hi, d4.lo)
-        pa[3] = __builtin_amdgcn_perm(d[4], d[2], 0x07060100u);  // (d2.lo, d4.hi)
-        pa[4] = __builtin_amdgcn_perm(d[2], d[1], 0x07060100u);  // (d1.lo, d2.hi)
-      }
+      const int r = id / (BK / 8), c8 = id % (BK / 8);
+      *reinterpret_cast<u32x4*>(&la[r * STR + 8 * c8]) = st.a[i];
     }
   };
   auto store_b = [&](const St& st, int buf, int i) {
@@ -308,20 +290,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const float offl[5] = {1024.f, 128.f, 512.f, 64.f, 8.f};
       const float offh[5] = {256.f, 32.f, 1024.f, 128.f, 1024.f};
       const int id = tid + NT * i;
-      if (id < BN * 13) {
-        const int r = id / 13, j = id % 13;
-        const uint32_t w = st.b[i];
-        const uint32_t t8 = w >> 8, u1 = w << 1;
-        const float zf = (float)((st.zw[i] >> st.zsh[i]) & 0xffu);
-        const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
-        const uint32_t raw[5] = {(w & 0x001C0007u) | kMagic2, (w & 0x00E00038u) | kMagic2,
-                                 (t8 & 0x0007000Eu) | kMagic2, (t8 & 0x00380070u) | kMagic2,
-                                 (u1 & 0x00070380u) | kMagic2};
-        uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * j]);
+      const int r = id >> 2, qt = id & 3;
+      const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
+      const float zf = (float)((st.zw[i] >> st.zsh[i]) & 0xffu);
+      const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
+      h2 add[5];
 #pragma unroll
-        for (int p = 0; p < 5; ++p) {
-          const h2 add = {(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
-          pb[p] = hbits(__builtin_elementwise_fma(hv(raw[p]), mul[p], add) * dh);
+      for (int p = 0; p < 5; ++p) add[p] = h2{(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // quarter 0 stores words 0-3, quarters 1 and 2 their first three,
+        // quarter 3 (loaded from word 9) words 10-12
+        const bool use = qt == 0 || (qt == 3 ? u > 0 : u < 3);
+        const uint32_t w = st.b[i][u];
+        const uint32_t t8 = w >> 8, u1 = w << 1;
+        const uint32_t raw[5] = {and_or(w, 0x001C0007u, kMagic2), and_or(w, 0x00E00038u, kMagic2),
+                                 and_or(t8, 0x0007000Eu, kMagic2), and_or(t8, 0x00380070u, kMagic2),
+                                 and_or(u1, 0x00070380u, kMagic2)};
+        uint32_t pr[5];  // (c0,c6) (c1,c7) (c3,c8) (c4,c9) (c2,c5) as c - z times delta
+#pragma unroll
+        for (int p = 0; p < 5; ++p)
+          pr[p] = hbits(__builtin_elementwise_fma(hv(raw[p]), mul[p], add[p]) * dh);
+        if (use) {
+          uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * (w0 + u)]);
+          pb[0] = plo(pr[0], pr[1]);                             // (c0, c1)
+          pb[1] = plo(pr[4], pr[2]);                             // (c2, c3)
+          pb[2] = __builtin_amdgcn_perm(pr[4], pr[3], 0x07060100u);  // (c4, c5)
+          pb[3] = phi(pr[0], pr[1]);                             // (c6, c7)
+          pb[4] = phi(pr[2], pr[3]);                             // (c8, c9)
         }
       }
     }
