@@ -102,12 +102,13 @@ struct Dq {
 // Word loads keep the loop-carried value 32 bits wide, so no byte
 // extension is scheduled ahead of the MFMAs (it would wait on the newest
 // loads).
-template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW>
+template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW, int NST>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const float* __restrict__ S,
     const uint8_t* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
     uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo) {
   constexpr int NT = 64 * WGM * WGN;
+  static_assert(NST == 2 || NST == 4, "register stages");
   using C = Cfg<BMODE, BM, BN, NT>;
   using St = Stage<BMODE, BM, BN, NT>;
   constexpr int STR = C::STR;
@@ -379,31 +380,57 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     }
     load_step(lst, lks, SZ);
     __syncthreads();
+    // keep the next step's dequantization below the barrier: hoisted above
+    // it, it would wait for loads issued just before
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Two register stages in flight: while step ks is computed from LDS,
-  // stage sa holds step ks + 1 (stored during the MFMAs) and sb step ks + 2.
-  // sa always carries even steps, sb odd ones. Loads past the last step
-  // re-read the last step (branch-free; the extra stores land in the buffer
-  // no later step reads).
-  using Even = std::integral_constant<bool, BMODE == 4>;
-  using Odd = std::integral_constant<bool, false>;
-  St sa, sb;
+  // NST register stages in flight: stage i carries the steps i (mod NST).
+  // While step t is computed from LDS, the stages hold steps t+1 .. t+NST;
+  // during the MFMAs step t+1 is stored to the other LDS buffer and its
+  // stage reloaded with step t+1+NST. With NST even, a stage's steps are all
+  // even or all odd (int4: even stages carry the group's scale and zero
+  // point). Loads past the last step re-read the last step (branch-free; the
+  // extra stores land in the buffer no later step reads).
+  St stg[NST];
   const int last = nsteps - 1;
-  load_step(sa, 0, Even{});
-  load_step(sb, min(1, last), Odd{});
-  set_dq(sa);
-  store_all(sa, 0);
-  load_step(sa, min(2, last), Even{});
-  __syncthreads();
-  int ks = 0;
-  for (; ks + 1 < nsteps; ks += 2) {
-    step(0, sb, sb, min(ks + 3, last), Odd{});
-    step(1, sa, sa, min(ks + 4, last), Even{});
+  auto prime = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+    load_step(stg[i], min(i, last), std::integral_constant<bool, BMODE == 4 && i % 2 == 0>{});
+  };
+  prime(std::integral_constant<int, 0>{});
+  prime(std::integral_constant<int, 1>{});
+  if constexpr (NST == 4) {
+    prime(std::integral_constant<int, 2>{});
+    prime(std::integral_constant<int, 3>{});
   }
-  if (ks < nsteps) {
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) mma(lds_a[0], lds_b[0], kk);
+  set_dq(stg[0]);
+  store_all(stg[0], 0);
+  load_step(stg[0], min(NST, last), std::integral_constant<bool, BMODE == 4>{});
+  __syncthreads();
+  // sub-step u of a group of NST steps starting at ks (a multiple of NST)
+  auto sub = [&](int ks, auto U) {
+    constexpr int u = decltype(U)::value;
+    constexpr int si = (u + 1) % NST;
+    step(u & 1, stg[si], stg[si], min(ks + u + 1 + NST, last),
+         std::integral_constant<bool, BMODE == 4 && si % 2 == 0>{});
+  };
+  // full groups: no branch inside the loop body, so the compiler keeps the
+  // in-flight loads counted exactly across the back edge
+  int ks = 0;
+  for (; ks + NST <= nsteps; ks += NST) {
+    sub(ks, std::integral_constant<int, 0>{});
+    sub(ks, std::integral_constant<int, 1>{});
+    if constexpr (NST == 4) {
+      sub(ks, std::integral_constant<int, 2>{});
+      sub(ks, std::integral_constant<int, 3>{});
+    }
+  }
+  // the last nsteps % NST steps (uniform branches)
+  if (ks < nsteps) sub(ks, std::integral_constant<int, 0>{});
+  if constexpr (NST == 4) {
+    if (ks + 1 < nsteps) sub(ks, std::integral_constant<int, 1>{});
+    if (ks + 2 < nsteps) sub(ks, std::integral_constant<int, 2>{});
   }
 
   // D layout of the 32x32 MFMA: lane l holds column l % 32, rows
@@ -474,27 +501,27 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   const unsigned cus = (unsigned)cu_n();
   const bool zw = ((size_t)N * (size_t)(K / group)) % 4 == 0;
-#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN)                                                      \
+#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST)                                                 \
   do {                                                                                          \
     if (zw)                                                                                     \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true>),                       \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST>),                  \
                          dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
                          zeros, M, N, K, wpr, gshift, y, nullptr, 0);                           \
     else                                                                                        \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false>),                      \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST>),                 \
                          dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
                          zeros, M, N, K, wpr, gshift, y, nullptr, 0);                           \
   } while (0)
   if (bits == 4) {
     // the largest tile that still gives every compute unit work
     if (tiles_of(M, N, 256, 256) >= cus)
-      AWQ_GEMM(4, 256, 256, 2, 4);
+      AWQ_GEMM(4, 256, 256, 2, 4, 2);
     else if (tiles_of(M, N, 128, 128) >= cus)
-      AWQ_GEMM(4, 128, 128, 2, 2);
+      AWQ_GEMM(4, 128, 128, 2, 2, 4);
     else
-      AWQ_GEMM(4, 64, 64, 2, 2);
+      AWQ_GEMM(4, 64, 64, 2, 2, 4);
   } else {
-    AWQ_GEMM(3, 64, 64, 2, 2);
+    AWQ_GEMM(3, 64, 64, 2, 2, 4);
   }
 #undef AWQ_GEMM
   return hipGetLastError();
@@ -505,7 +532,7 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
 // 128-wide k chunk (then the product is A (Bhi + Blo)^T)
 hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K, bool hilo,
                              double* partial, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false>), dim3(tiles_of(M, N, 128, 128)),
+  hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false, 2>), dim3(tiles_of(M, N, 128, 128)),
                      dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial,
                      hilo ? 1 : 0);
   return hipGetLastError();
