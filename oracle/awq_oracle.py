@@ -48,6 +48,11 @@ R7  the layer-output error is the squared Frobenius norm over calibration
     the original fp16 W; the first minimum over the grid wins.
 R9  packing: see ``pack``.
 R10 scales are stored as the float32 delta, zero points as uint8.
+R17 zero_point=false (the AwqConfig option, AWQ Explained -- "How the scale
+    is chosen", last paragraph) is the symmetric grid: delta = max|W'| /
+    (2^(b-1) - 1) per group, codes rint(W' / delta) in [-(2^(b-1) - 1),
+    2^(b-1) - 1] stored with the offset z = 2^(b-1) (so the packed layout and
+    the product are unchanged); an all-zero group gets delta = 1.
 """
 from __future__ import annotations
 
@@ -123,9 +128,32 @@ def quantize_groups(wp: np.ndarray, bits: int, group: int):
     return q.reshape(N, K), delta, z
 
 
-def quantize(W: np.ndarray, s, bits: int, group: int):
+def quantize_groups_symmetric(wp: np.ndarray, bits: int, group: int):
+    """Symmetric RTN (R17) of float32 W' [N, K] in groups of `group` along K.
+
+    Returns (q int64 [N, K] with the offset 2^(b-1) added, delta float32
+    [N, K/group], z int64 [N, K/group] = 2^(b-1)).
+    """
+    wp = np.asarray(wp, dtype=np.float32)
+    N, K = wp.shape
+    assert K % group == 0
+    half = 1 << (bits - 1)
+    g = wp.reshape(N, K // group, group)
+    amax = np.abs(g).max(axis=2).astype(np.float32)
+    flat = amax == 0
+    safe = np.where(flat, np.float32(1.0), amax).astype(np.float32)
+    delta = (safe / np.float32(half - 1)).astype(np.float32)
+    delta = np.where(flat, np.float32(1.0), delta).astype(np.float32)
+    z = np.full(delta.shape, half, dtype=np.int64)
+    q = np.rint((g / delta[..., None]).astype(np.float32)).astype(np.int64) + half
+    q = np.clip(q, 0, (1 << bits) - 1)
+    return q.reshape(N, K), delta, z
+
+
+def quantize(W: np.ndarray, s, bits: int, group: int, zero_point: bool = True):
     """(q, scales fp32 [N, K/G], zeros uint8 [N, K/G]) of W diag(s)."""
-    q, delta, z = quantize_groups(scaled_weight(W, s), bits, group)
+    qg = quantize_groups if zero_point else quantize_groups_symmetric
+    q, delta, z = qg(scaled_weight(W, s), bits, group)
     return q, delta.astype(np.float32), z.astype(np.uint8)
 
 
@@ -195,9 +223,9 @@ def unpack(qpacked: np.ndarray, bits: int, group: int, K: int) -> np.ndarray:
     return q.reshape(N, K)
 
 
-def quantize_pack(W: np.ndarray, s, bits: int, group: int):
+def quantize_pack(W: np.ndarray, s, bits: int, group: int, zero_point: bool = True):
     """The quantize-and-pack step: (qpacked uint32, scales fp32, zeros uint8)."""
-    q, scales, zeros = quantize(W, s, bits, group)
+    q, scales, zeros = quantize(W, s, bits, group, zero_point)
     return pack(q, bits, group), scales, zeros
 
 
@@ -232,23 +260,26 @@ def matmul_rows(Xp, qpacked, scales, zeros, bits, group, K, rows) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def quant_error(W: np.ndarray, s: np.ndarray, bits: int, group: int) -> np.ndarray:
+def quant_error(W: np.ndarray, s: np.ndarray, bits: int, group: int,
+                zero_point: bool = True) -> np.ndarray:
     """D = W - Q(W diag(s)) diag(s)^-1 in float64 [N, K]."""
-    q, scales, zeros = quantize(W, s, bits, group)
+    q, scales, zeros = quantize(W, s, bits, group, zero_point)
     what = dequantize(q, scales, zeros, group)
     return np.asarray(W, dtype=np.float16).astype(np.float64) - what / np.asarray(s, np.float64)[None, :]
 
 
-def layer_loss(xcal: np.ndarray, W: np.ndarray, s: np.ndarray, bits: int, group: int) -> float:
+def layer_loss(xcal: np.ndarray, W: np.ndarray, s: np.ndarray, bits: int, group: int,
+               zero_point: bool = True) -> float:
     """L = || Xcal D^T ||_F^2 (R7): the layer-output error on the calibration
     batch, sum over tokens t and output channels n of
     (sum_k x_tk (W_nk - Wq_nk / s_k))^2."""
-    D = quant_error(W, s, bits, group)
+    D = quant_error(W, s, bits, group, zero_point)
     E = np.asarray(xcal, dtype=np.float16).astype(np.float64) @ D.T
     return float(np.sum(E * E))
 
 
-def scale_search(W: np.ndarray, xcal: np.ndarray, alpha_grid, bits: int, group: int):
+def scale_search(W: np.ndarray, xcal: np.ndarray, alpha_grid, bits: int, group: int,
+                 zero_point: bool = True):
     """Grid search over alpha; returns (s float32 [K], best index, losses float64).
 
     The grid is scanned in the given order with a strict '<', so the first
@@ -258,7 +289,7 @@ def scale_search(W: np.ndarray, xcal: np.ndarray, alpha_grid, bits: int, group: 
     losses = np.empty(len(alpha_grid), dtype=np.float64)
     best = 0
     for i, a in enumerate(alpha_grid):
-        losses[i] = layer_loss(xcal, W, scale_from_stats(m, a), bits, group)
+        losses[i] = layer_loss(xcal, W, scale_from_stats(m, a), bits, group, zero_point)
         if losses[i] < losses[best]:
             best = i
     return scale_from_stats(m, alpha_grid[best]), best, losses

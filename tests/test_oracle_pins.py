@@ -429,3 +429,82 @@ def test_ties_round_half_even_and_zero_after_rint():
     assert sc[0, 0] == np.float32(1 / 16) and z[0, 0] == 7
     assert list(q[0, 112:127]) == spec["expected_tie_codes"]
     assert q[0, 127] == spec["expected_near_tie_code"]
+
+
+# ---------------------------------------------------------------------------
+# zero_point=false: the symmetric grid (R17)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _golden("exact_groups_symmetric.json")["cases"])
+def test_symmetric_exact_group(case):
+    bits, G = case["bits"], case["group"]
+    i = np.arange(G) % case["count"]
+    v = ((i - case["h"]) / case["den"]).astype(np.float16)
+    W = np.stack([v, v[::-1]])
+    q, scales, zeros = O.quantize(W, None, bits, G, zero_point=False)
+    assert np.all(scales == np.float32(case["delta"]))
+    assert np.all(zeros == case["zero"])
+    assert np.array_equal(q[0], i + 1) and np.array_equal(q[1], (i + 1)[::-1])
+    assert np.array_equal(O.dequantize(q, scales, zeros, G), W.astype(np.float64))
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(vals=_group_strategy(), bits=st.sampled_from([3, 4]), scale_exp=st.integers(-3, 3))
+def test_symmetric_half_step_bound_odd_symmetry(vals, bits, scale_exp):
+    W = np.array(vals, dtype=np.float16)[None, :]
+    s = np.full(128, np.float32(1.5 * 2.0 ** scale_exp), dtype=np.float32)
+    wp = O.scaled_weight(W, s)
+    q, scales, zeros = O.quantize(W, s, bits, 128, zero_point=False)
+    half = 1 << (bits - 1)
+    assert np.all(zeros == half)
+    assert q.min() >= 1 and q.max() <= 2 * half - 1   # never the unused code -2^(b-1)
+    d = float(scales[0, 0])
+    err = np.abs(O.dequantize(q, scales, zeros, 128)[0] - wp[0].astype(np.float64))
+    assert err.max() <= d * (0.5 + 1e-5), (err.max() / d)
+    # rint is odd-symmetric and max|W'| is the same, so -W gets the negated codes
+    qn, sn, zn = O.quantize(-W, s, bits, 128, zero_point=False)
+    assert np.array_equal(sn, scales) and np.array_equal(qn - half, -(q - half))
+    if np.all(W == 0):
+        assert d == 1.0 and np.all(q == half)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_symmetric_power_of_two_equivariance(bits):
+    W = datagen.random_f16((8, 256), 0.02, seed=3)
+    s = datagen.random_f32_positive(256, 0.3, 7.0, seed=4)
+    q1, sc1, z1 = O.quantize(W, s, bits, 128, zero_point=False)
+    q2, sc2, z2 = O.quantize(W, (s * np.float32(8.0)).astype(np.float32), bits, 128, zero_point=False)
+    assert np.array_equal(q1, q2) and np.array_equal(z1, z2)
+    assert np.array_equal(sc2, (sc1 * np.float32(8.0)).astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_symmetric_matmul_exact_rationals(bits):
+    K, N, M = 256, 3, 2
+    W = datagen.random_f16((N, K), 0.02, seed=30 + bits)
+    s = datagen.random_f32_positive(K, 0.5, 4.0, seed=31)
+    X = datagen.random_f16((M, K), 1.0, seed=32)
+    qp, sc, z = O.quantize_pack(W, s, bits, 128, zero_point=False)
+    Y = O.matmul(X, qp, sc, z, bits, 128, K)
+    for n in range(N):
+        codes = _unpack_by_hand(qp[n], bits, 128, K)
+        w = [(codes[k] - int(z[n, k // 128])) * Fraction(float(sc[n, k // 128])) for k in range(K)]
+        for m in range(M):
+            exact = sum(Fraction(float(X[m, k])) * w[k] for k in range(K))
+            assert Y[m, n] == pytest.approx(float(exact), rel=1e-12, abs=1e-15)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_symmetric_search(bits):
+    """alpha = 0 is plain symmetric RTN, and the search still protects the
+    outlier channels."""
+    W, Xc, _ = datagen.small_layer(512, 64, 64, 5, 40.0, seed=77)
+    grid = datagen.alpha_grid(20)
+    s, best, losses = O.scale_search(W, Xc, grid, bits, 128, zero_point=False)
+    q0, sc0, z0 = O.quantize(W, None, bits, 128, zero_point=False)
+    ones = O.scale_from_stats(O.act_stats(Xc), 0.0)
+    assert np.all(ones == 1.0)
+    assert losses[0] == O.layer_loss(Xc, W, ones, bits, 128, zero_point=False)
+    qa, sca, za = O.quantize(W, ones, bits, 128, zero_point=False)
+    assert np.array_equal(qa, q0) and np.array_equal(sca, sc0)
+    assert losses[best] < losses[0]
