@@ -118,6 +118,21 @@ awq_status awq_scale_candidates(const double* m, int K, const float* alpha, int 
 awq_status awq_quantize_pack(const uint16_t* W, const float* s, int N, int K, int bits, int group,
                              uint32_t* qpacked, float* scales, uint8_t* zeros, void* stream);
 
+/* awq_quantize_pack with the grid chosen by `zero_point` (the AwqConfig
+ * option of AWQ Explained -- "How the scale is chosen", last paragraph):
+ * 1 = the asymmetric grid above (awq_quantize_pack is this call with 1);
+ * 0 = the symmetric grid, per row n and group g:
+ *   a = max |W'|
+ *   a == 0:  delta = 1
+ *   else:    delta = a / (2^(bits-1) - 1)
+ *   z = 2^(bits-1),  q = rint(W' / delta) + z   (in [1, 2^bits - 1])
+ * so the codes are signed integers stored with a fixed offset and the packed
+ * layout, the zeros array and awq_w4a16_matmul are unchanged. Any other
+ * value of zero_point returns AWQ_ERR_INVALID_ARG. */
+awq_status awq_quantize_pack_ex(const uint16_t* W, const float* s, int N, int K, int bits,
+                                int group, int zero_point, uint32_t* qpacked, float* scales,
+                                uint8_t* zeros, void* stream);
+
 /* Fold diag(s)^-1 into the activation (AWQ Explained -- "Scaling instead of
  * mixed precision": the matching activation channel is divided by s):
  *   Xout[m, k] = fp16(float32(X[m, k]) / s[k])   (round-to-nearest-even)
@@ -172,6 +187,15 @@ awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, in
                             const float* alpha_grid, int n_alpha, int bits, int group, float* s_out,
                             double* loss_out, int* best_index, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* awq_scale_search with Q the grid chosen by `zero_point` (1 = asymmetric,
+ * as awq_scale_search; 0 = symmetric, as awq_quantize_pack_ex). Same
+ * arguments, workspace, accuracy and synchronization otherwise; any other
+ * value of zero_point returns AWQ_ERR_INVALID_ARG. */
+awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
+                               const float* alpha_grid, int n_alpha, int bits, int group,
+                               int zero_point, float* s_out, double* loss_out, int* best_index,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

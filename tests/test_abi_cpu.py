@@ -36,7 +36,7 @@ def test_status_strings_and_version():
     for code, name in _lib.STATUS.items():
         assert h.awq_status_string(code).decode() == name
     assert h.awq_status_string(99).decode() == "AWQ_ERR_UNKNOWN"
-    assert h.awq_version() == 100
+    assert h.awq_version() == 101
 
 
 @pytest.mark.parametrize("K,bits,group", [(128, 4, 128), (4096, 4, 128), (8192, 4, 128),
@@ -96,6 +96,8 @@ def test_valid_calls_without_device_report_no_device():
     assert _mm() == E.AWQ_ERR_NO_DEVICE
     assert _mm(M=2048, K=8192, N=128) == E.AWQ_ERR_NO_DEVICE
     assert h.awq_quantize_pack(P, NULL, 64, 256, 4, 128, P, P, P, NULL) == E.AWQ_ERR_NO_DEVICE
+    assert h.awq_quantize_pack_ex(P, NULL, 64, 256, 4, 128, 0, P, P, P,
+                                  NULL) == E.AWQ_ERR_NO_DEVICE
     assert h.awq_fold_inv_scale(P, P, 4, 256, P2, NULL) == E.AWQ_ERR_NO_DEVICE
     assert h.awq_act_stats(P, 64, 256, P2, NULL) == E.AWQ_ERR_NO_DEVICE
     assert h.awq_scale_candidates(P, 256, P, 20, P2, NULL) == E.AWQ_ERR_NO_DEVICE
@@ -109,6 +111,11 @@ def test_quantize_pack_validation():
     assert h.awq_quantize_pack(P, NULL, 0, 256, 4, 128, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
     assert h.awq_quantize_pack(P, NULL, 64, 256, 2, 128, P, P, P, NULL) == E.AWQ_ERR_UNSUPPORTED
     assert h.awq_quantize_pack(P, NULL, 64, 300, 4, 128, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    ex = h.awq_quantize_pack_ex
+    assert ex(P, NULL, 64, 256, 4, 128, 2, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert ex(P, NULL, 64, 256, 4, 128, -1, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert ex(NULL, NULL, 64, 256, 4, 128, 0, P, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert ex(P, NULL, 64, 256, 2, 128, 0, P, P, P, NULL) == E.AWQ_ERR_UNSUPPORTED
 
 
 def test_other_validation():
@@ -144,3 +151,9 @@ def test_scale_search_validation():
     bad = a.copy()
     bad[3] = 1.5
     assert call(alpha=bad.ctypes.data_as(ctypes.c_void_p)) == E.AWQ_ERR_INVALID_ARG
+
+    def call_ex(zp, ws=P, nbytes=need):
+        return h.awq_scale_search_ex(P, P, 64, 256, 32, ap, 20, 4, 128, zp, P2, lp,
+                                     ctypes.byref(best), ws, nbytes, NULL)
+    assert call_ex(2) == E.AWQ_ERR_INVALID_ARG
+    assert call_ex(0, ws=NULL) == E.AWQ_ERR_WORKSPACE

@@ -281,12 +281,14 @@ def test_prefill_workload(name, M):
 # scale search
 # ---------------------------------------------------------------------------
 
-def check_search(W, Xc, grid, bits, group, oracle_idx=None):
-    s_g, best_g, loss_g = awq.scale_search(dev(W), dev(Xc), grid, bits, group)
+def check_search(W, Xc, grid, bits, group, oracle_idx=None, zero_point=True):
+    s_g, best_g, loss_g = awq.scale_search(dev(W), dev(Xc), grid, bits, group,
+                                           zero_point=zero_point)
     s_g = host(s_g)
     m = O.act_stats(Xc)
     idx = range(len(grid)) if oracle_idx is None else sorted(set(oracle_idx) | {best_g})
-    loss_o = {i: O.layer_loss(Xc, W, O.scale_from_stats(m, grid[i]), bits, group) for i in idx}
+    loss_o = {i: O.layer_loss(Xc, W, O.scale_from_stats(m, grid[i]), bits, group,
+                              zero_point=zero_point) for i in idx}
     for i, lo in loss_o.items():
         assert abs(loss_g[i] - lo) <= 1e-4 * lo, (i, loss_g[i], lo)
     assert best_g == int(np.argmin(loss_g))

@@ -89,8 +89,10 @@ def scale_candidates(m, alpha, stream=None):
     return s
 
 
-def quantize_pack(W, s=None, bits: int = 4, group: int = 128, out=None, stream=None):
-    """Round-to-nearest quantize-and-pack of W diag(s).
+def quantize_pack(W, s=None, bits: int = 4, group: int = 128, out=None, stream=None,
+                  zero_point: bool = True):
+    """Round-to-nearest quantize-and-pack of W diag(s) on the asymmetric grid
+    (zero_point=True) or the symmetric one (zero_point=False).
 
     Returns (qpacked uint32-as-int32 [N, words_per_row], scales float32
     [N, K/group], zeros uint8 [N, K/group]).
@@ -110,8 +112,9 @@ def quantize_pack(W, s=None, bits: int = 4, group: int = 128, out=None, stream=N
         z = torch.empty((N, K // g), dtype=torch.uint8, device=W.device)
     else:
         q, sc, z = out
-    check(lib().awq_quantize_pack(_ptr(W), _ptr(s), N, K, bits, group, _ptr(q), _ptr(sc), _ptr(z),
-                                  _stream(stream)), "awq_quantize_pack")
+    check(lib().awq_quantize_pack_ex(_ptr(W), _ptr(s), N, K, bits, group, int(bool(zero_point)),
+                                     _ptr(q), _ptr(sc), _ptr(z), _stream(stream)),
+          "awq_quantize_pack_ex")
     return q, sc, z
 
 
@@ -159,8 +162,9 @@ def scale_search_workspace_bytes(N, K, T, n_alpha, bits=4, group=128) -> int:
 
 
 def scale_search(W, xcal, alpha_grid=None, bits: int = 4, group: int = 128, workspace=None,
-                 stream=None):
-    """Grid search over alpha for s = mean|x| ** alpha.
+                 stream=None, zero_point: bool = True):
+    """Grid search over alpha for s = mean|x| ** alpha, the weights quantized
+    on the asymmetric (zero_point=True) or symmetric grid.
 
     Returns (s float32 [K] on the device, best index, losses float64 numpy).
     Synchronizes the stream.
@@ -183,8 +187,9 @@ def scale_search(W, xcal, alpha_grid=None, bits: int = 4, group: int = 128, work
     s = torch.empty(K, dtype=torch.float32, device=W.device)
     losses = np.zeros(len(a), dtype=np.float64)
     best = ctypes.c_int(-1)
-    check(lib().awq_scale_search(
+    check(lib().awq_scale_search_ex(
         _ptr(W), _ptr(xcal), N, K, T, a.ctypes.data_as(ctypes.c_void_p), len(a), bits, group,
-        _ptr(s), losses.ctypes.data_as(ctypes.c_void_p), ctypes.byref(best), _ptr(workspace),
-        workspace.numel(), _stream(stream)), "awq_scale_search")
+        int(bool(zero_point)), _ptr(s), losses.ctypes.data_as(ctypes.c_void_p),
+        ctypes.byref(best), _ptr(workspace), workspace.numel(), _stream(stream)),
+        "awq_scale_search_ex")
     return s, int(best.value), losses

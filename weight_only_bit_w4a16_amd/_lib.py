@@ -30,11 +30,14 @@ SIGNATURES = {
     "awq_act_stats": (_i, [_p, _i, _i, _p, _p]),
     "awq_scale_candidates": (_i, [_p, _i, _p, _i, _p, _p]),
     "awq_quantize_pack": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p, _p]),
+    "awq_quantize_pack_ex": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "awq_fold_inv_scale": (_i, [_p, _p, _i, _i, _p, _p]),
     "awq_w4a16_matmul": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),
     "awq_w4a16_matmul_kernel": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p]),
     "awq_scale_search_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "awq_scale_search": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
+    "awq_scale_search_ex": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _sz,
+                                 _p]),
 }
 
 _LIB = None

@@ -111,7 +111,7 @@ const char* awq_status_string(int status) {
   }
 }
 
-int awq_version(void) { return 100; }
+int awq_version(void) { return 101; }
 
 size_t awq_packed_words_per_row(int K, int bits, int group) {
   int g = 0;
@@ -141,10 +141,12 @@ awq_status awq_scale_candidates(const double* m, int K, const float* alpha, int 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
-awq_status awq_quantize_pack(const uint16_t* W, const float* s, int N, int K, int bits, int group,
-                             uint32_t* qpacked, float* scales, uint8_t* zeros, void* stream) {
+awq_status awq_quantize_pack_ex(const uint16_t* W, const float* s, int N, int K, int bits,
+                                int group, int zero_point, uint32_t* qpacked, float* scales,
+                                uint8_t* zeros, void* stream) {
   if (!W || !qpacked || !scales || !zeros) return AWQ_ERR_INVALID_ARG;
   if (N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (zero_point != 0 && zero_point != 1) return AWQ_ERR_INVALID_ARG;
   if (!aligned16(W) || !aligned16(qpacked) || !aligned16(scales) || !aligned16(zeros) ||
       (s && !aligned16(s)))
     return AWQ_ERR_INVALID_ARG;
@@ -155,8 +157,13 @@ awq_status awq_quantize_pack(const uint16_t* W, const float* s, int N, int K, in
   st = device_ready();
   if (st != AWQ_OK) return st;
   return from_hip(awq::launch_quant_pack(reinterpret_cast<const __half*>(W), s, N, K, bits, g,
-                                         qpacked, scales, zeros,
+                                         zero_point != 0, qpacked, scales, zeros,
                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_quantize_pack(const uint16_t* W, const float* s, int N, int K, int bits, int group,
+                             uint32_t* qpacked, float* scales, uint8_t* zeros, void* stream) {
+  return awq_quantize_pack_ex(W, s, N, K, bits, group, 1, qpacked, scales, zeros, stream);
 }
 
 awq_status awq_fold_inv_scale(const uint16_t* X, const float* s, int M, int K, uint16_t* Xout,
@@ -191,11 +198,12 @@ size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bi
   return awq::search_workspace_bytes(N, K, T, n_alpha, bits, g);
 }
 
-awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
-                            const float* alpha_grid, int n_alpha, int bits, int group, float* s_out,
-                            double* loss_out, int* best_index, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
+                               const float* alpha_grid, int n_alpha, int bits, int group,
+                               int zero_point, float* s_out, double* loss_out, int* best_index,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!W || !Xcalib || !alpha_grid || !s_out) return AWQ_ERR_INVALID_ARG;
+  if (zero_point != 0 && zero_point != 1) return AWQ_ERR_INVALID_ARG;
   if (N <= 0 || K <= 0 || T <= 0 || n_alpha <= 0) return AWQ_ERR_INVALID_ARG;
   if (T >= 8192) return AWQ_ERR_UNSUPPORTED;
   if (!aligned16(W) || !aligned16(Xcalib) || !aligned16(s_out)) return AWQ_ERR_INVALID_ARG;
@@ -223,7 +231,8 @@ awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, in
   hipError_t e = hipMemcpyAsync(alpha_dev, alpha_grid, (size_t)n_alpha * 4, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return AWQ_ERR_HIP;
   e = awq::launch_search(reinterpret_cast<const __half*>(W), reinterpret_cast<const __half*>(Xcalib),
-                         N, K, T, alpha_dev, n_alpha, bits, g, rest, loss_dev, best_dev, s_out, s);
+                         N, K, T, alpha_dev, n_alpha, bits, g, zero_point != 0, rest, loss_dev,
+                         best_dev, s_out, s);
   if (e != hipSuccess) return from_hip(e);
   double* host_loss = loss_out;
   int host_best = 0;
@@ -237,6 +246,14 @@ awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, in
   if (e != hipSuccess) return AWQ_ERR_HIP;
   if (best_index) *best_index = host_best;
   return AWQ_OK;
+}
+
+awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
+                            const float* alpha_grid, int n_alpha, int bits, int group, float* s_out,
+                            double* loss_out, int* best_index, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return awq_scale_search_ex(W, Xcalib, N, K, T, alpha_grid, n_alpha, bits, group, 1, s_out,
+                             loss_out, best_index, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,8 +20,10 @@ inline int words_per_row(int K, int bits, int group) {
 hipError_t launch_act_stats(const __half* X, int T, int K, double* m, hipStream_t st);
 hipError_t launch_scale_candidates(const double* m, int K, const float* alpha, int n_alpha,
                                    float* s, hipStream_t st);
+// zero_point false: the symmetric grid
 hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int bits, int group,
-                             uint32_t* q, float* scales, uint8_t* zeros, hipStream_t st);
+                             bool zero_point, uint32_t* q, float* scales, uint8_t* zeros,
+                             hipStream_t st);
 hipError_t launch_fold(const __half* X, const float* s, int M, int K, __half* Y, hipStream_t st);
 
 // decode, int4, M <= 16. variant 0 picks the fastest kernel for the shape;
@@ -46,7 +48,8 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
 // scale search pieces
 size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);
 hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
-                         const float* alpha_dev, int n_alpha, int bits, int group, void* ws,
-                         double* loss_dev, int* best_dev, float* s_out, hipStream_t st);
+                         const float* alpha_dev, int n_alpha, int bits, int group,
+                         bool zero_point, void* ws, double* loss_dev, int* best_dev, float* s_out,
+                         hipStream_t st);
 
 }  // namespace awq

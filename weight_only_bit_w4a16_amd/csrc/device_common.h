@@ -42,6 +42,27 @@ __device__ __forceinline__ GroupGrid group_grid(float wmin, float wmax, int qmax
   return g;
 }
 
+// Symmetric grid of one group (the zero_point=false option of the AWQ
+// config): delta = max|W'| / (2^(b-1) - 1), codes rint(W' / delta) in
+// [-(2^(b-1) - 1), 2^(b-1) - 1] stored with the offset z = 2^(b-1); an
+// all-zero group gets delta = 1.
+__device__ __forceinline__ GroupGrid group_grid_sym(float amax, int half) {
+  GroupGrid g;
+  g.delta = amax == 0.0f ? 1.0f : amax / (float)(half - 1);
+  g.z = half;
+  g.rdelta = __builtin_amdgcn_rcpf(g.delta);
+  return g;
+}
+
+// the grid of a group from its min and max, symmetric or asymmetric
+template <bool SYM, int BITS>
+__device__ __forceinline__ GroupGrid grid_of(float wmin, float wmax) {
+  if constexpr (SYM)
+    return group_grid_sym(fmaxf(__builtin_fabsf(wmin), __builtin_fabsf(wmax)), 1 << (BITS - 1));
+  else
+    return group_grid(wmin, wmax, (1 << BITS) - 1);
+}
+
 // q = clamp(rint(wp / delta) + z, 0, qmax) with wp / delta the correctly
 // rounded fp32 quotient. |wp / delta| <= qmax, and wp * rdelta is within
 // 2 ulp of the exact quotient, so it rounds to the same integer unless it

@@ -14,7 +14,7 @@ namespace awq {
 // 8 codes into 24 bits; thread w of the group gathers the 24-bit blocks that
 // cover codes 10w..10w+9 from its neighbours and writes word w.
 // ---------------------------------------------------------------------------
-template <int BITS, int TPG>
+template <int BITS, int TPG, bool SYM>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ W,
                                                          const float* __restrict__ s, int N, int K,
                                                          uint32_t* __restrict__ Q,
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
       mn = fminf(mn, __shfl_xor(mn, off, TPG));
       mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
     }
-    const GroupGrid gg = group_grid(mn, mx, QMAX);
+    const GroupGrid gg = grid_of<SYM, BITS>(mn, mx);
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) packed |= (uint32_t)quant_code(wp[i], gg, QMAX) << (BITS * i);
@@ -108,15 +108,23 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
 }
 
 hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int bits, int group,
-                             uint32_t* q, float* scales, uint8_t* zeros, hipStream_t st) {
+                             bool zero_point, uint32_t* q, float* scales, uint8_t* zeros,
+                             hipStream_t st) {
   const int wpr = words_per_row(K, bits, group);
   // about 4 rows per thread
   const int gy = (N + 3) / 4 < 65535 ? (N + 3) / 4 : 65535;
   const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)gy);
   const uint16_t* w = reinterpret_cast<const uint16_t*>(W);
-#define AWQ_QP(B, T)                                                                           \
-  hipLaunchKernelGGL((quant_pack_kernel<B, T>), grid, dim3(256), 0, st, w, s, N, K, q, scales, \
-                     zeros, wpr)
+#define AWQ_QP1(B, T, SY)                                                                    \
+  hipLaunchKernelGGL((quant_pack_kernel<B, T, SY>), grid, dim3(256), 0, st, w, s, N, K, q, \
+                     scales, zeros, wpr)
+#define AWQ_QP(B, T)      \
+  do {                    \
+    if (zero_point)       \
+      AWQ_QP1(B, T, false); \
+    else                  \
+      AWQ_QP1(B, T, true);  \
+  } while (0)
   if (bits == 4) {
     if (group == 128) AWQ_QP(4, 16);
     else if (group == 256) AWQ_QP(4, 32);
@@ -127,6 +135,7 @@ hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int 
     else AWQ_QP(3, 64);
   }
 #undef AWQ_QP
+#undef AWQ_QP1
   return hipGetLastError();
 }
 

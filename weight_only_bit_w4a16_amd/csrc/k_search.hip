@@ -34,7 +34,7 @@ namespace {
 // (q - z) delta)), [N, K]. Otherwise D = W - (q - z) delta / s as hi = fp16(D)
 // and lo = fp16(D - hi), [N, 2K]: 128-wide k chunk c -> hi at 256 c, lo at
 // 256 c + 128.
-template <int BITS, int TPG, bool SCALED>
+template <int BITS, int TPG, bool SCALED, bool SYM>
 __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* __restrict__ W,
                                                                const float* __restrict__ s, int N,
                                                                int K, uint16_t* __restrict__ E) {
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
       mn = fminf(mn, __shfl_xor(mn, off, TPG));
       mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
     }
-    const GroupGrid gg = group_grid(mn, mx, QMAX);
+    const GroupGrid gg = grid_of<SYM, BITS>(mn, mx);
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -166,8 +166,9 @@ size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int gr
 }
 
 hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
-                         const float* alpha_dev, int n_alpha, int bits, int group, void* ws,
-                         double* loss_dev, int* best_dev, float* s_out, hipStream_t st) {
+                         const float* alpha_dev, int n_alpha, int bits, int group,
+                         bool zero_point, void* ws, double* loss_dev, int* best_dev, float* s_out,
+                         hipStream_t st) {
   const Layout L = layout(N, K, T, n_alpha);
   uint8_t* base = static_cast<uint8_t*>(ws);
   double* m = reinterpret_cast<double*>(base + L.m);
@@ -189,14 +190,19 @@ hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
   const bool scaled = (long long)T * N >= (1LL << 18);
   for (int a = 0; a < n_alpha; ++a) {
     const float* s = s_all + (size_t)a * K;
-#define AWQ_FQ(B, TP, SC) \
-  hipLaunchKernelGGL((fake_quant_error_kernel<B, TP, SC>), fgrid, dim3(256), 0, st, w, s, N, K, E)
-#define AWQ_FQ2(B, TP) \
-  do {                 \
-    if (scaled)        \
-      AWQ_FQ(B, TP, true); \
-    else               \
-      AWQ_FQ(B, TP, false); \
+#define AWQ_FQ(B, TP, SC, SY)                                                                  \
+  hipLaunchKernelGGL((fake_quant_error_kernel<B, TP, SC, SY>), fgrid, dim3(256), 0, st, w, s, N, \
+                     K, E)
+#define AWQ_FQ2(B, TP)                          \
+  do {                                          \
+    if (scaled && zero_point)                   \
+      AWQ_FQ(B, TP, true, false);               \
+    else if (scaled)                            \
+      AWQ_FQ(B, TP, true, true);                \
+    else if (zero_point)                        \
+      AWQ_FQ(B, TP, false, false);              \
+    else                                        \
+      AWQ_FQ(B, TP, false, true);               \
   } while (0)
     if (bits == 4) {
       if (group == 128) AWQ_FQ2(4, 16);
