@@ -48,6 +48,12 @@ R7  the layer-output error is the squared Frobenius norm over calibration
     the original fp16 W; the first minimum over the grid wins.
 R9  packing: see ``pack``.
 R10 scales are stored as the float32 delta, zero points as uint8.
+R18 the gated MLP that the fused gate/up product serves is LLaMA's:
+    Y = silu(X' Wg^T) * (X' Wu^T), silu(v) = v / (1 + e^-v); the pages credit
+    operator fusion for the speed-up (hungho77 blog -- "Why the engine is
+    part of the method") but name no activation. Gate and up read the same
+    normalized input, so they share one X' (one s). Evaluated here in
+    float64 from the exact products.
 R17 zero_point=false (the AwqConfig option, AWQ Explained -- "How the scale
     is chosen", last paragraph) is the symmetric grid: delta = max|W'| /
     (2^(b-1) - 1) per group, codes rint(W' / delta) in [-(2^(b-1) - 1),
@@ -253,6 +259,24 @@ def matmul_rows(Xp, qpacked, scales, zeros, bits, group, K, rows) -> np.ndarray:
     """Y[:, rows] only (for sampled checks at large N)."""
     rows = np.asarray(rows)
     return matmul(Xp, qpacked[rows], scales[rows], zeros[rows], bits, group, K)
+
+
+def silu(v) -> np.ndarray:
+    """silu(v) = v * sigmoid(v) = v / (1 + exp(-v)) in float64 (R18). For
+    v below about -709, exp(-v) overflows to inf and the quotient is -0,
+    the limit."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def gate_up_silu(Xp, qg, sg, zg, qu, su, zu, bits: int, group: int, K: int) -> np.ndarray:
+    """Y = silu(X' Wg^T) * (X' Wu^T) in float64 [M, N] (R18): the gate and
+    up projections of a gated MLP on one activation, then the elementwise
+    product."""
+    G = matmul(Xp, qg, sg, zg, bits, group, K)
+    U = matmul(Xp, qu, su, zu, bits, group, K)
+    return silu(G) * U
 
 
 # ----------------------------------------------------------------------------

@@ -508,3 +508,63 @@ def test_symmetric_search(bits):
     qa, sca, za = O.quantize(W, ones, bits, 128, zero_point=False)
     assert np.array_equal(qa, q0) and np.array_equal(sca, sc0)
     assert losses[best] < losses[0]
+
+
+# ---------------------------------------------------------------------------
+# gated MLP: silu(X' Wg^T) * (X' Wu^T) (R18)
+# ---------------------------------------------------------------------------
+
+def test_silu_against_library_and_identities():
+    torch = pytest.importorskip("torch")
+    v = np.concatenate([np.linspace(-30, 30, 1201), [-800.0, -710.0, 0.0, 1e-300, 50.0, 800.0]])
+    ref = torch.nn.functional.silu(torch.from_numpy(v)).numpy()
+    got = O.silu(v)
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-300)
+    assert O.silu(0.0) == 0.0 and O.silu(800.0) == 800.0 and O.silu(-800.0) == 0.0
+    # sigmoid(-v) = 1 - sigmoid(v)  =>  silu(-v) = silu(v) - v
+    w = np.linspace(-20, 20, 401)
+    assert np.allclose(O.silu(-w), O.silu(w) - w, rtol=0, atol=1e-12)
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_gate_up_silu_picks_single_weights(bits):
+    """A unit activation e_k selects column k of both matrices, so each output
+    is silu(wg_nk) * wu_nk of the dequantized weights (read here with an
+    independent bit-level unpack)."""
+    K, N = 256, 5
+    Wg = datagen.random_f16((N, K), 0.5, seed=50 + bits)
+    Wu = datagen.random_f16((N, K), 0.5, seed=60 + bits)
+    qg, sg, zg = O.quantize_pack(Wg, None, bits, 128)
+    qu, su, zu = O.quantize_pack(Wu, None, bits, 128)
+    for k in (0, 1, 127, 128, 255):
+        X = np.zeros((1, K), np.float16)
+        X[0, k] = 1.0
+        Y = O.gate_up_silu(X, qg, sg, zg, qu, su, zu, bits, 128, K)[0]
+        for n in range(N):
+            cg = _unpack_by_hand(qg[n], bits, 128, K)[k]
+            cu = _unpack_by_hand(qu[n], bits, 128, K)[k]
+            wg = (cg - int(zg[n, k // 128])) * float(sg[n, k // 128])
+            wu = (cu - int(zu[n, k // 128])) * float(su[n, k // 128])
+            assert Y[n] == pytest.approx(wg / (1.0 + math.exp(-wg)) * wu, rel=1e-14, abs=1e-300)
+
+
+def test_gate_up_silu_exact_products():
+    """Exact-rational gate and up products, then silu in float64."""
+    K, N, M = 256, 3, 2
+    Wg = datagen.random_f16((N, K), 0.02, seed=71)
+    Wu = datagen.random_f16((N, K), 0.02, seed=72)
+    X = datagen.random_f16((M, K), 1.0, seed=73)
+    qg, sg, zg = O.quantize_pack(Wg, None, 4, 128)
+    qu, su, zu = O.quantize_pack(Wu, None, 4, 128)
+    Y = O.gate_up_silu(X, qg, sg, zg, qu, su, zu, 4, 128, K)
+
+    def exact(qp, sc, z, n, m):
+        codes = _unpack_by_hand(qp[n], 4, 128, K)
+        return sum(Fraction(float(X[m, k])) * (codes[k] - int(z[n, k // 128]))
+                   * Fraction(float(sc[n, k // 128])) for k in range(K))
+    for m in range(M):
+        for n in range(N):
+            g = float(exact(qg, sg, zg, n, m))
+            u = float(exact(qu, su, zu, n, m))
+            assert Y[m, n] == pytest.approx(g / (1.0 + math.exp(-g)) * u, rel=1e-12)
