@@ -33,6 +33,7 @@ SEED_ROOT = 0xA3A
 STREAM_WEIGHT = 1
 STREAM_OUTLIER_CHANNELS = 2
 STREAM_CALIB = 3
+STREAM_GATE_WEIGHT = 4
 STREAM_ACT = 100  # + M, so that every batch size has its own stream
 
 
@@ -103,6 +104,12 @@ def outlier_channels(K: int, count: int, wid: int) -> np.ndarray:
 def weight(w: Workload) -> np.ndarray:
     """fp16 [N, K], row = output channel (PyTorch Linear layout)."""
     return normal_f16((w.N, w.K), 0.02, w.wid, STREAM_WEIGHT)
+
+
+def gate_weight(w: Workload) -> np.ndarray:
+    """fp16 [N, K]: the gate projection beside an up projection of the same
+    shape (a gated MLP), drawn like `weight` from its own stream."""
+    return normal_f16((w.N, w.K), 0.02, w.wid, STREAM_GATE_WEIGHT)
 
 
 def activations(w: Workload, rows: int, stream: int) -> np.ndarray:

@@ -162,6 +162,24 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
                                    const uint8_t* zeros, int M, int N, int K, int bits, int group,
                                    uint16_t* Y, int kernel, void* stream);
 
+/* The gate and up projections of a gated MLP fused into one call (hungho77
+ * blog -- "Why the engine is part of the method": the speed-up comes from
+ * kernels that fuse operators). Both projections read the same activation
+ * X' once and the elementwise epilogue runs on their float32 sums:
+ *   G[m, n] = sum_k X'[m, k] * (qg[n, k] - zg[n, g(k)]) * dg[n, g(k)]
+ *   U[m, n] = the same with (qu, su, zu)
+ *   Y[m, n] = fp16(silu(G) * U),  silu(v) = v / (1 + e^-v), in float32.
+ * X': dev fp16 [M, K], already divided by the scale s both matrices were
+ * quantized with (one s per activation: gate and up share their input);
+ * (qg, sg, zg) and (qu, su, zu): two [N, K] matrices packed as by
+ * awq_quantize_pack(_ex); Y: dev fp16 [M, N]. int3 needs group 128. M = 1
+ * (int4) runs the decode kernel, other M the prefill kernel, both reading
+ * X' once for the two matrices. Asynchronous on `stream`. */
+awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const float* sg,
+                                  const uint8_t* zg, const uint32_t* qu, const float* su,
+                                  const uint8_t* zu, int M, int N, int K, int bits, int group,
+                                  uint16_t* Y, void* stream);
+
 /* Bytes of device workspace awq_scale_search needs for these sizes
  * (0 if the sizes are invalid). */
 size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);

@@ -157,3 +157,21 @@ def test_scale_search_validation():
                                      ctypes.byref(best), ws, nbytes, NULL)
     assert call_ex(2) == E.AWQ_ERR_INVALID_ARG
     assert call_ex(0, ws=NULL) == E.AWQ_ERR_WORKSPACE
+
+
+def test_gate_up_validation():
+    h = awq.lib()
+    E = _lib
+
+    def call(X=P, qg=P, qu=P, M=1, N=64, K=256, bits=4, group=128, Y=P2):
+        return h.awq_w4a16_gate_up_silu(X, qg, P, P, qu, P, P, M, N, K, bits, group, Y, NULL)
+    assert call(X=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert call(qu=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert call(qg=MIS) == E.AWQ_ERR_INVALID_ARG
+    assert call(M=0) == E.AWQ_ERR_INVALID_ARG
+    assert call(K=200) == E.AWQ_ERR_INVALID_ARG
+    assert call(bits=2) == E.AWQ_ERR_UNSUPPORTED
+    assert call(bits=3, group=256, K=512) == E.AWQ_ERR_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == E.AWQ_ERR_NO_DEVICE

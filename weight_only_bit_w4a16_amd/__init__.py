@@ -20,7 +20,7 @@ from ._lib import AwqError, check, lib  # noqa: F401
 
 __all__ = [
     "AwqError", "lib", "packed_words_per_row", "act_stats", "scale_candidates",
-    "quantize_pack", "fold_inv_scale", "w4a16_matmul", "scale_search",
+    "quantize_pack", "fold_inv_scale", "w4a16_matmul", "gate_up_silu", "scale_search",
     "scale_search_workspace_bytes", "KERNEL_AUTO", "KERNEL_DECODE", "KERNEL_DECODE_EXACT",
     "KERNEL_PREFILL",
 ]
@@ -154,6 +154,31 @@ def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, ou
         r = lib().awq_w4a16_matmul_kernel(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M,
                                           N, K, bits, group, _ptr(y), kernel, st)
     check(r, "awq_w4a16_matmul")
+    return y
+
+
+def gate_up_silu(Xp, gate, up, bits: int = 4, group: int = 128, out=None, stream=None):
+    """Y = fp16(silu(X' Wg^T) * (X' Wu^T)) (fp16 [M, N]); `gate` and `up` are
+    (qpacked, scales, zeros) triples of two [N, K] matrices."""
+    torch = _torch()
+    _need(Xp, "Xp", torch.float16, 2)
+    M, K = Xp.shape
+    g = _group(K, group)
+    wpr = packed_words_per_row(K, bits, group)
+    N = gate[0].shape[0]
+    for name, (q, sc, z) in (("gate", gate), ("up", up)):
+        _need(q, f"{name} qpacked", torch.int32, 2)
+        _need(sc, f"{name} scales", torch.float32, 2)
+        _need(z, f"{name} zeros", torch.uint8, 2)
+        if tuple(q.shape) != (N, wpr):
+            raise ValueError(f"{name} qpacked must be [N, words_per_row]")
+        if tuple(sc.shape) != (N, K // g) or tuple(z.shape) != (N, K // g):
+            raise ValueError(f"{name} scales/zeros must be [N, K/group]")
+    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
+    check(lib().awq_w4a16_gate_up_silu(_ptr(Xp), _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]),
+                                       _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), M, N, K, bits,
+                                       group, _ptr(y), _stream(stream)),
+          "awq_w4a16_gate_up_silu")
     return y
 
 

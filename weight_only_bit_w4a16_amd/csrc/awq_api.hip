@@ -191,6 +191,38 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
   return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, kernel);
 }
 
+awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const float* sg,
+                                  const uint8_t* zg, const uint32_t* qu, const float* su,
+                                  const uint8_t* zu, int M, int N, int K, int bits, int group,
+                                  uint16_t* Y, void* stream) {
+  if (!X || !qg || !sg || !zg || !qu || !su || !zu || !Y) return AWQ_ERR_INVALID_ARG;
+  if (M <= 0 || N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(qg) || !aligned16(sg) || !aligned16(zg) || !aligned16(qu) ||
+      !aligned16(su) || !aligned16(zu) || !aligned16(Y))
+    return AWQ_ERR_INVALID_ARG;
+  int g = 0;
+  awq_status st = check_group(K, bits, group, &g);
+  if (st != AWQ_OK) return st;
+  if (bits == 3 && g != 128) return AWQ_ERR_UNSUPPORTED;
+  if ((long long)M * K > (1LL << 31) || (long long)N * K > (1LL << 34)) return AWQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != AWQ_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const __half* x = reinterpret_cast<const __half*>(X);
+  __half* y = reinterpret_cast<__half*>(Y);
+  hipError_t e = hipErrorNotSupported;
+  if (M == 1)
+    e = bits == 4 ? awq::launch_gate_up_w4_m1(x, qg, sg, zg, qu, su, zu, N, K, g, y, s)
+                  : awq::launch_gate_up_w3_m1(x, qg, sg, zg, qu, su, zu, N, K, g, y, s);
+  else if (bits == 4 && M <= 16)
+    e = awq::launch_gemv_w4_mx(x, qg, sg, zg, M, N, K, g, y, s, qu, su, zu);
+  if (e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    e = awq::launch_gemm_gate_up(x, qg, sg, zg, qu, su, zu, M, N, K, bits, g, y, s);
+  }
+  return from_hip(e);
+}
+
 size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group) {
   int g = 0;
   if (N <= 0 || T <= 0 || T >= 8192 || n_alpha <= 0) return 0;

@@ -45,6 +45,27 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
                        const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
                        hipStream_t st);
 
+// gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)); M = 1 int4 / int3 decode
+// (K up to 96 groups), and the prefill kernel for any M
+hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float* sg,
+                                const uint8_t* zg, const uint32_t* qu, const float* su,
+                                const uint8_t* zu, int N, int K, int group, __half* Y,
+                                hipStream_t st);
+// decode, int4, 2 <= M <= 16, K <= 8192 (NotSupported otherwise); with q2
+// set, the gated-MLP form silu(X Wq^T) * (X Wq2^T)
+hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* scales,
+                             const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st, const uint32_t* q2, const float* scales2,
+                             const uint8_t* zeros2);
+hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float* sg,
+                                const uint8_t* zg, const uint32_t* qu, const float* su,
+                                const uint8_t* zu, int N, int K, int group, __half* Y,
+                                hipStream_t st);
+hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float* sg,
+                               const uint8_t* zg, const uint32_t* qu, const float* su,
+                               const uint8_t* zu, int M, int N, int K, int bits, int group,
+                               __half* Y, hipStream_t st);
+
 // scale search pieces
 size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);
 hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,

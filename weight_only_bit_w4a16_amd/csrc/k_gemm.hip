@@ -97,6 +97,15 @@ struct Dq {
 
 }  // namespace
 
+// EPI: 0 stores Y = fp16(A B^T); 1 writes the float64 square sum of the
+// tile (the search); 2 is the gated-MLP form: B holds two weight matrices
+// (gate from Bsrc/S/Z, up from B2/S2/Z2) and the tile's B rows alternate
+// between them in blocks of 32 (tile row r reads row
+// n0 + 32 (r / 64) + r % 32 of matrix (r / 32) % 2), so every wavefront holds
+// the gate and up sums of the same outputs in neighbouring accumulators and
+// stores fp16(silu(g) u), silu(g) = g / (1 + e^-g), in fp32. A tile then
+// covers BN / 2 outputs.
+//
 // ZW: zero points are read as the aligned 32-bit word holding them (the
 // zero-point array is a whole number of words); otherwise byte by byte.
 // Word loads keep the loop-carried value 32 bits wide, so no byte
@@ -106,7 +115,8 @@ template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW, int NST
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const float* __restrict__ S,
     const uint8_t* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
-    uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo) {
+    uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo,
+    const void* __restrict__ B2, const float* __restrict__ S2, const uint8_t* __restrict__ Z2) {
   constexpr int NT = 64 * WGM * WGN;
   static_assert(NST == 2 || NST == 4, "register stages");
   using C = Cfg<BMODE, BM, BN, NT>;
@@ -115,6 +125,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   constexpr int BK = C::BK;
   constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;  // 32x32 tiles per wavefront
   static_assert(TM >= 1 && TN >= 1 && BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile");
+  static_assert(EPI != 2 || (TN % 2 == 0 && BMODE != 0), "gate/up pairs need an even TN");
+  constexpr int BNO = EPI == 2 ? BN / 2 : BN;  // outputs per tile along N
   __shared__ __align__(16) uint16_t lds_a[2][BM * STR];
   __shared__ __align__(16) uint16_t lds_b[2][BN * STR];
 
@@ -127,12 +139,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // XCD a contiguous run of tiles that walk M for a fixed N tile, so the
   // weight tile is reused from that XCD's L2
   const int mt = (M + BM - 1) / BM;
-  const int ntl = (N + BN - 1) / BN;
+  const int ntl = (N + BNO - 1) / BNO;
   const int total = mt * ntl;
   int t = blockIdx.x;
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   const int m0 = (t % mt) * BM;
-  const int n0 = (t / mt) * BN;
+  const int n0 = (t / mt) * BNO;
   // fp16 B with hilo set holds each term as a hi and a lo fp16 part,
   // [N][2K]: 256-wide block c = (hi of k 128c..128c+127 | lo of the same k),
   // so a 64-wide step s reads activations 128*(s/4) + 64*(s%2)
@@ -153,12 +165,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     }
   }
 
-  auto load_zero = [&](size_t idx, uint32_t& zw, uint32_t& zsh) {
+  // output row of tile B row r, and whether it belongs to the second matrix
+  auto brow_n = [&](int r) {
+    return EPI == 2 ? min(n0 + 32 * (r >> 6) + (r & 31), N - 1) : min(n0 + r, N - 1);
+  };
+  auto bsel = [&](int r) { return EPI == 2 && ((r >> 5) & 1) != 0; };
+  auto load_zero = [&](const uint8_t* Zp, size_t idx, uint32_t& zw, uint32_t& zsh) {
     if constexpr (ZW) {
-      zw = reinterpret_cast<const uint32_t*>(Z)[idx >> 2];
+      zw = reinterpret_cast<const uint32_t*>(Zp)[idx >> 2];
       zsh = 8u * (uint32_t)(idx & 3);
     } else {
-      zw = Z[idx];
+      zw = Zp[idx];
       zsh = 0u;
     }
   };
@@ -188,14 +205,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       }
     } else if constexpr (BMODE == 4) {
       // BW consecutive words of one row (8 words = 64 codes per row and step)
-      const uint32_t* Q = static_cast<const uint32_t*>(Bsrc);
       const int r = (tid * C::BW) / 8, w0 = (tid * C::BW) % 8;
-      const int n = min(n0 + r, N - 1);
+      const bool sel = bsel(r);
+      const uint32_t* Q = static_cast<const uint32_t*>(sel ? B2 : Bsrc);
+      const int n = brow_n(r);
       const uint32_t* p = Q + (size_t)n * wpr + 8 * ks + w0;
       if constexpr (SZ.value) {
         const int g = (ks * BK) >> (7 + gshift);
-        st.d = S[(size_t)n * ng + g];
-        load_zero((size_t)n * ng + g, st.zw, st.zsh);
+        st.d = (sel ? S2 : S)[(size_t)n * ng + g];
+        load_zero(sel ? Z2 : Z, (size_t)n * ng + g, st.zw, st.zsh);
       }
       if constexpr (C::BW == 4) {
         const u32x4 v = ld_nt(reinterpret_cast<const u32x4*>(p));
@@ -212,20 +230,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         for (int q = 0; q < C::BW; ++q) st.b[q] = ld_nt(p + q);
       }
     } else {  // int3: item = (row, quarter); quarters cover words 0-3, 4-6, 7-9, 10-12
-      const uint32_t* Q = static_cast<const uint32_t*>(Bsrc);
 #pragma unroll
       for (int i = 0; i < C::BIT; ++i) {
         const int id = tid + NT * i;
         const int r = id >> 2, qt = id & 3;
-        const int n = min(n0 + r, N - 1);
+        const bool sel = bsel(r);
+        const uint32_t* Q = static_cast<const uint32_t*>(sel ? B2 : Bsrc);
+        const int n = brow_n(r);
         // dword-aligned 16-byte load that stays inside the group: quarter 3
         // reads words 9..12 and uses the last three
         const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
         const u32x4a4 v =
             ld_nt(reinterpret_cast<const u32x4a4*>(Q + (size_t)n * wpr + ks * 13 + w0));
         st.b[i] = u32x4{v[0], v[1], v[2], v[3]};
-        st.d[i] = S[(size_t)n * ng + ks];
-        load_zero((size_t)n * ng + ks, st.zw[i], st.zsh[i]);
+        st.d[i] = (sel ? S2 : S)[(size_t)n * ng + ks];
+        load_zero(sel ? Z2 : Z, (size_t)n * ng + ks, st.zw[i], st.zsh[i]);
       }
     }
   };
@@ -448,6 +467,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
           if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][v]));
         }
       }
+  } else if constexpr (EPI == 2) {
+    // accumulator pair (j, j + 1) = (gate, up) of outputs n
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; j += 2) {
+        const int n = n0 + (BNO / WGN) * wn + 32 * (j >> 1) + lr;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m =
+              m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const float g = acc[i][j][v];
+          const float val = g / (1.0f + __expf(-g)) * acc[i][j + 1][v];
+          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(val));
+        }
+      }
   } else {
     __shared__ double wsum[WGM * WGN];
     float sq = 0.f;
@@ -506,11 +541,11 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
     if (zw)                                                                                     \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST>),                  \
                          dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
-                         zeros, M, N, K, wpr, gshift, y, nullptr, 0);                           \
+                         zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr, nullptr, nullptr); \
     else                                                                                        \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST>),                 \
                          dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
-                         zeros, M, N, K, wpr, gshift, y, nullptr, 0);                           \
+                         zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr, nullptr, nullptr); \
   } while (0)
   if (bits == 4) {
     // the largest tile that still gives every compute unit work
@@ -527,6 +562,46 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   return hipGetLastError();
 }
 
+// gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)), both products on one A tile
+hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float* sg,
+                               const uint8_t* zg, const uint32_t* qu, const float* su,
+                               const uint8_t* zu, int M, int N, int K, int bits, int group,
+                               __half* Y, hipStream_t st) {
+  if (bits == 3 && group != 128) return hipErrorNotSupported;
+  int gshift = 0;
+  while ((128 << gshift) < group) ++gshift;
+  const int wpr = words_per_row(K, bits, group);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  const unsigned cus = (unsigned)cu_n();
+  const bool zw = ((size_t)N * (size_t)(K / group)) % 4 == 0;
+#define AWQ_GU(BMODE, BM, BN, WGM, WGN, NST)                                                     \
+  do {                                                                                            \
+    if (zw)                                                                                       \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 2, BM, BN, WGM, WGN, true, NST>),                    \
+                         dim3(tiles_of(M, N, BM, BN / 2)), dim3(64 * WGM * WGN), 0, st, x, qg, sg, \
+                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu);                    \
+    else                                                                                          \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 2, BM, BN, WGM, WGN, false, NST>),                   \
+                         dim3(tiles_of(M, N, BM, BN / 2)), dim3(64 * WGM * WGN), 0, st, x, qg, sg, \
+                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu);                    \
+  } while (0)
+  if (bits == 4) {
+    if (tiles_of(M, N, 256, 128) >= cus)
+      AWQ_GU(4, 256, 256, 2, 4, 2);
+    else if (tiles_of(M, N, 128, 64) >= cus)
+      AWQ_GU(4, 128, 128, 2, 2, 4);
+    else
+      AWQ_GU(4, 64, 128, 2, 2, 4);
+  } else {
+    // 8 wavefronts, so each thread loads one (row, quarter) item per step
+    // (two items per thread put the register stages in scratch memory)
+    AWQ_GU(3, 128, 128, 4, 2, 4);
+  }
+#undef AWQ_GU
+  return hipGetLastError();
+}
+
 // ||A B^T||_F^2 as one float64 partial per workgroup tile; A is [M, K] fp16,
 // B is [N, K] fp16, or with hilo [N, 2K] holding hi and lo parts per
 // 128-wide k chunk (then the product is A (Bhi + Blo)^T)
@@ -534,7 +609,7 @@ hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N,
                              double* partial, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false, 2>), dim3(tiles_of(M, N, 128, 128)),
                      dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial,
-                     hilo ? 1 : 0);
+                     hilo ? 1 : 0, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -353,11 +353,19 @@ int cu_count() {
 // The activation operands of all pieces depend only on k: they are prepared
 // once per workgroup in LDS and shared by its 4 wavefronts, which stream
 // different rows.
+//
+// DUAL (the gate and up projections of a gated MLP, which read the same
+// activation): the ring walks items 2i (gate row n_i, from Q/S/Z) and 2i + 1
+// (up row n_i, from Q2/S2/Z2); the gate sum waits in a register and the up
+// item stores fp16(silu(g) * u), silu(g) = g / (1 + e^-g), in fp32.
 // ---------------------------------------------------------------------------
-template <int SP, int RPF, bool FULL>
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int SP, int RPF, bool FULL, bool DUAL>
 __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int gshift) {
+    const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
+    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int gshift) {
   __shared__ u32x4 xs[SP][4][64];  // [piece][operand][lane]
   __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
   const int lane = threadIdx.x & 63;
@@ -457,21 +465,27 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
       db[r][s] = 0.f;
       zb[r][s] = 0u;
     }
-  const int last = max(cnt - 1, 0);
+  const int items = DUAL ? 2 * cnt : cnt;  // ring items (rows, or gate/up row pairs)
+  const int last = max(items - 1, 0);
   const uint32_t magic = kMagic2;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + 16 * j + 4 * jj;
+  const uint32_t* qlane2 = DUAL ? Q2 + 16 * j + 4 * jj : qlane;
   float outv = 0.f;
-  for (int i0 = -RPF; i0 < cnt; i0 += RPF) {
+  float gsum = 0.f;  // DUAL: the gate sum of the current row
+  for (int i0 = -RPF; i0 < items; i0 += RPF) {
 #pragma unroll
     for (int r = 0; r < RPF; ++r) {
-      const int row = i0 + r;
-      const size_t nn = (size_t)min(gw + min(row + RPF, last) * NW, N - 1);  // refill target
+      const int row = i0 + r;  // ring item
+      const int nit = min(row + RPF, last);  // refill target item
+      const size_t nn = (size_t)min(gw + (DUAL ? nit >> 1 : nit) * NW, N - 1);
+      // the refill target's matrix (i0 is a multiple of RPF)
+      const bool up2 = DUAL && ((RPF % 2 == 0) ? (r & 1) != 0 : (nit & 1) != 0);
       // keep the rows in program order, so that each row waits only for its
       // own slots and the other RPF - 1 rows' loads stay in flight
       __builtin_amdgcn_sched_barrier(0);
       if (row >= 0) {  // uniform
-        const bool vrow = row < cnt;
+        const bool vrow = row < items;
         float y = 0.f;
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
@@ -510,14 +524,21 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
             (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
-        outv = (row & 63) == lane ? sum : outv;
+        if constexpr (DUAL) {
+          const bool is_up = (RPF % 2 == 0) ? (r & 1) != 0 : (row & 1) != 0;
+          const float val = silu_f(gsum) * sum;
+          outv = (is_up && ((row >> 1) & 63) == lane) ? val : outv;
+          gsum = sum;
+        } else {
+          outv = (row & 63) == lane ? sum : outv;
+        }
       }
       // refill the slots with the same pieces of the row RPF ahead
-      const uint32_t* qn = qlane + nn * wpr;
-      const float* sn = S + nn * ngr;
-      const uint8_t* zn = Z + nn * ngr;
+      const uint32_t* qn = (up2 ? qlane2 : qlane) + nn * wpr;
+      const float* sn = (up2 ? S2 : S) + nn * ngr;
+      const uint8_t* zn = (up2 ? Z2 : Z) + nn * ngr;
       // rows past this wavefront's last need no loads (uniform branch)
-      if (row + RPF < cnt) {
+      if (row + RPF < items) {
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
           wb[r][s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
@@ -567,10 +588,12 @@ constexpr float kW3InvHi[5] = {0.25f, 0.03125f, 1.f, 0.125f, 1.f};
 __device__ __forceinline__ int w3_first_word(int jj) { return jj == 0 ? 0 : (jj == 1 ? 4 : (jj == 2 ? 7 : 9)); }
 }  // namespace
 
-template <int SP, int RPF, bool FULL>
+// DUAL: gate and up rows alternate in the ring as in the int4 kernel.
+template <int SP, int RPF, bool FULL, bool DUAL>
 __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int wpr) {
+    const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
+    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int wpr) {
   __shared__ u32x4 xs[SP][5][64];  // [piece][operand][lane]
   __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
   const int lane = threadIdx.x & 63;
@@ -673,19 +696,24 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
       db[r][s] = 0.f;
       zb[r][s] = 0u;
     }
-  const int last = max(cnt - 1, 0);
+  const int items = DUAL ? 2 * cnt : cnt;  // ring items (rows, or gate/up row pairs)
+  const int last = max(items - 1, 0);
   const uint32_t magic = kMagic2;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + woff;
+  const uint32_t* qlane2 = DUAL ? Q2 + woff : qlane;
   float outv = 0.f;
-  for (int i0 = -RPF; i0 < cnt; i0 += RPF) {
+  float gsum = 0.f;  // DUAL: the gate sum of the current row
+  for (int i0 = -RPF; i0 < items; i0 += RPF) {
 #pragma unroll
     for (int r = 0; r < RPF; ++r) {
-      const int row = i0 + r;
-      const size_t nn = (size_t)min(gw + min(row + RPF, last) * NW, N - 1);  // refill target
+      const int row = i0 + r;  // ring item
+      const int nit = min(row + RPF, last);  // refill target item
+      const size_t nn = (size_t)min(gw + (DUAL ? nit >> 1 : nit) * NW, N - 1);
+      const bool up2 = DUAL && ((RPF % 2 == 0) ? (r & 1) != 0 : (nit & 1) != 0);
       __builtin_amdgcn_sched_barrier(0);
       if (row >= 0) {  // uniform
-        const bool vrow = row < cnt;
+        const bool vrow = row < items;
         float y = 0.f;
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
@@ -724,13 +752,20 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
             (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
-        outv = (row & 63) == lane ? sum : outv;
+        if constexpr (DUAL) {
+          const bool is_up = (RPF % 2 == 0) ? (r & 1) != 0 : (row & 1) != 0;
+          const float val = silu_f(gsum) * sum;
+          outv = (is_up && ((row >> 1) & 63) == lane) ? val : outv;
+          gsum = sum;
+        } else {
+          outv = (row & 63) == lane ? sum : outv;
+        }
       }
-      const uint32_t* qn = qlane + nn * wpr;
-      const float* sn = S + nn * nch;
-      const uint8_t* zn = Z + nn * nch;
+      const uint32_t* qn = (up2 ? qlane2 : qlane) + nn * wpr;
+      const float* sn = (up2 ? S2 : S) + nn * nch;
+      const uint8_t* zn = (up2 ? Z2 : Z) + nn * nch;
       // rows past this wavefront's last need no loads (uniform branch)
-      if (row + RPF < cnt) {
+      if (row + RPF < items) {
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
           const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
@@ -759,14 +794,14 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   const bool full = nch % 16 == 0;
-#define AWQ_W3(SM, RP)                                                                          \
-  do {                                                                                          \
-    if (full)                                                                                   \
-      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true>), g1, block, 0, st, x, q, scales,     \
-                         zeros, y, N, K, wpr);                                                  \
-    else                                                                                        \
-      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false>), g1, block, 0, st, x, q, scales,    \
-                         zeros, y, N, K, wpr);                                                  \
+#define AWQ_W3(SM, RP)                                                                        \
+  do {                                                                                        \
+    if (full)                                                                                 \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, false>), g1, block, 0, st, x, q,    \
+                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr);             \
+    else                                                                                      \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, false>), g1, block, 0, st, x, q,   \
+                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr);             \
   } while (0)
   switch (sp) {
     case 1: AWQ_W3(1, 4); break;
@@ -796,10 +831,14 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
 // through a 4-chunk register ring that runs across row blocks; the scales
 // and zero points of the next row block are staged in LDS meanwhile, and
 // the slices' partial sums of a row block are added in LDS in a fixed order.
-template <int CPW>
+// DUAL (gate and up of a gated MLP): the workgroup walks items 2j (gate row
+// block j, from Q/S/Z) and 2j + 1 (up row block j, from Q2/S2/Z2); the
+// gate sums wait in LDS and the up item stores fp16(silu(g) * u).
+template <int CPW, bool DUAL>
 __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
+    const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
+    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
     int rbw) {
   static_assert(CPW % 4 == 0, "the ring of 4 chunks must tile a slice");
   extern __shared__ __align__(16) uint8_t smem[];
@@ -813,19 +852,29 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   const int nrb = (N + 15) >> 4;
   const int rb0 = blockIdx.x * rbw;
   const int nj = min(rbw, nrb - rb0);
+  const int nit = DUAL ? 2 * nj : nj;  // items: row blocks, or gate/up row block pairs
   const int cbeg = wave * CPW;
 
   float2* csx = reinterpret_cast<float2*>(smem);                  // [nch][16] (C, S)
   float* szf = reinterpret_cast<float*>(csx + (size_t)nch * 16);  // [2][16][ngr] scales
   float* part = szf + 2 * 16 * ngr;                               // [2][WV][4][64] partials
-  uint8_t* szb = reinterpret_cast<uint8_t*>(part + 2 * WV * 256);  // [2][16][ngr] zeros
+  float* gsum = part + 2 * WV * 256;                              // [256] DUAL gate sums
+  uint8_t* szb = reinterpret_cast<uint8_t*>(gsum + (DUAL ? 256 : 0));  // [2][16][ngr] zeros
 
-  // ---- weight ring: 4 chunks ahead, across row blocks -----------------------
+  // first row of item it's row block, and whether it reads the up matrix
+  auto item_row = [&](int it) {
+    const int c = min(it, nit - 1);
+    return (rb0 + (DUAL ? c >> 1 : c)) * 16;
+  };
+  auto item_up = [&](int it) { return DUAL && (min(it, nit - 1) & 1) != 0; };
+
+  // ---- weight ring: 4 chunks ahead, across items ----------------------------
   const uint32_t* qlane = Q + 4 * q;
-  auto wload = [&](int j, int i) {  // chunk i of the slice, row block j
-    const size_t n = (size_t)min((rb0 + min(j, nj - 1)) * 16 + nl, N - 1);
+  const uint32_t* qlane2 = DUAL ? Q2 + 4 * q : qlane;
+  auto wload = [&](int it, int i) {  // chunk i of the slice, item it
+    const size_t n = (size_t)min(item_row(it) + nl, N - 1);
     const int c = min(cbeg + i, nch - 1);
-    return ld_nt(reinterpret_cast<const u32x4*>(qlane + n * wpr + c * 16));
+    return ld_nt(reinterpret_cast<const u32x4*>((item_up(it) ? qlane2 : qlane) + n * wpr + c * 16));
   };
   u32x4 ring[4];
 #pragma unroll
@@ -837,14 +886,16 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   constexpr int SZI = 3;     // per thread: 16 * 96 / 512 (K up to 12288)
   float szv[SZI];
   uint8_t zzv[SZI];
-  auto sz_load = [&](int j) {
+  auto sz_load = [&](int it) {
+    const float* Sp = item_up(it) ? S2 : S;
+    const uint8_t* Zp = item_up(it) ? Z2 : Z;
 #pragma unroll
     for (int u = 0; u < SZI; ++u) {
       const int idx = min((int)threadIdx.x + (int)blockDim.x * u, szn - 1);
       const int r = idx / ngr, g = idx - r * ngr;
-      const size_t n = (size_t)min((rb0 + min(j, nj - 1)) * 16 + r, N - 1);
-      szv[u] = S[n * ngr + g];
-      zzv[u] = Z[n * ngr + g];
+      const size_t n = (size_t)min(item_row(it) + r, N - 1);
+      szv[u] = Sp[n * ngr + g];
+      zzv[u] = Zp[n * ngr + g];
     }
   };
   auto sz_store = [&](int buf) {
@@ -887,9 +938,9 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
 
   const uint32_t magic = kMagic2;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < nj; ++j) {
+  for (int j = 0; j < nit; ++j) {  // j: item
     const int buf = j & 1;
-    if (j + 1 < nj) sz_load(j + 1);  // uniform
+    if (j + 1 < nit) sz_load(j + 1);  // uniform
     floatx4 y = zero4;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -925,15 +976,23 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[((buf * WV + wave) * 4 + r) * 64 + lane] = y[r];
-    if (j + 1 < nj) sz_store(buf ^ 1);
+    if (j + 1 < nit) sz_store(buf ^ 1);
     __syncthreads();
-    // slices' partials of row block j, added in slice order
+    // slices' partials of item j, added in slice order (thread t always
+    // handles the same entries, so a gate sum is read back by its writer)
     for (int t = threadIdx.x; t < 256; t += blockDim.x) {
       const int l = t & 63, r = t >> 6;
       float v = 0.f;
       for (int w = 0; w < WV; ++w) v += part[((buf * WV + w) * 4 + r) * 64 + l];
       const int m = 4 * (l >> 4) + r;
-      const int n = (rb0 + j) * 16 + (l & 15);
+      const int n = item_row(j) + (l & 15);
+      if constexpr (DUAL) {
+        if ((j & 1) == 0) {
+          gsum[t] = v;
+          continue;
+        }
+        v = silu_f(gsum[t]) * v;
+      }
       if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(v));
     }
   }
@@ -958,7 +1017,9 @@ hipError_t allow_lds(size_t lds) {
 // (K up to 8192; larger K does not fit the register budget)
 hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* scales,
                              const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                             hipStream_t st) {
+                             hipStream_t st, const uint32_t* q2, const float* scales2,
+                             const uint8_t* zeros2) {
+  const bool dual = q2 != nullptr;
   const int gshift = log2i(group / 128);
   const int nch = K / 128;
   const int cpw = 4 * (((nch + 7) / 8 + 3) / 4);
@@ -971,15 +1032,20 @@ hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* sc
   const int rbw = (nrb + resident - 1) / resident;
   const dim3 grid((unsigned)((nrb + rbw - 1) / rbw)), block((unsigned)(64 * wv));
   const size_t lds = (size_t)nch * 16 * 8 + (size_t)2 * 16 * ngr * 4 + (size_t)2 * wv * 256 * 4 +
-                     (size_t)2 * 16 * ngr;
+                     (dual ? 256 * 4 : 0) + (size_t)2 * 16 * ngr;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
-  if (cpw == 4)
-    hipLaunchKernelGGL((gemv_w4_mx_kernel<4>), grid, block, lds, st, x, q, scales, zeros, y, M, N,
-                       K, gshift, rbw);
-  else
-    hipLaunchKernelGGL((gemv_w4_mx_kernel<8>), grid, block, lds, st, x, q, scales, zeros, y, M, N,
-                       K, gshift, rbw);
+#define AWQ_MX(CP, DU)                                                                          \
+  hipLaunchKernelGGL((gemv_w4_mx_kernel<CP, DU>), grid, block, lds, st, x, q, scales, zeros, q2, \
+                     scales2, zeros2, y, M, N, K, gshift, rbw)
+  if (cpw == 4) {
+    if (dual) AWQ_MX(4, true);
+    else AWQ_MX(4, false);
+  } else {
+    if (dual) AWQ_MX(8, true);
+    else AWQ_MX(8, false);
+  }
+#undef AWQ_MX
   return hipGetLastError();
 }
 
@@ -997,7 +1063,8 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   if (variant == 0 && M >= 2) {
-    const hipError_t e = launch_gemv_w4_mx(X, q, scales, zeros, M, N, K, group, Y, st);
+    const hipError_t e =
+        launch_gemv_w4_mx(X, q, scales, zeros, M, N, K, group, Y, st, nullptr, nullptr, nullptr);
     if (e != hipErrorNotSupported) return e;
   }
   if (variant == 0 && M == 1) {
@@ -1009,11 +1076,11 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
 #define AWQ_M1(SM, RP)                                                                          \
   do {                                                                                          \
     if (full)                                                                                   \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true>), g1, block, 0, st, x, q, scales,     \
-                         zeros, y, N, K, gshift);                                               \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, false>), g1, block, 0, st, x, q,     \
+                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);            \
     else                                                                                        \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false>), g1, block, 0, st, x, q, scales,    \
-                         zeros, y, N, K, gshift);                                               \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, false>), g1, block, 0, st, x, q,    \
+                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);            \
   } while (0)
     switch (sp) {
       case 1: AWQ_M1(1, 4); break;
@@ -1058,6 +1125,76 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((gemv_w4_kernel<kExact, 16, kGemvPF>), grid, block, lds, st, x, q, scales,
                      zeros, y, M, N, K, gshift, rbw);
+  return hipGetLastError();
+}
+
+// Fused gate/up decode at M = 1, int4: Y = fp16(silu(X Wg^T) * (X Wu^T)).
+hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float* sg,
+                                const uint8_t* zg, const uint32_t* qu, const float* su,
+                                const uint8_t* zu, int N, int K, int group, __half* Y,
+                                hipStream_t st) {
+  const int gshift = log2i(group / 128);
+  const int nch = K / 128;
+  const int sp = (nch + 15) / 16;
+  if (sp > 6) return hipErrorNotSupported;
+  const int nw = max(cu_count() * 8, (N + 63) / 64);
+  const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
+  const bool full = nch % 16 == 0;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+#define AWQ_GU(SM, RP)                                                                        \
+  do {                                                                                        \
+    if (full)                                                                                 \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, true>), g1, block, 0, st, x, qg, sg, \
+                         zg, qu, su, zu, y, N, K, gshift);                                    \
+    else                                                                                      \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, true>), g1, block, 0, st, x, qg,   \
+                         sg, zg, qu, su, zu, y, N, K, gshift);                                \
+  } while (0)
+  switch (sp) {
+    case 1: AWQ_GU(1, 4); break;
+    case 2: AWQ_GU(2, 2); break;
+    case 3: AWQ_GU(3, 2); break;
+    case 4: AWQ_GU(4, 2); break;
+    case 5: AWQ_GU(5, 2); break;
+    default: AWQ_GU(6, 2); break;
+  }
+#undef AWQ_GU
+  return hipGetLastError();
+}
+
+// Fused gate/up decode at M = 1, int3, group 128.
+hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float* sg,
+                                const uint8_t* zg, const uint32_t* qu, const float* su,
+                                const uint8_t* zu, int N, int K, int group, __half* Y,
+                                hipStream_t st) {
+  const int nch = K / 128;
+  const int sp = (nch + 15) / 16;
+  if (group != 128 || sp > 6) return hipErrorNotSupported;
+  const int wpr = words_per_row(K, 3, group);
+  const int nw = max(cu_count() * 8, (N + 63) / 64);
+  const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
+  const bool full = nch % 16 == 0;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+#define AWQ_GU3(SM, RP)                                                                       \
+  do {                                                                                        \
+    if (full)                                                                                 \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, true>), g1, block, 0, st, x, qg,    \
+                         sg, zg, qu, su, zu, y, N, K, wpr);                                   \
+    else                                                                                      \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, true>), g1, block, 0, st, x, qg,   \
+                         sg, zg, qu, su, zu, y, N, K, wpr);                                   \
+  } while (0)
+  switch (sp) {
+    case 1: AWQ_GU3(1, 4); break;
+    case 2: AWQ_GU3(2, 2); break;
+    case 3: AWQ_GU3(3, 2); break;
+    case 4: AWQ_GU3(4, 2); break;
+    case 5: AWQ_GU3(5, 2); break;
+    default: AWQ_GU3(6, 2); break;
+  }
+#undef AWQ_GU3
   return hipGetLastError();
 }
 
