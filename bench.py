@@ -218,6 +218,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # fused gated-MLP product (gate and up of the same shape), outside the
+    # timed steps: M = 1 on pairs of cold copies, then the prefill batch
+    gu_dec, gu_pre = [], []
+    pairs = [(r, r + 1) for r in range(1, R - 1, 2)] or [(0, 1)]
+    for i in range(max(4, args.steps)):
+        a, b = ev(), ev()
+        a.record(stream)
+        for r0, r1 in pairs:
+            awq.gate_up_silu(X1f, copies[(i + r0) % R], copies[(i + r1) % R], w.bits, w.group,
+                             out=Y1)
+        b.record(stream)
+        gu_dec.append((a, b, len(pairs)))
+    for i in range(2):
+        a, b = ev(), ev()
+        a.record(stream)
+        awq.gate_up_silu(Xpf, copies[i % R], copies[(i + 1) % R], w.bits, w.group, out=Yp)
+        b.record(stream)
+        gu_pre.append((a, b, 1))
+    torch.cuda.synchronize()
+
     def mean_ms(k):
         v = [a.elapsed_time(b) for a, b in rec[k]]
         if not v:
@@ -239,6 +259,9 @@ def main():
     search_flops = 2.0 * w.T * w.N * w.K * len(grid)  # the contraction Xcal D^T per alpha
 
     traffic = measured_traffic(w.name)
+    gu_dec_ms = float(np.mean([a.elapsed_time(b) / n for a, b, n in gu_dec[1:]]))
+    gu_pre_ms = float(np.mean([a.elapsed_time(b) / n for a, b, n in gu_pre[1:]]))
+    gu_dec_bytes = 2 * packed_bytes + 2 * M_dec * w.K + 2 * M_dec * w.N
 
     out = {
         "metric": "W4A16 GEMV effective HBM GB/s (% peak) at M=1; prefill GEMM TFLOP/s (% MFMA)",
@@ -271,6 +294,13 @@ def main():
             "unit": "TFLOP/s", "frac": round(pre_tfs / FP16_MFMA_PEAK_TF, 4),
             "kernel": f"prefill GEMM (M={M_pre})", "flops_per_launch": pre_flops,
             "mean_us": round(pre_ms * 1e3, 1),
+        },
+        "gate_up_silu": {
+            "what": "fp16(silu(X' Wg^T) * (X' Wu^T)), two matrices of the workload's shape",
+            "decode_M1_us": round(gu_dec_ms * 1e3, 2),
+            "decode_M1_gbs": round(gu_dec_bytes / (gu_dec_ms * 1e-3) / 1e9, 1),
+            "prefill_us": round(gu_pre_ms * 1e3, 1),
+            "prefill_tflops": round(2 * pre_flops / (gu_pre_ms * 1e-3) / 1e12, 1),
         },
         "rows": {
             "scale_search_ms": round(search_ms, 3),
