@@ -54,6 +54,16 @@ R18 the gated MLP that the fused gate/up product serves is LLaMA's:
     part of the method") but name no activation. Gate and up read the same
     normalized input, so they share one X' (one s). Evaluated here in
     float64 from the exact products.
+R20 the fold of diag(s)^-1 into the normalization that precedes the layer
+    (AWQ Explained -- "Scaling instead of mixed precision": it is done
+    offline and what ships is a modified norm) is read for RMSNorm,
+    y_k = x_k * r * gamma_k with r = (mean_k x_k^2 + eps)^-1/2: the folded
+    weight is gamma'_k = fp16(float32(gamma_k) / s_k) (the weight keeps its
+    fp16 storage, one rounding) and the norm with gamma' yields X' directly.
+    Here r and the product are exact (float64) and rounded once to fp16.
+R21 one norm carries one s, so layers that read the same normalized input
+    (q/k/v; gate/up) share s, and its search minimizes the sum of their
+    layer-output errors, summed in layer order; the first minimum wins.
 R17 zero_point=false (the AwqConfig option, AWQ Explained -- "How the scale
     is chosen", last paragraph) is the symmetric grid: delta = max|W'| /
     (2^(b-1) - 1) per group, codes rint(W' / delta) in [-(2^(b-1) - 1),
@@ -314,6 +324,48 @@ def scale_search(W: np.ndarray, xcal: np.ndarray, alpha_grid, bits: int, group: 
     best = 0
     for i, a in enumerate(alpha_grid):
         losses[i] = layer_loss(xcal, W, scale_from_stats(m, a), bits, group, zero_point)
+        if losses[i] < losses[best]:
+            best = i
+    return scale_from_stats(m, alpha_grid[best]), best, losses
+
+
+# ----------------------------------------------------------------------------
+# the scale folded into the preceding RMSNorm, and the joint search of
+# layers that share it
+# ----------------------------------------------------------------------------
+
+
+def fold_norm_weight(gamma: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """gamma' = fp16(float32(gamma) / s): the RMSNorm weight with diag(s)^-1
+    folded in (R20), one float32 division and one rounding to fp16."""
+    g = np.asarray(gamma, dtype=np.float16).astype(np.float32)
+    return (g / np.asarray(s, dtype=np.float32)).astype(np.float32).astype(np.float16)
+
+
+def rmsnorm(X: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """fp16(x_k * r * gamma_k), r = (mean_k x_k^2 + eps)^-1/2, per row of the
+    fp16 X [M, K] with the fp16 weight gamma [K]; r and the product in
+    float64, one rounding to fp16 (R20)."""
+    x = np.asarray(X, dtype=np.float16).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + float(eps))
+    g = np.asarray(gamma, dtype=np.float16).astype(np.float64)
+    return (x * r * g[None, :]).astype(np.float16)
+
+
+def joint_scale_search(Ws, xcal: np.ndarray, alpha_grid, bits: int, group: int,
+                       zero_point: bool = True):
+    """One s for the layers Ws (each [N_l, K]) that read the same input
+    (R21): losses[i] = sum over layers, in order, of layer_loss at s_i; the
+    first minimum wins. Returns (s float32 [K], best index, losses)."""
+    m = act_stats(xcal)
+    losses = np.empty(len(alpha_grid), dtype=np.float64)
+    best = 0
+    for i, a in enumerate(alpha_grid):
+        s = scale_from_stats(m, a)
+        total = 0.0
+        for W in Ws:
+            total += layer_loss(xcal, W, s, bits, group, zero_point)
+        losses[i] = total
         if losses[i] < losses[best]:
             best = i
     return scale_from_stats(m, alpha_grid[best]), best, losses

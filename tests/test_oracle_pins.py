@@ -568,3 +568,74 @@ def test_gate_up_silu_exact_products():
             g = float(exact(qg, sg, zg, n, m))
             u = float(exact(qu, su, zu, n, m))
             assert Y[m, n] == pytest.approx(g / (1.0 + math.exp(-g)) * u, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm with the folded scale (R20) and the joint search (R21)
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_against_library():
+    """torch's functional rms_norm (a library routine) in float64, rounded
+    once to fp16, agrees bit for bit except where the float64 value sits
+    within rounding of an fp16 midpoint (then one ulp)."""
+    torch = pytest.importorskip("torch")
+    X = datagen.random_f16((7, 4096), 1.0, seed=81)
+    gamma = (1.0 + datagen.random_f16((4096,), 0.1, seed=82)).astype(np.float16)
+    eps = 1e-6
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(X.astype(np.float64)), (4096,),
+                                       torch.from_numpy(gamma.astype(np.float64)), eps)
+    ref16 = ref.numpy().astype(np.float16)
+    got = O.rmsnorm(X, gamma, eps)
+    diff = np.abs(got.astype(np.float32) - ref16.astype(np.float32))
+    ulp = np.abs(np.spacing(ref16)).astype(np.float32)
+    assert np.all(diff <= ulp)
+    assert np.mean(got == ref16) > 0.999
+
+
+def test_rmsnorm_closed_forms():
+    """A row of equal values c normalizes to sign(c) * gamma / sqrt(1 + eps/c^2);
+    scaling a row by 2^j leaves the output unchanged when eps = 0."""
+    K = 256
+    gamma = np.full(K, 0.5, np.float16)
+    X = np.stack([np.full(K, 3.0), np.full(K, -0.25)]).astype(np.float16)
+    Y = O.rmsnorm(X, gamma, 0.0)
+    assert np.all(Y[0] == np.float16(0.5)) and np.all(Y[1] == np.float16(-0.5))
+    Z = datagen.random_f16((3, K), 1.0, seed=83)
+    g = datagen.random_f16((K,), 1.0, seed=84)
+    assert np.array_equal(O.rmsnorm(Z, g, 0.0), O.rmsnorm((Z * np.float16(4)).astype(np.float16), g, 0.0))
+    assert O.rmsnorm(np.zeros((1, K), np.float16), g, 1e-6).max() == 0
+
+
+def test_folded_norm_equals_norm_then_division():
+    """norm with gamma / s == (norm with gamma) / s, up to the fp16 roundings
+    of gamma' and of the output (each 2^-11 relative)."""
+    K = 1024
+    X = datagen.random_f16((5, K), 1.0, seed=85)
+    gamma = (1.0 + datagen.random_f16((K,), 0.1, seed=86)).astype(np.float16)
+    s = datagen.random_f32_positive(K, 0.2, 9.0, seed=87)
+    gp = O.fold_norm_weight(gamma, s)
+    assert gp.dtype == np.float16
+    assert np.array_equal(gp, (gamma.astype(np.float32) / s).astype(np.float16))
+    a = O.rmsnorm(X, gp, 1e-6).astype(np.float64)
+    x = X.astype(np.float64)
+    b = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6) * gamma.astype(np.float64) / s
+    assert np.all(np.abs(a - b) <= (2.0 ** -10 + 2.0 ** -20) * np.abs(b) + 2.0 ** -24)
+    # s = 1 folds to gamma itself
+    assert np.array_equal(O.fold_norm_weight(gamma, np.ones(K, np.float32)), gamma)
+
+
+def test_joint_search_equals_search_on_stacked_rows():
+    """The loss is a sum over output channels and every group lies in one
+    row, so the joint search over [W1, W2] is the plain search over the
+    stacked matrix; with one layer it is the plain search."""
+    W1, Xc, _ = datagen.small_layer(256, 48, 40, 3, 40.0, seed=88)
+    W2 = datagen.random_f16((32, 256), 0.02, seed=89)
+    grid = datagen.alpha_grid(10)
+    for zp in (True, False):
+        sj, bj, lj = O.joint_scale_search([W1, W2], Xc, grid, 4, 128, zp)
+        ss, bs, ls = O.scale_search(np.vstack([W1, W2]), Xc, grid, 4, 128, zp)
+        assert np.allclose(lj, ls, rtol=1e-12, atol=0)
+        assert bj == bs and np.array_equal(sj, ss)
+        s1, b1, l1 = O.joint_scale_search([W1], Xc, grid, 3, 128, zp)
+        s0, b0, l0 = O.scale_search(W1, Xc, grid, 3, 128, zp)
+        assert np.array_equal(l1, l0) and b1 == b0 and np.array_equal(s1, s0)
