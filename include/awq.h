@@ -215,6 +215,45 @@ awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N,
                                int zero_point, float* s_out, double* loss_out, int* best_index,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Layers that read the same normalized input (q/k/v projections; gate and
+ * up) can carry only one s, since it is folded into the one norm in front of
+ * them (AWQ Explained -- "Scaling instead of mixed precision"). Their search
+ * adds the layers' losses per candidate, in layer order, and picks the first
+ * minimum of the sum:
+ *   loss[i] = sum_l || Xcalib D_l,i^T ||_F^2,  D_l,i as in awq_scale_search.
+ * W: host array of n_layers (1..16) dev pointers to fp16 [N[l], K] matrices;
+ * N: host int [n_layers]; the other arguments, the accuracy and the
+ * synchronization are those of awq_scale_search_ex (one layer gives exactly
+ * awq_scale_search_ex). workspace: dev, at least
+ * awq_scale_search_joint_workspace_bytes(...) bytes (0 if the sizes are
+ * invalid). */
+size_t awq_scale_search_joint_workspace_bytes(const int* N, int n_layers, int K, int T,
+                                              int n_alpha, int bits, int group);
+awq_status awq_scale_search_joint(const uint16_t* const* W, const int* N, int n_layers,
+                                  const uint16_t* Xcalib, int K, int T, const float* alpha_grid,
+                                  int n_alpha, int bits, int group, int zero_point, float* s_out,
+                                  double* loss_out, int* best_index, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* The fold of diag(s)^-1 into the RMSNorm in front of the layer (AWQ
+ * Explained -- "Scaling instead of mixed precision": done offline; what
+ * ships is a slightly modified norm):
+ *   gamma_out[k] = fp16(float32(gamma[k]) / s[k])   (round-to-nearest-even)
+ * gamma, gamma_out: dev fp16 [K] (may be the same buffer); s: dev float32
+ * [K]. Asynchronous on `stream`. */
+awq_status awq_fold_norm_weight(const uint16_t* gamma, const float* s, int K, uint16_t* gamma_out,
+                                void* stream);
+
+/* RMSNorm, which with the folded weight yields X' = norm(X) diag(s)^-1 for
+ * the W4A16 product directly:
+ *   r = 1 / sqrt(sum_k X[m, k]^2 / K + eps),  Y[m, k] = fp16(X[m, k] r gamma[k])
+ * in float32 (r from a fixed-order tree sum), one rounding to fp16; within
+ * one fp16 ulp of the exact value. X, Y: dev fp16 [M, K] (may be the same
+ * buffer); gamma: dev fp16 [K]; eps >= 0. K must be a multiple of 8 and at
+ * most 16384 (else AWQ_ERR_UNSUPPORTED). Asynchronous on `stream`. */
+awq_status awq_rmsnorm(const uint16_t* X, const uint16_t* gamma, int M, int K, float eps,
+                       uint16_t* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -175,3 +175,44 @@ def test_gate_up_validation():
     import torch
     if not torch.cuda.is_available():
         assert call() == E.AWQ_ERR_NO_DEVICE
+
+
+def test_norm_and_joint_validation():
+    h = awq.lib()
+    E = _lib
+    assert h.awq_fold_norm_weight(NULL, P, 256, P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_fold_norm_weight(P, P, 0, P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_fold_norm_weight(P, MIS, 256, P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    f = ctypes.c_float
+    assert h.awq_rmsnorm(P, P, 4, 256, f(1e-6), NULL, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_rmsnorm(P, P, 0, 256, f(1e-6), P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_rmsnorm(P, P, 4, 256, f(-1.0), P2, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_rmsnorm(P, P, 4, 250, f(1e-6), P2, NULL) == E.AWQ_ERR_UNSUPPORTED
+    assert h.awq_rmsnorm(P, P, 4, 16392, f(1e-6), P2, NULL) == E.AWQ_ERR_UNSUPPORTED
+    Ns = (ctypes.c_int * 3)(64, 64, 32)
+    Ws = (ctypes.c_void_p * 3)(0x10000, 0x20000, 0x30000)
+    a = np.arange(20, dtype=np.float32) / 20
+    ap = a.ctypes.data_as(ctypes.c_void_p)
+    need = h.awq_scale_search_joint_workspace_bytes(Ns, 3, 256, 32, 20, 4, 128)
+    assert need > h.awq_scale_search_workspace_bytes(64, 256, 32, 20, 4, 128)
+    one = (ctypes.c_int * 1)(64)
+    assert h.awq_scale_search_joint_workspace_bytes(one, 1, 256, 32, 20, 4, 128) == \
+        h.awq_scale_search_workspace_bytes(64, 256, 32, 20, 4, 128)
+    assert h.awq_scale_search_joint_workspace_bytes(Ns, 0, 256, 32, 20, 4, 128) == 0
+    assert h.awq_scale_search_joint_workspace_bytes(Ns, 17, 256, 32, 20, 4, 128) == 0
+    best = ctypes.c_int(0)
+
+    def call(W=Ws, n=3, ws=P, nbytes=need, zp=1):
+        return h.awq_scale_search_joint(W, Ns, n, P, 256, 32, ap, 20, 4, 128, zp, P2, NULL,
+                                        ctypes.byref(best), ws, nbytes, NULL)
+    assert call(n=0) == E.AWQ_ERR_INVALID_ARG
+    assert call(zp=3) == E.AWQ_ERR_INVALID_ARG
+    bad = (ctypes.c_void_p * 3)(0x10000, None, 0x30000)
+    assert call(W=bad) == E.AWQ_ERR_INVALID_ARG
+    assert call(ws=NULL) == E.AWQ_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == E.AWQ_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == E.AWQ_ERR_NO_DEVICE
+        assert h.awq_rmsnorm(P, P, 4, 256, f(1e-6), P2, NULL) == E.AWQ_ERR_NO_DEVICE
+        assert h.awq_fold_norm_weight(P, P, 256, P2, NULL) == E.AWQ_ERR_NO_DEVICE

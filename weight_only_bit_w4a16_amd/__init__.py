@@ -21,6 +21,7 @@ from ._lib import AwqError, check, lib  # noqa: F401
 __all__ = [
     "AwqError", "lib", "packed_words_per_row", "act_stats", "scale_candidates",
     "quantize_pack", "fold_inv_scale", "w4a16_matmul", "gate_up_silu", "scale_search",
+    "scale_search_joint", "scale_search_joint_workspace_bytes", "fold_norm_weight", "rmsnorm",
     "scale_search_workspace_bytes", "KERNEL_AUTO", "KERNEL_DECODE", "KERNEL_DECODE_EXACT",
     "KERNEL_PREFILL",
 ]
@@ -218,3 +219,77 @@ def scale_search(W, xcal, alpha_grid=None, bits: int = 4, group: int = 128, work
         ctypes.byref(best), _ptr(workspace), workspace.numel(), _stream(stream)),
         "awq_scale_search_ex")
     return s, int(best.value), losses
+
+
+def scale_search_joint_workspace_bytes(Ns, K, T, n_alpha, bits=4, group=128) -> int:
+    arr = (ctypes.c_int * len(Ns))(*[int(n) for n in Ns])
+    return int(lib().awq_scale_search_joint_workspace_bytes(arr, len(Ns), K, T, n_alpha, bits,
+                                                            group))
+
+
+def scale_search_joint(Ws, xcal, alpha_grid=None, bits: int = 4, group: int = 128,
+                       workspace=None, stream=None, zero_point: bool = True):
+    """One s for the layers Ws (each [N_l, K], fp16) that read the same
+    input: the layers' losses are added per candidate before the argmin.
+
+    Returns (s float32 [K] on the device, best index, summed losses float64
+    numpy). Synchronizes the stream.
+    """
+    torch = _torch()
+    Ws = list(Ws)
+    if not Ws:
+        raise ValueError("Ws must hold at least one matrix")
+    _need(xcal, "xcal", torch.float16, 2)
+    T, K = xcal.shape
+    for i, W in enumerate(Ws):
+        _need(W, f"Ws[{i}]", torch.float16, 2)
+        if W.shape[1] != K:
+            raise ValueError("every W must be [N_l, K] with the K of xcal")
+    if alpha_grid is None:
+        alpha_grid = (np.arange(20, dtype=np.float64) / 20).astype(np.float32)
+    a = np.ascontiguousarray(np.asarray(alpha_grid, dtype=np.float32))
+    Ns = [int(W.shape[0]) for W in Ws]
+    need = scale_search_joint_workspace_bytes(Ns, K, T, len(a), bits, group)
+    if need == 0:
+        raise ValueError("unsupported scale_search_joint sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xcal.device)
+    s = torch.empty(K, dtype=torch.float32, device=xcal.device)
+    losses = np.zeros(len(a), dtype=np.float64)
+    best = ctypes.c_int(-1)
+    ptrs = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
+    narr = (ctypes.c_int * len(Ws))(*Ns)
+    check(lib().awq_scale_search_joint(
+        ptrs, narr, len(Ws), _ptr(xcal), K, T, a.ctypes.data_as(ctypes.c_void_p), len(a), bits,
+        group, int(bool(zero_point)), _ptr(s), losses.ctypes.data_as(ctypes.c_void_p),
+        ctypes.byref(best), _ptr(workspace), workspace.numel(), _stream(stream)),
+        "awq_scale_search_joint")
+    return s, int(best.value), losses
+
+
+def fold_norm_weight(gamma, s, out=None, stream=None):
+    """gamma' = fp16(float32(gamma) / s): the RMSNorm weight with diag(s)^-1
+    folded in (fp16 [K])."""
+    torch = _torch()
+    _need(gamma, "gamma", torch.float16, 1)
+    _need(s, "s", torch.float32, 1)
+    if s.numel() != gamma.numel():
+        raise ValueError("gamma and s must have K entries each")
+    y = torch.empty_like(gamma) if out is None else out
+    check(lib().awq_fold_norm_weight(_ptr(gamma), _ptr(s), gamma.numel(), _ptr(y),
+                                     _stream(stream)), "awq_fold_norm_weight")
+    return y
+
+
+def rmsnorm(X, gamma, eps: float = 1e-6, out=None, stream=None):
+    """fp16(X r gamma) with r = (mean_k X^2 + eps)^-1/2 per row (fp16 [M, K])."""
+    torch = _torch()
+    _need(X, "X", torch.float16, 2)
+    _need(gamma, "gamma", torch.float16, 1)
+    M, K = X.shape
+    if gamma.numel() != K:
+        raise ValueError("gamma must have K entries")
+    y = torch.empty_like(X) if out is None else out
+    check(lib().awq_rmsnorm(_ptr(X), _ptr(gamma), M, K, ctypes.c_float(eps), _ptr(y),
+                            _stream(stream)), "awq_rmsnorm")
+    return y

@@ -39,6 +39,11 @@ SIGNATURES = {
     "awq_scale_search": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
     "awq_scale_search_ex": (_i, [_p, _p, _i, _i, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _sz,
                                  _p]),
+    "awq_scale_search_joint_workspace_bytes": (_sz, [_p, _i, _i, _i, _i, _i, _i]),
+    "awq_scale_search_joint": (_i, [_p, _p, _i, _p, _i, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p,
+                                    _sz, _p]),
+    "awq_fold_norm_weight": (_i, [_p, _p, _i, _p, _p]),
+    "awq_rmsnorm": (_i, [_p, _p, _i, _i, ctypes.c_float, _p, _p]),
 }
 
 _LIB = None

@@ -12,6 +12,9 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// layers of one joint search (q, k, v or gate, up, and room to spare)
+constexpr int kMaxLayers = 16;
+
 // normalise the group argument (-1 means the whole row); 0 if unsupported
 int resolve_group(int K, int group) {
   if (group == -1) group = K;
@@ -230,22 +233,42 @@ size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bi
   return awq::search_workspace_bytes(N, K, T, n_alpha, bits, g);
 }
 
-awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
-                               const float* alpha_grid, int n_alpha, int bits, int group,
-                               int zero_point, float* s_out, double* loss_out, int* best_index,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-  if (!W || !Xcalib || !alpha_grid || !s_out) return AWQ_ERR_INVALID_ARG;
-  if (zero_point != 0 && zero_point != 1) return AWQ_ERR_INVALID_ARG;
-  if (N <= 0 || K <= 0 || T <= 0 || n_alpha <= 0) return AWQ_ERR_INVALID_ARG;
+static awq_status awq_scale_search_joint_workspace_bytes_impl(const int* N, int n_layers, int K,
+                                                             int T, int n_alpha, int bits,
+                                                             int group, size_t* out) {
+  *out = 0;
+  if (!N || n_layers <= 0 || n_layers > kMaxLayers) return AWQ_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l)
+    if (N[l] <= 0) return AWQ_ERR_INVALID_ARG;
+  if (T <= 0 || n_alpha <= 0) return AWQ_ERR_INVALID_ARG;
   if (T >= 8192) return AWQ_ERR_UNSUPPORTED;
-  if (!aligned16(W) || !aligned16(Xcalib) || !aligned16(s_out)) return AWQ_ERR_INVALID_ARG;
+  int g = 0;
+  const awq_status st = check_group(K, bits, group, &g);
+  if (st != AWQ_OK) return st;
+  *out = awq::search_workspace_bytes_joint(N, n_layers, K, T, n_alpha);
+  return AWQ_OK;
+}
+
+awq_status awq_scale_search_joint(const uint16_t* const* W, const int* N, int n_layers,
+                                  const uint16_t* Xcalib, int K, int T, const float* alpha_grid,
+                                  int n_alpha, int bits, int group, int zero_point, float* s_out,
+                                  double* loss_out, int* best_index, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!W || !N || !Xcalib || !alpha_grid || !s_out) return AWQ_ERR_INVALID_ARG;
+  if (n_layers <= 0 || n_layers > kMaxLayers || K <= 0 || T <= 0 || n_alpha <= 0)
+    return AWQ_ERR_INVALID_ARG;
+  if (zero_point != 0 && zero_point != 1) return AWQ_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l)
+    if (!W[l] || N[l] <= 0 || !aligned16(W[l])) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(Xcalib) || !aligned16(s_out)) return AWQ_ERR_INVALID_ARG;
   for (int i = 0; i < n_alpha; ++i)
     if (!(alpha_grid[i] >= 0.0f && alpha_grid[i] <= 1.0f)) return AWQ_ERR_INVALID_ARG;
-  int g = 0;
-  awq_status st = check_group(K, bits, group, &g);
+  size_t need = 0;
+  awq_status st =
+      awq_scale_search_joint_workspace_bytes_impl(N, n_layers, K, T, n_alpha, bits, group, &need);
   if (st != AWQ_OK) return st;
-  const size_t need = awq::search_workspace_bytes(N, K, T, n_alpha, bits, g);
-  if (need == 0) return AWQ_ERR_UNSUPPORTED;
+  int g = 0;
+  (void)check_group(K, bits, group, &g);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return AWQ_ERR_WORKSPACE;
   st = device_ready();
   if (st != AWQ_OK) return st;
@@ -262,14 +285,15 @@ awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N,
 
   hipError_t e = hipMemcpyAsync(alpha_dev, alpha_grid, (size_t)n_alpha * 4, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return AWQ_ERR_HIP;
-  e = awq::launch_search(reinterpret_cast<const __half*>(W), reinterpret_cast<const __half*>(Xcalib),
-                         N, K, T, alpha_dev, n_alpha, bits, g, zero_point != 0, rest, loss_dev,
-                         best_dev, s_out, s);
+  const __half* wl[kMaxLayers];
+  for (int l = 0; l < n_layers; ++l) wl[l] = reinterpret_cast<const __half*>(W[l]);
+  e = awq::launch_search_joint(wl, N, n_layers, reinterpret_cast<const __half*>(Xcalib), K, T,
+                               alpha_dev, n_alpha, bits, g, zero_point != 0, rest, loss_dev,
+                               best_dev, s_out, s);
   if (e != hipSuccess) return from_hip(e);
-  double* host_loss = loss_out;
   int host_best = 0;
-  if (host_loss) {
-    e = hipMemcpyAsync(host_loss, loss_dev, (size_t)n_alpha * 8, hipMemcpyDeviceToHost, s);
+  if (loss_out) {
+    e = hipMemcpyAsync(loss_out, loss_dev, (size_t)n_alpha * 8, hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return AWQ_ERR_HIP;
   }
   e = hipMemcpyAsync(&host_best, best_dev, sizeof(int), hipMemcpyDeviceToHost, s);
@@ -278,6 +302,51 @@ awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N,
   if (e != hipSuccess) return AWQ_ERR_HIP;
   if (best_index) *best_index = host_best;
   return AWQ_OK;
+}
+
+size_t awq_scale_search_joint_workspace_bytes(const int* N, int n_layers, int K, int T,
+                                              int n_alpha, int bits, int group) {
+  size_t need = 0;
+  (void)awq_scale_search_joint_workspace_bytes_impl(N, n_layers, K, T, n_alpha, bits, group,
+                                                    &need);
+  return need;
+}
+
+awq_status awq_scale_search_ex(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,
+                               const float* alpha_grid, int n_alpha, int bits, int group,
+                               int zero_point, float* s_out, double* loss_out, int* best_index,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W) return AWQ_ERR_INVALID_ARG;
+  const uint16_t* wl[1] = {W};
+  return awq_scale_search_joint(wl, &N, 1, Xcalib, K, T, alpha_grid, n_alpha, bits, group,
+                                zero_point, s_out, loss_out, best_index, workspace,
+                                workspace_bytes, stream);
+}
+
+awq_status awq_fold_norm_weight(const uint16_t* gamma, const float* s, int K, uint16_t* gamma_out,
+                                void* stream) {
+  if (!gamma || !s || !gamma_out) return AWQ_ERR_INVALID_ARG;
+  if (K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(gamma) || !aligned16(s) || !aligned16(gamma_out)) return AWQ_ERR_INVALID_ARG;
+  const awq_status st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_fold_norm_weight(reinterpret_cast<const __half*>(gamma), s, K,
+                                               reinterpret_cast<__half*>(gamma_out),
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_rmsnorm(const uint16_t* X, const uint16_t* gamma, int M, int K, float eps,
+                       uint16_t* Y, void* stream) {
+  if (!X || !gamma || !Y) return AWQ_ERR_INVALID_ARG;
+  if (M <= 0 || K <= 0 || !(eps >= 0.0f)) return AWQ_ERR_INVALID_ARG;
+  if (K % 8 != 0 || K > awq::kRmsNormMaxK) return AWQ_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(gamma) || !aligned16(Y)) return AWQ_ERR_INVALID_ARG;
+  const awq_status st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_rmsnorm(reinterpret_cast<const __half*>(X),
+                                      reinterpret_cast<const __half*>(gamma), M, K, eps,
+                                      reinterpret_cast<__half*>(Y),
+                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 awq_status awq_scale_search(const uint16_t* W, const uint16_t* Xcalib, int N, int K, int T,

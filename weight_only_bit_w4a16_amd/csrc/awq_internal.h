@@ -73,4 +73,18 @@ hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
                          bool zero_point, void* ws, double* loss_dev, int* best_dev, float* s_out,
                          hipStream_t st);
 
+// layers sharing one input: losses added per candidate in layer order
+size_t search_workspace_bytes_joint(const int* N, int n_layers, int K, int T, int n_alpha);
+hipError_t launch_search_joint(const __half* const* W, const int* N, int n_layers, const __half* Xc,
+                               int K, int T, const float* alpha_dev, int n_alpha, int bits,
+                               int group, bool zero_point, void* ws, double* loss_dev,
+                               int* best_dev, float* s_out, hipStream_t st);
+
+// RMSNorm with the scale folded into its weight
+hipError_t launch_fold_norm_weight(const __half* gamma, const float* s, int K, __half* out,
+                                   hipStream_t st);
+constexpr int kRmsNormMaxK = 16384;
+hipError_t launch_rmsnorm(const __half* X, const __half* gamma, int M, int K, float eps, __half* Y,
+                          hipStream_t st);
+
 }  // namespace awq

@@ -16,8 +16,10 @@
 //    the outlier-heavy layers, so below about 1.2e-5 at 2^18.
 //  * hi/lo (small T N): Xcal as given (exact fp16) against D split into an
 //    fp16 hi and lo part, contracted as one product over 2K.
-// Then best = first index of the minimum loss and s_out = s_best. Everything
-// runs on the device; the host only enqueues.
+// Then best = first index of the minimum loss and s_out = s_best. Layers
+// that share one input (and so one s) are searched jointly: their losses are
+// added per candidate, in layer order, before the argmin. Everything runs on
+// the device; the host only enqueues.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -138,56 +140,49 @@ __global__ void argmin_copy_kernel(const double* __restrict__ loss, int n_alpha,
     s_out[k] = s_all[(size_t)b * K + k];
 }
 
+// loss[a] = sum over layers l, in order, of lloss[l][a]
+__global__ void sum_layers_kernel(const double* __restrict__ lloss, int n_layers, int n_alpha,
+                                  double* __restrict__ loss) {
+  const int a = blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= n_alpha) return;
+  double v = 0.0;
+  for (int l = 0; l < n_layers; ++l) v += lloss[(size_t)l * n_alpha + a];
+  loss[a] = v;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// workspace: statistic, candidate scales, Xcal / s, the error term of the
+// largest layer, the tile partials of the largest layer, per-layer losses
 struct Layout {
-  size_t m, s_all, xs, e, partial, total;
+  size_t m, s_all, xs, e, partial, lloss, total;
 };
 
-Layout layout(int N, int K, int T, int n_alpha) {
+Layout layout(int maxN, int K, int T, int n_alpha, unsigned max_tiles, int n_layers) {
   Layout L;
   L.m = 0;
   L.s_all = L.m + align256((size_t)K * 8);
   L.xs = L.s_all + align256((size_t)n_alpha * K * 4);
   L.e = L.xs + align256((size_t)T * K * 2);
-  L.partial = L.e + align256((size_t)N * K * 4);  // E [N, K] or hi/lo D [N, 2K]
-  L.total = L.partial + align256((size_t)n_alpha * sqnorm_abt_tiles(T, N) * 8);
+  L.partial = L.e + align256((size_t)maxN * K * 4);  // E [N, K] or hi/lo D [N, 2K]
+  L.lloss = L.partial + align256((size_t)n_alpha * max_tiles * 8);
+  L.total = L.lloss + (n_layers > 1 ? align256((size_t)n_layers * n_alpha * 8) : 0);
   return L;
 }
 
-}  // namespace
-
-size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group) {
-  (void)bits;
-  (void)group;
-  // + the head the API layer keeps for the grid, the losses and the index
-  return layout(N, K, T, n_alpha).total + align256((size_t)n_alpha * 4) +
-         align256((size_t)n_alpha * 8) + 256;
-}
-
-hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
-                         const float* alpha_dev, int n_alpha, int bits, int group,
-                         bool zero_point, void* ws, double* loss_dev, int* best_dev, float* s_out,
-                         hipStream_t st) {
-  const Layout L = layout(N, K, T, n_alpha);
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  double* m = reinterpret_cast<double*>(base + L.m);
-  float* s_all = reinterpret_cast<float*>(base + L.s_all);
-  uint16_t* Xs = reinterpret_cast<uint16_t*>(base + L.xs);
-  uint16_t* E = reinterpret_cast<uint16_t*>(base + L.e);
-  double* partial = reinterpret_cast<double*>(base + L.partial);
+// the losses of every candidate scale for one layer W [N, K] -> loss[n_alpha]
+hipError_t layer_losses(const __half* W, const __half* Xc, int N, int K, int T,
+                        const float* s_all, int n_alpha, int bits, int group, bool zero_point,
+                        uint16_t* Xs, uint16_t* E, double* partial, double* loss,
+                        hipStream_t st) {
   const unsigned tiles = sqnorm_abt_tiles(T, N);
   const uint16_t* w = reinterpret_cast<const uint16_t*>(W);
-
-  hipError_t e = launch_act_stats(Xc, T, K, m, st);
-  if (e != hipSuccess) return e;
-  e = launch_scale_candidates(m, K, alpha_dev, n_alpha, s_all, st);
-  if (e != hipSuccess) return e;
   const int gy = (N + 3) / 4 < 65535 ? (N + 3) / 4 : 65535;  // about 4 rows per thread
   const dim3 fgrid((unsigned)((K / 8 + 255) / 256), (unsigned)gy);
   // the scaled single product's rounding effect on the loss shrinks as
   // 1/sqrt(T N); from 2^18 on it stays below about 1.2e-5
   const bool scaled = (long long)T * N >= (1LL << 18);
+  hipError_t e;
   for (int a = 0; a < n_alpha; ++a) {
     const float* s = s_all + (size_t)a * K;
 #define AWQ_FQ(B, TP, SC, SY)                                                                  \
@@ -228,12 +223,77 @@ hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(reduce_loss_kernel, dim3(n_alpha), dim3(256), 0, st, partial, (int)tiles,
-                     scaled ? 1.0 / 65536.0 : 1.0, loss_dev);
-  e = hipGetLastError();
+                     scaled ? 1.0 / 65536.0 : 1.0, loss);
+  return hipGetLastError();
+}
+
+unsigned max_tiles_of(const int* N, int n_layers, int T) {
+  unsigned t = 0;
+  for (int l = 0; l < n_layers; ++l) t = t > sqnorm_abt_tiles(T, N[l]) ? t : sqnorm_abt_tiles(T, N[l]);
+  return t;
+}
+
+int max_of(const int* N, int n_layers) {
+  int v = 0;
+  for (int l = 0; l < n_layers; ++l) v = v > N[l] ? v : N[l];
+  return v;
+}
+
+}  // namespace
+
+size_t search_workspace_bytes_joint(const int* N, int n_layers, int K, int T, int n_alpha) {
+  const Layout L =
+      layout(max_of(N, n_layers), K, T, n_alpha, max_tiles_of(N, n_layers, T), n_layers);
+  // + the head the API layer keeps for the grid, the losses and the index
+  return L.total + align256((size_t)n_alpha * 4) + align256((size_t)n_alpha * 8) + 256;
+}
+
+size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group) {
+  (void)bits;
+  (void)group;
+  return search_workspace_bytes_joint(&N, 1, K, T, n_alpha);
+}
+
+hipError_t launch_search_joint(const __half* const* W, const int* N, int n_layers, const __half* Xc,
+                               int K, int T, const float* alpha_dev, int n_alpha, int bits,
+                               int group, bool zero_point, void* ws, double* loss_dev,
+                               int* best_dev, float* s_out, hipStream_t st) {
+  const Layout L =
+      layout(max_of(N, n_layers), K, T, n_alpha, max_tiles_of(N, n_layers, T), n_layers);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  double* m = reinterpret_cast<double*>(base + L.m);
+  float* s_all = reinterpret_cast<float*>(base + L.s_all);
+  uint16_t* Xs = reinterpret_cast<uint16_t*>(base + L.xs);
+  uint16_t* E = reinterpret_cast<uint16_t*>(base + L.e);
+  double* partial = reinterpret_cast<double*>(base + L.partial);
+  double* lloss = n_layers > 1 ? reinterpret_cast<double*>(base + L.lloss) : loss_dev;
+
+  hipError_t e = launch_act_stats(Xc, T, K, m, st);
   if (e != hipSuccess) return e;
+  e = launch_scale_candidates(m, K, alpha_dev, n_alpha, s_all, st);
+  if (e != hipSuccess) return e;
+  for (int l = 0; l < n_layers; ++l) {
+    e = layer_losses(W[l], Xc, N[l], K, T, s_all, n_alpha, bits, group, zero_point, Xs, E, partial,
+                     lloss + (size_t)l * n_alpha, st);
+    if (e != hipSuccess) return e;
+  }
+  if (n_layers > 1) {
+    hipLaunchKernelGGL(sum_layers_kernel, dim3((n_alpha + 63) / 64), dim3(64), 0, st, lloss,
+                       n_layers, n_alpha, loss_dev);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(argmin_copy_kernel, dim3((K + 255) / 256), dim3(256), 0, st, loss_dev,
                      n_alpha, s_all, K, best_dev, s_out);
   return hipGetLastError();
+}
+
+hipError_t launch_search(const __half* W, const __half* Xc, int N, int K, int T,
+                         const float* alpha_dev, int n_alpha, int bits, int group,
+                         bool zero_point, void* ws, double* loss_dev, int* best_dev, float* s_out,
+                         hipStream_t st) {
+  return launch_search_joint(&W, &N, 1, Xc, K, T, alpha_dev, n_alpha, bits, group, zero_point, ws,
+                             loss_dev, best_dev, s_out, st);
 }
 
 }  // namespace awq
