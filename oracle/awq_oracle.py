@@ -46,7 +46,7 @@ R6  round-half-to-even everywhere; an all-zero group gets delta = 1, z = 0.
 R7  the layer-output error is the squared Frobenius norm over calibration
     tokens and output channels, evaluated in exact (float64) arithmetic with
     the original fp16 W; the first minimum over the grid wins.
-R9  packing: see ``pack``.
+R9  packing: see ``code_position``.
 R10 scales are stored as the float32 delta, zero points as uint8.
 R18 the gated MLP that the fused gate/up product serves is LLaMA's:
     Y = silu(X' Wg^T) * (X' Wu^T), silu(v) = v / (1 + e^-v); the pages credit
@@ -186,57 +186,63 @@ def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int)
 
 
 def words_per_group(bits: int, group: int) -> int:
-    """int4: 8 codes per 32-bit word; int3: 10 codes per word (bits 30-31 unused)."""
+    """int4: 8 codes per 32-bit word; int3: 10 codes per word (bits 30-31
+    unused) in blocks of 128 codes, 13 words per block (the last word holds
+    8 codes). Groups are multiples of 128 codes."""
     if bits == 4:
         assert group % 8 == 0
         return group // 8
     if bits == 3:
-        return -(-group // 10)
+        assert group % 128 == 0
+        return 13 * (group // 128)
     raise ValueError("bits must be 3 or 4")
 
 
 def words_per_row(K: int, bits: int, group: int) -> int:
-    """Groups are stored back to back, each starting on a word boundary; the
-    row is padded with zero words to a multiple of 4 words (16 bytes)."""
+    """Groups are stored back to back; the row is padded with zero words to
+    a multiple of 4 words (16 bytes)."""
     assert K % group == 0
     w = (K // group) * words_per_group(bits, group)
     return -(-w // 4) * 4
 
 
-def pack(q: np.ndarray, bits: int, group: int) -> np.ndarray:
-    """Pack codes q [N, K] into uint32 [N, words_per_row].
+def code_position(k, bits: int):
+    """(word, bit offset) of the code at position k of a row (R9).
 
-    Inside group g of row n, the code at position j (k = g*group + j) sits in
-    word g*words_per_group + j // c at bits [b*(j % c), b*(j % c) + b), with
-    c = 8 for int4 and c = 10 for int3. Unused slots, the two top bits of an
-    int3 word and the row padding are zero.
+    int4: word k // 8, bits 4 (k % 8). int3: the row is cut into blocks of
+    128 codes, each starting on a word boundary and taking 13 words; inside
+    a block the code at j = k % 128 sits in word j // 10 at bits 3 (j % 10).
+    The layout does not depend on the group size (groups are whole blocks).
     """
+    k = np.asarray(k)
+    if bits == 4:
+        return k // 8, 4 * (k % 8)
+    j = k % 128
+    return 13 * (k // 128) + j // 10, 3 * (j % 10)
+
+
+def pack(q: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Pack codes q [N, K] into uint32 [N, words_per_row] at the positions
+    of ``code_position``. Unused slots, the two top bits of an int3 word and
+    the row padding are zero."""
     N, K = q.shape
-    cpw = 8 if bits == 4 else 10
-    wpg = words_per_group(bits, group)
-    ng = K // group
     out = np.zeros((N, words_per_row(K, bits, group)), dtype=np.uint64)
-    qg = q.reshape(N, ng, group).astype(np.uint64)
-    for j in range(group):
-        word = j // cpw
-        shift = np.uint64(bits * (j % cpw))
-        cols = np.arange(ng) * wpg + word
-        out[:, cols] |= qg[:, :, j] << shift
+    word, shift = code_position(np.arange(K), bits)
+    qq = q.astype(np.uint64)
+    for k in range(K):
+        out[:, word[k]] |= qq[:, k] << np.uint64(shift[k])
     return out.astype(np.uint32)
 
 
 def unpack(qpacked: np.ndarray, bits: int, group: int, K: int) -> np.ndarray:
     N = qpacked.shape[0]
-    cpw = 8 if bits == 4 else 10
-    wpg = words_per_group(bits, group)
-    ng = K // group
     mask = np.uint64((1 << bits) - 1)
     w = qpacked.astype(np.uint64)
-    q = np.empty((N, ng, group), dtype=np.int64)
-    for j in range(group):
-        cols = np.arange(ng) * wpg + j // cpw
-        q[:, :, j] = ((w[:, cols] >> np.uint64(bits * (j % cpw))) & mask).astype(np.int64)
-    return q.reshape(N, K)
+    word, shift = code_position(np.arange(K), bits)
+    q = np.empty((N, K), dtype=np.int64)
+    for k in range(K):
+        q[:, k] = ((w[:, word[k]] >> np.uint64(shift[k])) & mask).astype(np.int64)
+    return q
 
 
 def quantize_pack(W: np.ndarray, s, bits: int, group: int, zero_point: bool = True):

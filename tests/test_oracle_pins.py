@@ -302,11 +302,13 @@ def test_step_growth_hurts_others():
 # ---------------------------------------------------------------------------
 
 def _unpack_by_hand(words, bits, group, K):
+    # int3 words come in blocks of 128 codes (13 words), whatever the group
     cpw = 8 if bits == 4 else 10
-    wpg = -(-group // cpw)
+    blk = group if bits == 4 else 128
+    wpg = -(-blk // cpw)
     codes = []
     for k in range(K):
-        g, j = divmod(k, group)
+        g, j = divmod(k, blk)
         w = int(words[g * wpg + j // cpw])
         codes.append((w >> (bits * (j % cpw))) & ((1 << bits) - 1))
     return codes
@@ -371,17 +373,31 @@ def test_pack_layout_golden():
     assert w3b.shape[1] == spec[2]["words_per_row"]
     assert np.array_equal(w3b[0, 13:26], w3[0, :13]) and np.all(w3b[0, 26:] == 0)
     assert np.all((w3b.astype(np.uint64) >> np.uint64(30)) == 0)
+    # groups are whole 128-code blocks: the layout does not depend on the group
+    w3c = O.pack(q3b, 3, 256)
+    assert w3c.shape[1] == spec[3]["words_per_row"] and np.array_equal(w3c, w3b)
+    q3d = (np.arange(384) % 8)[None, :]
+    w3d = O.pack(q3d, 3, 384)
+    assert w3d.shape[1] == spec[4]["words_per_row"]
+    for b in range(3):
+        assert np.array_equal(w3d[0, 13 * b:13 * b + 13], w3[0, :13])
+    assert w3d[0, 39] == 0
 
 
 @pytest.mark.parametrize("bits", [3, 4])
 def test_pack_roundtrip(bits):
     rng = np.random.default_rng(5)
-    for K in (128, 384, 4096, 11008):
+    for K, group in ((128, 128), (384, 128), (4096, 128), (11008, 128), (1024, 256),
+                     (2048, 512), (384, 384), (11008, 11008)):
         q = rng.integers(0, 1 << bits, size=(3, K))
-        w = O.pack(q, bits, 128)
-        assert w.dtype == np.uint32 and w.shape == (3, O.words_per_row(K, bits, 128))
-        assert np.array_equal(O.unpack(w, bits, 128, K), q)
+        w = O.pack(q, bits, group)
+        assert w.dtype == np.uint32 and w.shape == (3, O.words_per_row(K, bits, group))
+        assert np.array_equal(O.unpack(w, bits, group, K), q)
         assert w.shape[1] % 4 == 0
+        # every bit of a code shows up once, at its own position
+        word, shift = O.code_position(np.arange(K), bits)
+        assert len(set(zip(word.tolist(), shift.tolist()))) == K
+        assert word.max() < w.shape[1] and shift.max() + bits <= 30 + 2 * (bits == 4)
 
 
 def test_words_per_row_values():
