@@ -41,17 +41,21 @@
  *   - The library keeps no state between calls; calls on different streams
  *     may run concurrently as long as their output buffers do not overlap.
  *
- * Supported shapes: bits in {3, 4}; group in {128, 256, 512} (or -1,
- * meaning group = K, when K is one of those); K a multiple of group.
+ * Supported shapes: bits in {3, 4}; group in {128, 256, 512} with K a
+ * multiple of group, or group = -1 (or K): one group per output channel
+ * (the whole row, AwqConfig group_size = -1), for K a multiple of 128 up to
+ * 32768.
  *
  * Packed weight layout (Qpacked, uint32 [N, awq_packed_words_per_row]):
- *   group g of row n holds its codes along K; the code at position j of the
- *   group (k = g*group + j) sits in word g*wpg + j / c, bits
- *   [b*(j % c), b*(j % c) + b), where c = 8 codes per word for int4 and
- *   c = 10 codes per word for int3 (bits 30-31 zero), and
- *   wpg = ceil(group / c) words per group. Every group starts on a word
- *   boundary; unused slots are zero; each row is padded with zero words to a
- *   multiple of 4 words (16 bytes).
+ *   codes along K, lowest slot in the lowest bits. int4: the code at
+ *   position k of a row sits in word k / 8, bits [4 (k % 8), 4 (k % 8) + 4).
+ *   int3: the row is cut into blocks of 128 codes, each starting on a word
+ *   boundary and taking 13 words of 10 codes (bits 30-31 zero; the 13th word
+ *   holds 8 codes); code j = k % 128 of block k / 128 sits in word
+ *   13 (k / 128) + j / 10, bits [3 (j % 10), 3 (j % 10) + 3). The layout does
+ *   not depend on the group (groups are whole blocks). Unused slots are
+ *   zero; each row is padded with zero words to a multiple of 4 words
+ *   (16 bytes).
  *   scales: float32 [N, K/group], the grid step delta of each group.
  *   zeros:  uint8   [N, K/group], the integer zero point z of each group.
  *   A weight dequantizes to (q - z) * delta.
@@ -82,8 +86,8 @@ const char* awq_status_string(int status);
 int awq_version(void);
 
 /* uint32 words per packed row for (K, bits, group); 0 if the combination is
- * invalid. int4 + group 128: K/8. int3 + group 128: 13 words per group,
- * rounded up to a multiple of 4. */
+ * invalid. int4: K/8. int3: 13 words per 128 codes, rounded up to a
+ * multiple of 4. */
 size_t awq_packed_words_per_row(int K, int bits, int group);
 
 /* Activation statistic (AWQ Explained -- "How the scale is chosen": the
@@ -172,7 +176,7 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
  * X': dev fp16 [M, K], already divided by the scale s both matrices were
  * quantized with (one s per activation: gate and up share their input);
  * (qg, sg, zg) and (qu, su, zu): two [N, K] matrices packed as by
- * awq_quantize_pack(_ex); Y: dev fp16 [M, N]. int3 needs group 128. M = 1
+ * awq_quantize_pack(_ex); Y: dev fp16 [M, N]. M = 1
  * (int4) runs the decode kernel, other M the prefill kernel, both reading
  * X' once for the two matrices. Asynchronous on `stream`. */
 awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const float* sg,

@@ -47,6 +47,15 @@ def test_words_per_row_matches_layout(K, bits, group):
     assert awq.packed_words_per_row(K, bits, group) == O.words_per_row(K, bits, group)
 
 
+@pytest.mark.parametrize("K,bits", [(384, 4), (384, 3), (11008, 4), (11008, 3), (28672, 4)])
+def test_words_per_row_per_channel(K, bits):
+    # group -1 (and group = K) is one group per output channel
+    h = awq.lib()
+    assert h.awq_packed_words_per_row(K, bits, -1) == O.words_per_row(K, bits, K)
+    assert h.awq_packed_words_per_row(K, bits, K) == O.words_per_row(K, bits, K)
+    assert O.words_per_row(K, bits, K) == O.words_per_row(K, bits, 128)
+
+
 def test_words_per_row_rejects():
     h = awq.lib()
     assert h.awq_packed_words_per_row(4096, 5, 128) == 0
@@ -54,6 +63,9 @@ def test_words_per_row_rejects():
     assert h.awq_packed_words_per_row(4096, 4, 64) == 0
     assert h.awq_packed_words_per_row(256, 4, -1) == 256 // 8
     assert h.awq_packed_words_per_row(0, 4, 128) == 0
+    assert h.awq_packed_words_per_row(200, 4, -1) == 0        # not a multiple of 128
+    assert h.awq_packed_words_per_row(4096 * 8 + 128, 4, -1) == 0  # past the per-row kernels
+    assert h.awq_packed_words_per_row(1024, 4, 1024 + 128) == 0
 
 
 # fake, aligned, never-dereferenced device addresses
@@ -171,7 +183,7 @@ def test_gate_up_validation():
     assert call(M=0) == E.AWQ_ERR_INVALID_ARG
     assert call(K=200) == E.AWQ_ERR_INVALID_ARG
     assert call(bits=2) == E.AWQ_ERR_UNSUPPORTED
-    assert call(bits=3, group=256, K=512) == E.AWQ_ERR_UNSUPPORTED
+    assert call(group=64) == E.AWQ_ERR_UNSUPPORTED
     import torch
     if not torch.cuda.is_available():
         assert call() == E.AWQ_ERR_NO_DEVICE

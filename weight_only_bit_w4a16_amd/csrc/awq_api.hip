@@ -15,12 +15,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // layers of one joint search (q, k, v or gate, up, and room to spare)
 constexpr int kMaxLayers = 16;
 
-// normalise the group argument (-1 means the whole row); 0 if unsupported
+// normalise the group argument (-1 means the whole row); 0 if unsupported.
+// Groups of 128, 256 or 512 codes, or of the whole row (per output channel)
+// when K is a multiple of 128 and the row fits the per-row kernels.
 int resolve_group(int K, int group) {
   if (group == -1) group = K;
-  if (group != 128 && group != 256 && group != 512) return 0;
   if (K <= 0 || K % group != 0) return 0;
-  return group;
+  if (group == 128 || group == 256 || group == 512) return group;
+  if (group == K && K % 128 == 0 && K <= 4096 * awq::kRowMaxChunks) return group;
+  return 0;
 }
 
 awq_status device_ready() {
@@ -206,7 +209,6 @@ awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const f
   int g = 0;
   awq_status st = check_group(K, bits, group, &g);
   if (st != AWQ_OK) return st;
-  if (bits == 3 && g != 128) return AWQ_ERR_UNSUPPORTED;
   if ((long long)M * K > (1LL << 31) || (long long)N * K > (1LL << 34)) return AWQ_ERR_UNSUPPORTED;
   st = device_ready();
   if (st != AWQ_OK) return st;

@@ -10,8 +10,27 @@
 
 namespace awq {
 
-// words of one packed group: int4 -> group/8, int3 -> ceil(group/10)
-inline int words_per_group(int bits, int group) { return bits == 4 ? group / 8 : (group + 9) / 10; }
+// words of one packed group: int4 -> group/8; int3 -> 13 per 128-code block
+// (every block starts on a word boundary, whatever the group)
+inline int words_per_group(int bits, int group) { return bits == 4 ? group / 8 : 13 * (group / 128); }
+
+// Kernels index a group's scale by (128-code block) >> gshift, with
+// gshift = ceil(log2(group / 128)), and take max(1, blocks >> gshift) groups
+// per row: exact for groups of 128, 256 and 512, and for a group of the
+// whole row (then every block maps to group 0).
+// per-output-channel groups (the whole row) are quantized with the row in
+// registers: K <= 4096 kRowMaxChunks
+constexpr int kRowMaxChunks = 8;
+
+// a group the per-group kernels do not tile (128, 256 or 512 codes): one
+// group of the whole row, quantized by the per-row kernels
+inline bool row_group(int group) { return group != 128 && group != 256 && group != 512; }
+
+inline int group_shift(int group) {
+  int s = 0;
+  while ((128 << s) < group) ++s;
+  return s;
+}
 inline int words_per_row(int K, int bits, int group) {
   int w = (K / group) * words_per_group(bits, group);
   return (w + 3) & ~3;

@@ -76,6 +76,46 @@ __device__ __forceinline__ int quant_code(float wp, GroupGrid g, int qmax) {
   return q < 0 ? 0 : (q > qmax ? qmax : q);
 }
 
+// int3 packing: the 16 lanes of one 128-code block (an aligned 16-lane
+// segment) each hold 8 consecutive codes as 24 bits (lane i: codes
+// 8i .. 8i+7); lane w < 13 gets word w of the block, codes 10w .. 10w+9 at
+// bits 3 (k - 10w) (the last word holds codes 120 .. 127); lanes 13 .. 15 get 0.
+__device__ __forceinline__ uint32_t int3_block_word(uint32_t packed24, int w) {
+  const int t1 = (10 * w) >> 3;
+  const uint32_t lo24 = __shfl(packed24, t1 < 15 ? t1 : 15, 16);
+  const uint32_t hi24 = __shfl(packed24, t1 + 1 < 15 ? t1 + 1 : 15, 16);
+  const uint64_t both = (uint64_t)lo24 | ((uint64_t)(t1 + 1 < 16 ? hi24 : 0u) << 24);
+  const int first = 10 * w - 8 * t1;
+  const int count = w < 12 ? 10 : (w == 12 ? 8 : 0);
+  const uint32_t word = (uint32_t)(both >> (3 * first));
+  return word & (count >= 10 ? 0x3fffffffu : ((1u << (3 * count)) - 1u));
+}
+
+// min and max over a workgroup of NT threads (NT / 64 wavefronts): wavefront
+// shuffles, then the wavefront results through LDS (red holds 2 NT / 64
+// floats); every thread gets the result
+template <int NT>
+__device__ __forceinline__ void block_minmax(float& mn, float& mx, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off));
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[wave] = mn;
+    red[NT / 64 + wave] = mx;
+  }
+  __syncthreads();
+  mn = red[0];
+  mx = red[NT / 64];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) {
+    mn = fminf(mn, red[w]);
+    mx = fmaxf(mx, red[NT / 64 + w]);
+  }
+}
+
 __device__ __forceinline__ float h2f(uint16_t b) {
   return __half2float(__ushort_as_half(b));
 }

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // [N][2K]: 256-wide block c = (hi of k 128c..128c+127 | lo of the same k),
   // so a 64-wide step s reads activations 128*(s/4) + 64*(s%2)
   const int nsteps = BMODE == 0 && hilo ? 2 * (K / BK) : K / BK;
-  const int ng = K >> (7 + gshift);  // quantization groups per row
+  const int ng = max(1, K >> (7 + gshift));  // quantization groups per row
 
   if (BMODE == 3) {
     // zero the slots 128..143 of every row of both buffers once: activation
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         const u32x4a4 v =
             ld_nt(reinterpret_cast<const u32x4a4*>(Q + (size_t)n * wpr + ks * 13 + w0));
         st.b[i] = u32x4{v[0], v[1], v[2], v[3]};
-        st.d[i] = (sel ? S2 : S)[(size_t)n * ng + ks];
-        load_zero(sel ? Z2 : Z, (size_t)n * ng + ks, st.zw[i], st.zsh[i]);
+        st.d[i] = (sel ? S2 : S)[(size_t)n * ng + (ks >> gshift)];
+        load_zero(sel ? Z2 : Z, (size_t)n * ng + (ks >> gshift), st.zw[i], st.zsh[i]);
       }
     }
   };
@@ -528,9 +528,7 @@ unsigned tiles_of(int M, int N, int bm, int bn) {
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
                        const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
                        hipStream_t st) {
-  if (bits == 3 && group != 128) return hipErrorNotSupported;
-  int gshift = 0;
-  while ((128 << gshift) < group) ++gshift;
+  const int gshift = group_shift(group);
   const int wpr = words_per_row(K, bits, group);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
@@ -567,9 +565,7 @@ hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float*
                                const uint8_t* zg, const uint32_t* qu, const float* su,
                                const uint8_t* zu, int M, int N, int K, int bits, int group,
                                __half* Y, hipStream_t st) {
-  if (bits == 3 && group != 128) return hipErrorNotSupported;
-  int gshift = 0;
-  while ((128 << gshift) < group) ++gshift;
+  const int gshift = group_shift(group);
   const int wpr = words_per_row(K, bits, group);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);

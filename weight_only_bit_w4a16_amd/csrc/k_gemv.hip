@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
   const int nrb = (N + 15) >> 4;
   const int rb0 = blockIdx.x * rbw;
   const int nj = min(rbw, nrb - rb0);
-  const int ngr = nch >> gshift;
+  const int ngr = max(1, nch >> gshift);
   const int wpr = K >> 3;
   const int xr = min(nl, (MODE == kOffset ? MP : M) - 1);  // A-operand row of this lane
 
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
   const int j = lane & 15;
   const int jj = lane >> 4;
   const int nch = K >> 7;  // groups of 128 codes per row; SP = ceil(nch / 16)
-  const int ngr = nch >> gshift;
+  const int ngr = max(1, nch >> gshift);
   const int wpr = K >> 3;
   const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
@@ -593,7 +593,7 @@ template <int SP, int RPF, bool FULL, bool DUAL>
 __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
     const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
-    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int wpr) {
+    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int wpr, int gshift) {
   __shared__ u32x4 xs[SP][5][64];  // [piece][operand][lane]
   __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
   const int lane = threadIdx.x & 63;
@@ -602,7 +602,8 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
   const int NW = gridDim.x * 4;
   const int j = lane & 15;
   const int jj = lane >> 4;
-  const int nch = K >> 7;  // groups per row; SP = ceil(nch / 16)
+  const int nch = K >> 7;  // 128-code blocks per row; SP = ceil(nch / 16)
+  const int ngr = max(1, nch >> gshift);  // groups per row
   const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
   const bool diag = jj == (j >> 2);
@@ -762,16 +763,16 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
         }
       }
       const uint32_t* qn = (up2 ? qlane2 : qlane) + nn * wpr;
-      const float* sn = (up2 ? S2 : S) + nn * nch;
-      const uint8_t* zn = (up2 ? Z2 : Z) + nn * nch;
+      const float* sn = (up2 ? S2 : S) + nn * ngr;
+      const uint8_t* zn = (up2 ? Z2 : Z) + nn * ngr;
       // rows past this wavefront's last need no loads (uniform branch)
       if (row + RPF < items) {
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
           const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
           wb[r][s] = u32x4{v[0], v[1], v[2], v[3]};
-          db[r][s] = sn[goff[s]];
-          zb[r][s] = zn[goff[s]];
+          db[r][s] = sn[goff[s] >> gshift];
+          zb[r][s] = zn[goff[s] >> gshift];
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -787,7 +788,8 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
                              hipStream_t st) {
   const int nch = K / 128;
   const int sp = (nch + 15) / 16;
-  if (group != 128 || sp > 6) return hipErrorNotSupported;
+  if (sp > 6) return hipErrorNotSupported;
+  const int gshift = group_shift(group);
   const int wpr = words_per_row(K, 3, group);
   const int nw = max(cu_count() * 8, (N + 63) / 64);
   const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
@@ -798,10 +800,10 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
   do {                                                                                        \
     if (full)                                                                                 \
       hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, false>), g1, block, 0, st, x, q,    \
-                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr);             \
+                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr, gshift);     \
     else                                                                                      \
       hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, false>), g1, block, 0, st, x, q,   \
-                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr);             \
+                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr, gshift);     \
   } while (0)
   switch (sp) {
     case 1: AWQ_W3(1, 4); break;
@@ -847,7 +849,7 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   const int WV = blockDim.x >> 6;
   const int nl = lane & 15, q = lane >> 4;
   const int nch = K >> 7;
-  const int ngr = nch >> gshift;
+  const int ngr = max(1, nch >> gshift);
   const int wpr = K >> 3;
   const int nrb = (N + 15) >> 4;
   const int rb0 = blockIdx.x * rbw;
@@ -1025,7 +1027,7 @@ hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* sc
   const int cpw = 4 * (((nch + 7) / 8 + 3) / 4);
   if (cpw > 8) return hipErrorNotSupported;
   const int wv = (nch + cpw - 1) / cpw;
-  const int ngr = nch >> gshift;
+  const int ngr = max(1, nch >> gshift);
   const int nrb = (N + 15) / 16;
   // one workgroup of 8 wavefronts fills a compute unit at this register use
   const int resident = cu_count() * (wv <= 4 ? 8 / wv : 1);
@@ -1096,7 +1098,7 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   }
   // LDS: activations in MFMA order and their C, S (offset form), the row
   // blocks' partial sums, and the staged scales and zero points
-  const size_t sz = (size_t)rbw * 16 * (nch >> gshift) * 5;
+  const size_t sz = (size_t)rbw * 16 * max(1, nch >> gshift) * 5;
   if (variant == 0 && M <= 16) {
     const int mp = M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16)));
     const int r = mp < 4 ? mp : 4;
@@ -1170,7 +1172,8 @@ hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float
                                 hipStream_t st) {
   const int nch = K / 128;
   const int sp = (nch + 15) / 16;
-  if (group != 128 || sp > 6) return hipErrorNotSupported;
+  if (sp > 6) return hipErrorNotSupported;
+  const int gshift = group_shift(group);
   const int wpr = words_per_row(K, 3, group);
   const int nw = max(cu_count() * 8, (N + 63) / 64);
   const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
@@ -1181,10 +1184,10 @@ hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float
   do {                                                                                        \
     if (full)                                                                                 \
       hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, true>), g1, block, 0, st, x, qg,    \
-                         sg, zg, qu, su, zu, y, N, K, wpr);                                   \
+                         sg, zg, qu, su, zu, y, N, K, wpr, gshift);                           \
     else                                                                                      \
       hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, true>), g1, block, 0, st, x, qg,   \
-                         sg, zg, qu, su, zu, y, N, K, wpr);                                   \
+                         sg, zg, qu, su, zu, y, N, K, wpr, gshift);                           \
   } while (0)
   switch (sp) {
     case 1: AWQ_GU3(1, 4); break;

@@ -64,9 +64,10 @@ __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ S,
                                                       const uint8_t* __restrict__ Z,
                                                       uint16_t* __restrict__ Y, int M, int N,
-                                                      int K, int wpr, int RB) {
+                                                      int K, int wpr, int RB, int gshift) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int ng = K >> 7;
+  const int ng = K >> 7;                  // 128-code blocks per row
+  const int ngr = max(1, ng >> gshift);  // groups per row (scale / zero-point stride)
   u32x4* xp4 = reinterpret_cast<u32x4*>(smem);                                  // [MR][ng][13][8]
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem);
   float2* cs = reinterpret_cast<float2*>(smem + (size_t)MR * ng * GSTR * 4);     // [MR][ng]
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict
       const uint32_t* qg = Q + n * wpr + 13 * g;
 #pragma unroll
       for (int k = 0; k < 13; ++k) wv[u][k] = ld_nt(qg + k);
-      dl[u] = S[n * ng + g];
-      zl[u] = Z[n * ng + g];
+      dl[u] = S[n * ngr + (g >> gshift)];
+      zl[u] = Z[n * ngr + (g >> gshift)];
     }
   };
   // the first pass's weights are in flight while the activations are prepared
@@ -218,7 +219,8 @@ int cus() {
 hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scales,
                           const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
                           hipStream_t st) {
-  if (group != 128 || M > kGemvW3MaxM) return hipErrorNotSupported;
+  if (M > kGemvW3MaxM) return hipErrorNotSupported;
+  const int gshift = group_shift(group);
   const int ng = K / 128;
   const int RB = (256 * IPT) / ng;  // rows per pass
   if (RB < 1) return hipErrorNotSupported;
@@ -233,13 +235,13 @@ hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scale
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   if (mr == 1)
     hipLaunchKernelGGL((gemv_w3_kernel<1>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
-                       wpr, RB);
+                       wpr, RB, gshift);
   else if (mr == 2)
     hipLaunchKernelGGL((gemv_w3_kernel<2>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
-                       wpr, RB);
+                       wpr, RB, gshift);
   else
     hipLaunchKernelGGL((gemv_w3_kernel<4>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
-                       wpr, RB);
+                       wpr, RB, gshift);
   return hipGetLastError();
 }
 

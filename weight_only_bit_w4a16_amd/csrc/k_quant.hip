@@ -11,8 +11,9 @@ namespace awq {
 // One thread owns 8 consecutive codes of one group; the TPG = group/8
 // threads of a group sit in one wavefront and reduce min/max with shuffles.
 // int4: each thread writes its own packed word. int3: each thread folds its
-// 8 codes into 24 bits; thread w of the group gathers the 24-bit blocks that
-// cover codes 10w..10w+9 from its neighbours and writes word w.
+// 8 codes into 24 bits; within each 128-code block (16 threads, 13 words),
+// thread w gathers the 24-bit pieces that cover codes 10w..10w+9 from its
+// neighbours and writes word w.
 // ---------------------------------------------------------------------------
 template <int BITS, int TPG, bool SYM>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ W,
@@ -80,23 +81,14 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
     if (BITS == 4) {
       if (active) qrow[g * (G / 8) + j] = packed;
     } else {
-      constexpr int WPG = (G + 9) / 10;
-      // word w holds codes 10w .. 10w+9, which lie in the 8-code blocks t1, t1+1
-      const int w = j;
-      const int t1 = (10 * w) >> 3;
-      const uint32_t lo24 = __shfl(packed, t1 < TPG ? t1 : TPG - 1, TPG);
-      const uint32_t hi24 = __shfl(packed, t1 + 1 < TPG ? t1 + 1 : TPG - 1, TPG);
-      const uint64_t both = (uint64_t)lo24 | ((uint64_t)(t1 + 1 < TPG ? hi24 : 0u) << 24);
-      const int first = 10 * w - 8 * t1;          // code offset inside block t1
-      const int left = G - 10 * w;  // codes of this group from slot 0 of word w on
-      const int count = left < 0 ? 0 : (left < 10 ? left : 10);
-      uint32_t word = (uint32_t)(both >> (3 * first));
-      word &= count >= 10 ? 0x3fffffffu : ((1u << (3 * count)) - 1u);
+      const int jb = j & 15;                         // lane in the 128-code block
+      const int blk = g * (G / 128) + (j >> 4);      // block of the row
+      const uint32_t word = int3_block_word(packed, jb);
       if (active) {
-        if (w < WPG) {
-          qrow[g * WPG + w] = word;
-        } else if (g == ng - 1 && g * WPG + w < wpr) {
-          qrow[g * WPG + w] = 0u;  // row padding to 16 bytes
+        if (jb < 13) {
+          qrow[13 * blk + jb] = word;
+        } else if (blk == K / 128 - 1 && 13 * blk + jb < wpr) {
+          qrow[13 * blk + jb] = 0u;  // row padding to 16 bytes
         }
       }
     }
@@ -107,9 +99,117 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-output-channel groups (a group of the whole row, K a multiple of 128):
+// one workgroup of 512 threads per row, the row held in registers (CH chunks
+// of 8 codes per thread, K <= 4096 CH) between the row-wide min / max and the
+// quantization. Chunk c of thread t covers codes 8 (t + 512 c) .. + 7, so the
+// 16 threads of a 128-code block are one aligned 16-lane segment, as the
+// int3 word gather needs.
+// ---------------------------------------------------------------------------
+template <int BITS, int CH, bool SYM>
+__global__ __launch_bounds__(512) void quant_pack_row_kernel(const uint16_t* __restrict__ W,
+                                                             const float* __restrict__ s, int K,
+                                                             uint32_t* __restrict__ Q,
+                                                             float* __restrict__ scales,
+                                                             uint8_t* __restrict__ zeros,
+                                                             int wpr) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  __shared__ float red[16];
+  const size_t n = blockIdx.x;
+  const int t = threadIdx.x;
+  u32x4 raw[CH];
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k0 = 8 * (t + 512 * c);
+    raw[c] = k0 < K ? *reinterpret_cast<const u32x4*>(W + n * K + k0) : u32x4{0u, 0u, 0u, 0u};
+    if (k0 < K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sv = s != nullptr ? s[k0 + i] : 1.0f;
+        const float wp = h2f((uint16_t)(raw[c][i >> 1] >> (16 * (i & 1)))) * sv;
+        mn = fminf(mn, wp);
+        mx = fmaxf(mx, wp);
+      }
+    }
+  }
+  block_minmax<512>(mn, mx, red);
+  const GroupGrid gg = grid_of<SYM, BITS>(mn, mx);
+  uint32_t* qrow = Q + n * wpr;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k0 = 8 * (t + 512 * c);
+    if (8 * 512 * c >= K) break;  // uniform: no thread has this chunk
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sv = s != nullptr && k0 < K ? s[k0 + i] : 1.0f;
+      const float wp = h2f((uint16_t)(raw[c][i >> 1] >> (16 * (i & 1)))) * sv;
+      packed |= (uint32_t)quant_code(wp, gg, QMAX) << (BITS * i);
+    }
+    if (BITS == 4) {
+      if (k0 < K) qrow[k0 >> 3] = packed;
+    } else {
+      // blocks are whole 16-lane segments, all inside or all past the row
+      const int jb = t & 15, blk = k0 >> 7;
+      const uint32_t word = int3_block_word(packed, jb);
+      if (k0 < K) {
+        if (jb < 13)
+          qrow[13 * blk + jb] = word;
+        else if (blk == K / 128 - 1 && 13 * blk + jb < wpr)
+          qrow[13 * blk + jb] = 0u;  // row padding to 16 bytes
+      }
+    }
+  }
+  if (BITS == 4 && t < wpr - K / 8) qrow[K / 8 + t] = 0u;  // int4 rows are whole 16 B
+  if (t == 0) {
+    scales[n] = gg.delta;
+    zeros[n] = (uint8_t)gg.z;
+  }
+}
+
+hipError_t launch_quant_pack_row(const __half* W, const float* s, int N, int K, int bits,
+                                 bool zero_point, uint32_t* q, float* scales, uint8_t* zeros,
+                                 hipStream_t st) {
+  const int ch = (K + 4095) / 4096;
+  if (ch > kRowMaxChunks) return hipErrorNotSupported;
+  const int wpr = words_per_row(K, bits, K);
+  const uint16_t* w = reinterpret_cast<const uint16_t*>(W);
+#define AWQ_QR(B, C, SY)                                                                       \
+  hipLaunchKernelGGL((quant_pack_row_kernel<B, C, SY>), dim3((unsigned)N), dim3(512), 0, st, w, \
+                     s, K, q, scales, zeros, wpr)
+#define AWQ_QR2(C)                    \
+  do {                                \
+    if (bits == 4 && zero_point)      \
+      AWQ_QR(4, C, false);            \
+    else if (bits == 4)               \
+      AWQ_QR(4, C, true);             \
+    else if (zero_point)              \
+      AWQ_QR(3, C, false);            \
+    else                              \
+      AWQ_QR(3, C, true);             \
+  } while (0)
+  switch (ch) {
+    case 1: AWQ_QR2(1); break;
+    case 2: AWQ_QR2(2); break;
+    case 3: AWQ_QR2(3); break;
+    case 4: AWQ_QR2(4); break;
+    case 5: AWQ_QR2(5); break;
+    case 6: AWQ_QR2(6); break;
+    case 7: AWQ_QR2(7); break;
+    default: AWQ_QR2(8); break;
+  }
+#undef AWQ_QR2
+#undef AWQ_QR
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int bits, int group,
                              bool zero_point, uint32_t* q, float* scales, uint8_t* zeros,
                              hipStream_t st) {
+  if (row_group(group))
+    return launch_quant_pack_row(W, s, N, K, bits, zero_point, q, scales, zeros, st);
   const int wpr = words_per_row(K, bits, group);
   // about 4 rows per thread
   const int gy = (N + 3) / 4 < 65535 ? (N + 3) / 4 : 65535;

@@ -112,6 +112,74 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
   }
 }
 
+// The same for per-output-channel groups (the whole row): one workgroup of
+// 512 threads per row, the row in registers between the row-wide min / max
+// and the error terms (chunk c of thread t: codes 8 (t + 512 c) .. + 7).
+template <int BITS, int CH, bool SCALED, bool SYM>
+__global__ __launch_bounds__(512) void fake_quant_error_row_kernel(const uint16_t* __restrict__ W,
+                                                                   const float* __restrict__ s,
+                                                                   int K,
+                                                                   uint16_t* __restrict__ E) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  __shared__ float red[16];
+  const size_t n = blockIdx.x;
+  const int t = threadIdx.x;
+  u32x4 raw[CH];
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k0 = 8 * (t + 512 * c);
+    raw[c] = k0 < K ? *reinterpret_cast<const u32x4*>(W + n * K + k0) : u32x4{0u, 0u, 0u, 0u};
+    if (k0 < K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wp = h2f((uint16_t)(raw[c][i >> 1] >> (16 * (i & 1)))) * s[k0 + i];
+        mn = fminf(mn, wp);
+        mx = fmaxf(mx, wp);
+      }
+    }
+  }
+  block_minmax<512>(mn, mx, red);
+  const GroupGrid gg = grid_of<SYM, BITS>(mn, mx);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k0 = 8 * (t + 512 * c);
+    if (k0 >= K) continue;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t h[2], l[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * p + e;
+        const float sv = s[k0 + i];
+        const float w = h2f((uint16_t)(raw[c][p] >> (16 * e)));
+        const float wp = w * sv;
+        const int q = quant_code(wp, gg, QMAX);
+        const float back = (float)(q - gg.z) * gg.delta;
+        if constexpr (SCALED) {
+          h[e] = __half_as_ushort(__float2half_rn((wp - back) * 256.0f));
+          l[e] = 0u;
+        } else {
+          const float dv = w - back * __builtin_amdgcn_rcpf(sv);
+          const __half dh = __float2half_rn(dv);
+          h[e] = __half_as_ushort(dh);
+          l[e] = __half_as_ushort(__float2half_rn(dv - __half2float(dh)));
+        }
+      }
+      hi[p] = h[0] | (h[1] << 16);
+      lo[p] = l[0] | (l[1] << 16);
+    }
+    if constexpr (SCALED) {
+      *reinterpret_cast<uint4*>(E + n * K + k0) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    } else {
+      uint16_t* row = E + n * 2 * K + 256 * (k0 >> 7) + (k0 & 127);
+      *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(row + 128) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+  }
+}
+
 // loss[a] = sum of the tile partials of alpha a, in a fixed order
 __global__ void reduce_loss_kernel(const double* __restrict__ partial, int tiles, double scale,
                                    double* __restrict__ loss) {
@@ -199,7 +267,37 @@ hipError_t layer_losses(const __half* W, const __half* Xc, int N, int K, int T,
     else                                        \
       AWQ_FQ(B, TP, false, true);               \
   } while (0)
-    if (bits == 4) {
+#define AWQ_FR(B, C, SC, SY)                                                                \
+  hipLaunchKernelGGL((fake_quant_error_row_kernel<B, C, SC, SY>), dim3((unsigned)N), dim3(512), 0, \
+                     st, w, s, K, E)
+#define AWQ_FR2(B, C)                           \
+  do {                                          \
+    if (scaled && zero_point)                   \
+      AWQ_FR(B, C, true, false);                \
+    else if (scaled)                            \
+      AWQ_FR(B, C, true, true);                 \
+    else if (zero_point)                        \
+      AWQ_FR(B, C, false, false);               \
+    else                                        \
+      AWQ_FR(B, C, false, true);                \
+  } while (0)
+#define AWQ_FR3(B)                              \
+  do {                                          \
+    switch ((K + 4095) / 4096) {                \
+      case 1: AWQ_FR2(B, 1); break;             \
+      case 2: AWQ_FR2(B, 2); break;             \
+      case 3: AWQ_FR2(B, 3); break;             \
+      case 4: AWQ_FR2(B, 4); break;             \
+      case 5: AWQ_FR2(B, 5); break;             \
+      case 6: AWQ_FR2(B, 6); break;             \
+      case 7: AWQ_FR2(B, 7); break;             \
+      default: AWQ_FR2(B, 8); break;            \
+    }                                           \
+  } while (0)
+    if (row_group(group)) {  // per output channel
+      if (bits == 4) AWQ_FR3(4);
+      else AWQ_FR3(3);
+    } else if (bits == 4) {
       if (group == 128) AWQ_FQ2(4, 16);
       else if (group == 256) AWQ_FQ2(4, 32);
       else AWQ_FQ2(4, 64);
@@ -208,6 +306,9 @@ hipError_t layer_losses(const __half* W, const __half* Xc, int N, int K, int T,
       else if (group == 256) AWQ_FQ2(3, 32);
       else AWQ_FQ2(3, 64);
     }
+#undef AWQ_FR3
+#undef AWQ_FR2
+#undef AWQ_FR
 #undef AWQ_FQ2
 #undef AWQ_FQ
     e = hipGetLastError();
