@@ -64,6 +64,13 @@ R20 the fold of diag(s)^-1 into the normalization that precedes the layer
 R21 one norm carries one s, so layers that read the same normalized input
     (q/k/v; gate/up) share s, and its search minimizes the sum of their
     layer-output errors, summed in layer order; the first minimum wins.
+R23 the ablations the pages report as perplexities are reported here as the
+    layer-output error of R7 (no model or corpus exists here): keeping the
+    salient fraction (1%, AWQ Explained -- "The premise: 1% of channels") of
+    input channels in FP16 means quantizing W as usual and restoring those
+    columns to their FP16 values; salient by activation is the largest
+    mean |x| (the statistic of R1), by weight the largest mean |W| over the
+    column's output channels; ties go to the lower channel index.
 R17 zero_point=false (the AwqConfig option, AWQ Explained -- "How the scale
     is chosen", last paragraph) is the symmetric grid: delta = max|W'| /
     (2^(b-1) - 1) per group, codes rint(W' / delta) in [-(2^(b-1) - 1),
@@ -375,3 +382,35 @@ def joint_scale_search(Ws, xcal: np.ndarray, alpha_grid, bits: int, group: int,
         if losses[i] < losses[best]:
             best = i
     return scale_from_stats(m, alpha_grid[best]), best, losses
+
+
+# ----------------------------------------------------------------------------
+# ablations (R23): FP16-kept salient channels against scaling
+# ----------------------------------------------------------------------------
+
+
+def weight_channel_magnitude(W: np.ndarray) -> np.ndarray:
+    """mean_n |W[n, k]| per input channel k, in float64 (exact sums)."""
+    return np.abs(np.asarray(W, dtype=np.float16).astype(np.float64)).mean(axis=0)
+
+
+def salient_channels(score: np.ndarray, count: int) -> np.ndarray:
+    """Indices of the `count` largest scores, ties to the lower index, in
+    increasing order."""
+    score = np.asarray(score, dtype=np.float64)
+    order = sorted(range(len(score)), key=lambda k: (-score[k], k))
+    return np.sort(np.asarray(order[:count], dtype=np.int64))
+
+
+def layer_loss_fp16_kept(xcal: np.ndarray, W: np.ndarray, channels, bits: int, group: int,
+                         zero_point: bool = True) -> float:
+    """R7's loss with plain RTN (s = 1) except that the input channels
+    `channels` keep their FP16 weights: D = W - Wq with those columns of Wq
+    replaced by W's."""
+    q, scales, zeros = quantize(W, None, bits, group, zero_point)
+    what = dequantize(q, scales, zeros, group)
+    w = np.asarray(W, dtype=np.float16).astype(np.float64)
+    ch = np.asarray(channels, dtype=np.int64)
+    what[:, ch] = w[:, ch]
+    E = np.asarray(xcal, dtype=np.float16).astype(np.float64) @ (w - what).T
+    return float(np.sum(E * E))

@@ -655,3 +655,51 @@ def test_joint_search_equals_search_on_stacked_rows():
         s1, b1, l1 = O.joint_scale_search([W1], Xc, grid, 3, 128, zp)
         s0, b0, l0 = O.scale_search(W1, Xc, grid, 3, 128, zp)
         assert np.array_equal(l1, l0) and b1 == b0 and np.array_equal(s1, s0)
+
+
+# ---------------------------------------------------------------------------
+# ablations (R23)
+# ---------------------------------------------------------------------------
+
+def test_salient_channels_hand_cases():
+    assert O.salient_channels([0.1, 5.0, 0.3, 5.0, 2.0], 2).tolist() == [1, 3]
+    assert O.salient_channels([0.1, 5.0, 0.3, 5.0, 2.0], 3).tolist() == [1, 3, 4]
+    assert O.salient_channels([1.0, 1.0, 1.0], 2).tolist() == [0, 1]  # ties: lower index
+    assert O.salient_channels([3.0, 1.0], 0).tolist() == []
+    W = np.array([[1, -4, 0.5], [-1, 2, 0.5]], np.float16)
+    assert O.weight_channel_magnitude(W).tolist() == [1.0, 3.0, 0.5]
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_fp16_kept_limits_and_masked_identity(bits):
+    """No kept channel is plain RTN; every channel kept is exact (loss 0);
+    and keeping channels C is the RTN loss of the calibration batch with the
+    columns C set to zero (D's columns C vanish)."""
+    W, Xc, ch = datagen.small_layer(512, 64, 48, 5, 40.0, seed=95)
+    rtn = O.layer_loss(Xc, W, np.ones(512, np.float32), bits, 128)
+    assert O.layer_loss_fp16_kept(Xc, W, [], bits, 128) == rtn
+    assert O.layer_loss_fp16_kept(Xc, W, np.arange(512), bits, 128) == 0.0
+    Xm = Xc.copy()
+    Xm[:, ch] = 0
+    kept = O.layer_loss_fp16_kept(Xc, W, ch, bits, 128)
+    assert kept == pytest.approx(O.layer_loss(Xm, W, np.ones(512, np.float32), bits, 128),
+                                 rel=1e-12)
+
+
+def test_ablation_orderings_on_outlier_layer():
+    """The pages' qualitative findings, as layer-output errors on a layer
+    whose 1% outlier channels carry large activations: keeping the
+    activation-salient 1% in FP16 removes most of the RTN error, keeping
+    the weight-salient 1% barely helps, and the scale search recovers most
+    of the gap without mixed precision."""
+    w = datagen.WORKLOADS["llama7b_attn_4096x4096_int4"]
+    W, Xc = datagen.weight(w)[:512], datagen.calibration(w)
+    n = round(0.01 * w.K)
+    rtn = O.layer_loss(Xc, W, np.ones(w.K, np.float32), 4, 128)
+    act = O.layer_loss_fp16_kept(Xc, W, O.salient_channels(O.act_stats(Xc), n), 4, 128)
+    wgt = O.layer_loss_fp16_kept(Xc, W, O.salient_channels(O.weight_channel_magnitude(W), n),
+                                 4, 128)
+    _, _, losses = O.scale_search(W, Xc, datagen.alpha_grid(20), 4, 128)
+    assert act < 0.1 * rtn
+    assert wgt > 0.9 * rtn
+    assert losses.min() < 0.3 * rtn
