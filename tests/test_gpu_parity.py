@@ -259,6 +259,20 @@ def test_prefill_int4_larger_groups(group):
     assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, group, K))
 
 
+def test_prefill_split_tail():
+    """2048 x 9316: 296 tiles of 256 x 256, so the first 8192 columns run as
+    one whole round of big tiles and the rest on 128 x 256 tiles; the
+    checked columns straddle the split and the ragged end."""
+    M, N, K = 2048, 9316, 512
+    W = datagen.random_f16((N, K), 0.02, seed=41)
+    X = datagen.random_f16((M, K), 1.0, seed=42)
+    q, sc, z = _packed(W, None, 4, 128)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, 128))
+    qo, so, zo = O.quantize_pack(W, None, 4, 128)
+    cols = np.r_[0:64, 8160:8224, 9216:9316]
+    assert_rows_close(Y[:, cols], O.matmul_rows(X, qo, so, zo, 4, 128, K, cols))
+
+
 def _prefill_cases():
     return [(name, M) for name, w in datagen.WORKLOADS.items() for M in w.prefill_M]
 

@@ -116,7 +116,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const float* __restrict__ S,
     const uint8_t* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
     uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo,
-    const void* __restrict__ B2, const float* __restrict__ S2, const uint8_t* __restrict__ Z2) {
+    const void* __restrict__ B2, const float* __restrict__ S2, const uint8_t* __restrict__ Z2,
+    int nbase, int nend) {
   constexpr int NT = 64 * WGM * WGN;
   static_assert(NST == 2 || NST == 4, "register stages");
   using C = Cfg<BMODE, BM, BN, NT>;
@@ -139,12 +140,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // XCD a contiguous run of tiles that walk M for a fixed N tile, so the
   // weight tile is reused from that XCD's L2
   const int mt = (M + BM - 1) / BM;
-  const int ntl = (N + BNO - 1) / BNO;
+  // this launch covers outputs [nbase, nend) of the N (Y's row stride)
+  const int ntl = (nend - nbase + BNO - 1) / BNO;
   const int total = mt * ntl;
   int t = blockIdx.x;
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   const int m0 = (t % mt) * BM;
-  const int n0 = (t / mt) * BNO;
+  const int n0 = nbase + (t / mt) * BNO;
   // fp16 B with hilo set holds each term as a hi and a lo fp16 part,
   // [N][2K]: 256-wide block c = (hi of k 128c..128c+127 | lo of the same k),
   // so a 64-wide step s reads activations 128*(s/4) + 64*(s%2)
@@ -464,7 +466,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         for (int v = 0; v < 16; ++v) {
           const int m =
               m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][v]));
+          if (m < M && n < nend)
+            Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][v]));
         }
       }
   } else if constexpr (EPI == 2) {
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
               m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const float g = acc[i][j][v];
           const float val = g / (1.0f + __expf(-g)) * acc[i][j + 1][v];
-          if (m < M && n < N) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(val));
+          if (m < M && n < nend) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(val));
         }
       }
   } else {
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
           const int m =
               m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const float e = acc[i][j][v];
-          if (m < M && n < N) sq = __builtin_fmaf(e, e, sq);
+          if (m < M && n < nend) sq = __builtin_fmaf(e, e, sq);
         }
       }
     double ds = (double)sq;
@@ -534,27 +537,44 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   const unsigned cus = (unsigned)cu_n();
   const bool zw = ((size_t)N * (size_t)(K / group)) % 4 == 0;
-#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST)                                                 \
+#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST, NB, NE)                                         \
   do {                                                                                          \
     if (zw)                                                                                     \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST>),                  \
-                         dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
-                         zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr, nullptr, nullptr); \
+                         dim3(tiles_of(M, (NE) - (NB), BM, BN)), dim3(64 * WGM * WGN), 0, st, x, \
+                         q, scales, zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr,        \
+                         nullptr, nullptr, NB, NE);                                             \
     else                                                                                        \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST>),                 \
-                         dim3(tiles_of(M, N, BM, BN)), dim3(64 * WGM * WGN), 0, st, x, q, scales, \
-                         zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr, nullptr, nullptr); \
+                         dim3(tiles_of(M, (NE) - (NB), BM, BN)), dim3(64 * WGM * WGN), 0, st, x, \
+                         q, scales, zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr,        \
+                         nullptr, nullptr, NB, NE);                                             \
   } while (0)
   if (bits == 4) {
     // the largest tile that still gives every compute unit work
-    if (tiles_of(M, N, 256, 256) >= cus)
-      AWQ_GEMM(4, 256, 256, 2, 4, 2);
-    else if (tiles_of(M, N, 128, 128) >= cus)
-      AWQ_GEMM(4, 128, 128, 2, 2, 4);
-    else
-      AWQ_GEMM(4, 64, 64, 2, 2, 4);
+    const unsigned big = tiles_of(M, N, 256, 256);
+    if (big >= cus) {
+      // Whole rounds of 256 x 256 tiles (one per compute unit each), and the
+      // columns past them on 128 x 256 tiles when those fit in one round:
+      // a partial last round of big tiles would leave compute units idle for
+      // a whole tile time, the small tiles take about half of it.
+      const int mt = (M + 255) / 256;
+      const int nsplit = (int)((big / cus) * cus / (unsigned)mt) * 256;
+      const bool split = big % cus != 0 && nsplit > 0 && nsplit < N &&
+                         tiles_of(M, N - nsplit, 128, 256) <= cus;
+      if (split) {
+        AWQ_GEMM(4, 256, 256, 2, 4, 2, 0, nsplit);
+        AWQ_GEMM(4, 128, 256, 2, 4, 4, nsplit, N);
+      } else {
+        AWQ_GEMM(4, 256, 256, 2, 4, 2, 0, N);
+      }
+    } else if (tiles_of(M, N, 128, 128) >= cus) {
+      AWQ_GEMM(4, 128, 128, 2, 2, 4, 0, N);
+    } else {
+      AWQ_GEMM(4, 64, 64, 2, 2, 4, 0, N);
+    }
   } else {
-    AWQ_GEMM(3, 64, 64, 2, 2, 4);
+    AWQ_GEMM(3, 64, 64, 2, 2, 4, 0, N);
   }
 #undef AWQ_GEMM
   return hipGetLastError();
@@ -576,11 +596,11 @@ hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float*
     if (zw)                                                                                       \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 2, BM, BN, WGM, WGN, true, NST>),                    \
                          dim3(tiles_of(M, N, BM, BN / 2)), dim3(64 * WGM * WGN), 0, st, x, qg, sg, \
-                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu);                    \
+                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N);              \
     else                                                                                          \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 2, BM, BN, WGM, WGN, false, NST>),                   \
                          dim3(tiles_of(M, N, BM, BN / 2)), dim3(64 * WGM * WGN), 0, st, x, qg, sg, \
-                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu);                    \
+                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N);              \
   } while (0)
   if (bits == 4) {
     if (tiles_of(M, N, 256, 128) >= cus)
@@ -605,7 +625,7 @@ hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N,
                              double* partial, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false, 2>), dim3(tiles_of(M, N, 128, 128)),
                      dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial,
-                     hilo ? 1 : 0, nullptr, nullptr, nullptr);
+                     hilo ? 1 : 0, nullptr, nullptr, nullptr, 0, N);
   return hipGetLastError();
 }
 

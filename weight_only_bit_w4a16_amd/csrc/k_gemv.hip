@@ -1071,8 +1071,12 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   }
   if (variant == 0 && M == 1) {
     const int sp = (nch + 15) / 16;
-    // wavefronts: all resident at ~2 per SIMD, and at most 64 rows each
-    const int nw = max(cu_count() * 8, (N + 63) / 64);
+    // wavefronts: all resident, at most 64 rows each; 2 per SIMD, or 3 when
+    // the registers allow it (up to 4 pieces) and every wavefront still gets
+    // 5 or more rows (measured: 3 per SIMD is 2-4% faster there and slower
+    // for fewer rows or longer rows)
+    const int wpc = sp <= 4 && N >= 5 * 8 * cu_count() ? 12 : 8;
+    const int nw = max(cu_count() * wpc, (N + 63) / 64);
     const dim3 g1((unsigned)((min(N, nw) + 3) / 4));
     const bool full = nch % 16 == 0;
 #define AWQ_M1(SM, RP)                                                                          \
