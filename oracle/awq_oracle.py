@@ -71,6 +71,12 @@ R23 the ablations the pages report as perplexities are reported here as the
     columns to their FP16 values; salient by activation is the largest
     mean |x| (the statistic of R1), by weight the largest mean |W| over the
     column's output channels; ties go to the lower channel index.
+R24 compact storage of the group parameters (an AwqConfig storage variant):
+    the step as fp16 (one rounding of the float32 delta) and the zero points
+    as 4-bit fields, 8 per uint32 word in group order (group g of a row in
+    word g // 8, bits 4 (g % 8)), each row padded to whole words. Every zero
+    point fits 4 bits (at most 2^b - 1 <= 15). The product then dequantizes
+    with the fp16 step: (q - z) * float(fp16(delta)).
 R17 zero_point=false (the AwqConfig option, AWQ Explained -- "How the scale
     is chosen", last paragraph) is the symmetric grid: delta = max|W'| /
     (2^(b-1) - 1) per group, codes rint(W' / delta) in [-(2^(b-1) - 1),
@@ -414,3 +420,36 @@ def layer_loss_fp16_kept(xcal: np.ndarray, W: np.ndarray, channels, bits: int, g
     what[:, ch] = w[:, ch]
     E = np.asarray(xcal, dtype=np.float16).astype(np.float64) @ (w - what).T
     return float(np.sum(E * E))
+
+
+# ----------------------------------------------------------------------------
+# compact storage of the group parameters (R24)
+# ----------------------------------------------------------------------------
+
+
+def compact_group_params(scales: np.ndarray, zeros: np.ndarray):
+    """(fp16 steps [N, ng], uint32 packed zero points [N, ceil(ng / 8)])."""
+    sc = np.asarray(scales, dtype=np.float32)
+    z = np.asarray(zeros, dtype=np.uint8)
+    assert np.all(z <= 15)
+    N, ng = z.shape
+    zw = np.zeros((N, -(-ng // 8)), dtype=np.uint64)
+    for g in range(ng):
+        zw[:, g // 8] |= z[:, g].astype(np.uint64) << np.uint64(4 * (g % 8))
+    return sc.astype(np.float16), zw.astype(np.uint32)
+
+
+def expand_group_params(scales16: np.ndarray, zeros4: np.ndarray, ng: int):
+    """Inverse of the packing: (float32 steps as stored, uint8 zero points)."""
+    N = scales16.shape[0]
+    z = np.empty((N, ng), dtype=np.uint8)
+    w = zeros4.astype(np.uint64)
+    for g in range(ng):
+        z[:, g] = ((w[:, g // 8] >> np.uint64(4 * (g % 8))) & np.uint64(15)).astype(np.uint8)
+    return np.asarray(scales16, dtype=np.float16).astype(np.float32), z
+
+
+def matmul_compact(Xp, qpacked, scales16, zeros4, bits: int, group: int, K: int) -> np.ndarray:
+    """The W4A16 product with compactly stored group parameters (R24)."""
+    sc, z = expand_group_params(scales16, zeros4, K // group)
+    return matmul(Xp, qpacked, sc, z, bits, group, K)

@@ -703,3 +703,41 @@ def test_ablation_orderings_on_outlier_layer():
     assert act < 0.1 * rtn
     assert wgt > 0.9 * rtn
     assert losses.min() < 0.3 * rtn
+
+
+# ---------------------------------------------------------------------------
+# compact storage of the group parameters (R24)
+# ---------------------------------------------------------------------------
+
+def test_compact_group_params_hand_words():
+    """Zero points 0..15 of one row read back from a word printed in hex
+    (slot 7 down to slot 0), and fp16 steps rounded once."""
+    z = np.arange(16, dtype=np.uint8)[None, :]
+    sc = np.full((1, 16), 0.1, np.float32)
+    s16, z4 = O.compact_group_params(sc, z)
+    assert [format(int(v), "08x") for v in z4[0]] == ["76543210", "fedcba98"]
+    assert s16.dtype == np.float16 and np.all(s16 == np.float16(0.1))
+    # 9 groups: the second word holds one zero point, the rest is zero
+    s16, z4 = O.compact_group_params(sc[:, :9], np.full((1, 9), 13, np.uint8))
+    assert z4.shape == (1, 2) and int(z4[0, 0]) == 0xDDDDDDDD and int(z4[0, 1]) == 0xD
+
+
+@pytest.mark.parametrize("bits,group,K", [(4, 128, 1024), (3, 128, 640), (4, 256, 2048),
+                                          (4, 384, 384), (3, 512, 1024)])
+def test_compact_roundtrip_and_product(bits, group, K):
+    W = datagen.random_f16((9, K), 0.02, seed=K + group)
+    X = datagen.random_f16((3, K), 1.0, seed=7)
+    qp, sc, z = O.quantize_pack(W, None, bits, group)
+    s16, z4 = O.compact_group_params(sc, z)
+    sc2, z2 = O.expand_group_params(s16, z4, K // group)
+    assert np.array_equal(z2, z)
+    assert np.array_equal(sc2, sc.astype(np.float16).astype(np.float32))
+    # the compact product is the plain product with the fp16-rounded steps
+    Yc = O.matmul_compact(X, qp, s16, z4, bits, group, K)
+    Yr = O.matmul(X, qp, sc.astype(np.float16).astype(np.float32), z, bits, group, K)
+    assert np.array_equal(Yc, Yr)
+    # and within fp16's step rounding (2^-11 relative per group) of the exact one
+    Y = O.matmul(X, qp, sc, z, bits, group, K)
+    bound = 2.0 ** -11 * (np.abs(X.astype(np.float64)) @ np.abs(O.dequantize(
+        O.unpack(qp, bits, group, K), sc, z, group)).T)
+    assert np.all(np.abs(Yc - Y) <= bound * (1 + 1e-9))
