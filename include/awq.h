@@ -184,6 +184,31 @@ awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const f
                                   const uint8_t* zu, int M, int N, int K, int bits, int group,
                                   uint16_t* Y, void* stream);
 
+/* Compact storage of the group parameters (the fp16-scale, packed-zero
+ * format of common AWQ checkpoints; AWQ Explained -- "How the scale is
+ * chosen" names the group size and zero-point options it stores):
+ *   scales16[n, g] = fp16(scales[n, g])             (round-to-nearest-even)
+ *   zeros4[n, g / 8] bits [4 (g % 8), 4 (g % 8) + 4) = zeros[n, g]
+ * scales, zeros: dev, as written by awq_quantize_pack(_ex) for this
+ * (N, K, group) (every zero point fits 4 bits); scales16: dev fp16
+ * [N, K/group]; zeros4: dev uint32 [N, ceil(K/group / 8)], unused fields
+ * zero. A step of 65520 or more becomes infinite in fp16 (the weights' scale
+ * must keep the steps below that). Asynchronous on `stream`. */
+awq_status awq_compact_group_params(const float* scales, const uint8_t* zeros, int N, int K,
+                                    int group, uint16_t* scales16, uint32_t* zeros4,
+                                    void* stream);
+
+/* The product over compactly stored group parameters:
+ *   Y[m, n] = sum_k X'[m, k] * (q[n, k] - z[n, g(k)]) * float(fp16 step)
+ * with the same kernels, accumulation and rounding as
+ * awq_w4a16_matmul_kernel (kernel 0 = automatic, 1 = decode, 2 = int4 exact
+ * decode, 3 = prefill). The parameters take 2.5 of the plain 5 bytes per
+ * group. Asynchronous on `stream`. */
+awq_status awq_w4a16_matmul_compact(const uint16_t* X, const uint32_t* qpacked,
+                                    const uint16_t* scales16, const uint32_t* zeros4, int M, int N,
+                                    int K, int bits, int group, uint16_t* Y, int kernel,
+                                    void* stream);
+
 /* Bytes of device workspace awq_scale_search needs for these sizes
  * (0 if the sizes are invalid). */
 size_t awq_scale_search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);

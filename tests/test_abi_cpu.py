@@ -228,3 +228,22 @@ def test_norm_and_joint_validation():
         assert call() == E.AWQ_ERR_NO_DEVICE
         assert h.awq_rmsnorm(P, P, 4, 256, f(1e-6), P2, NULL) == E.AWQ_ERR_NO_DEVICE
         assert h.awq_fold_norm_weight(P, P, 256, P2, NULL) == E.AWQ_ERR_NO_DEVICE
+
+
+def test_compact_validation():
+    h = awq.lib()
+    E = _lib
+    assert h.awq_compact_group_params(NULL, P, 64, 256, 128, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_compact_group_params(P, P, 0, 256, 128, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+    assert h.awq_compact_group_params(P, P, 64, 256, 64, P, P, NULL) == E.AWQ_ERR_UNSUPPORTED
+    assert h.awq_compact_group_params(P, MIS, 64, 256, 128, P, P, NULL) == E.AWQ_ERR_INVALID_ARG
+
+    def mm(X=P, M=1, kernel=0, bits=4):
+        return h.awq_w4a16_matmul_compact(X, P, P, P, M, 64, 256, bits, 128, P2, kernel, NULL)
+    assert mm(X=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert mm(kernel=5) == E.AWQ_ERR_INVALID_ARG
+    assert mm(kernel=2, bits=3) == E.AWQ_ERR_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        assert mm() == E.AWQ_ERR_NO_DEVICE
+        assert h.awq_compact_group_params(P, P, 64, 256, 128, P, P, NULL) == E.AWQ_ERR_NO_DEVICE

@@ -22,6 +22,7 @@ __all__ = [
     "AwqError", "lib", "packed_words_per_row", "act_stats", "scale_candidates",
     "quantize_pack", "fold_inv_scale", "w4a16_matmul", "gate_up_silu", "scale_search",
     "scale_search_joint", "scale_search_joint_workspace_bytes", "fold_norm_weight", "rmsnorm",
+    "compact_group_params", "w4a16_matmul_compact",
     "scale_search_workspace_bytes", "KERNEL_AUTO", "KERNEL_DECODE", "KERNEL_DECODE_EXACT",
     "KERNEL_PREFILL",
 ]
@@ -155,6 +156,44 @@ def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, ou
         r = lib().awq_w4a16_matmul_kernel(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M,
                                           N, K, bits, group, _ptr(y), kernel, st)
     check(r, "awq_w4a16_matmul")
+    return y
+
+
+def compact_group_params(scales, zeros, K: int, group: int = 128, stream=None):
+    """(fp16 steps [N, ng], int32 words of 4-bit zero points [N, ceil(ng/8)])
+    from the plain float32 / uint8 group parameters of an [N, K] matrix."""
+    torch = _torch()
+    _need(scales, "scales", torch.float32, 2)
+    _need(zeros, "zeros", torch.uint8, 2)
+    N, ng = scales.shape
+    if tuple(zeros.shape) != (N, ng) or ng != K // _group(K, group):
+        raise ValueError("scales and zeros must be [N, K/group]")
+    s16 = torch.empty((N, ng), dtype=torch.float16, device=scales.device)
+    z4 = torch.empty((N, (ng + 7) // 8), dtype=torch.int32, device=scales.device)
+    check(lib().awq_compact_group_params(_ptr(scales), _ptr(zeros), N, K, group, _ptr(s16),
+                                         _ptr(z4), _stream(stream)), "awq_compact_group_params")
+    return s16, z4
+
+
+def w4a16_matmul_compact(Xp, qpacked, scales16, zeros4, bits: int = 4, group: int = 128,
+                         out=None, kernel: int = KERNEL_AUTO, stream=None):
+    """Y = X' dequant(Q)^T over compactly stored group parameters."""
+    torch = _torch()
+    _need(Xp, "Xp", torch.float16, 2)
+    _need(qpacked, "qpacked", torch.int32, 2)
+    _need(scales16, "scales16", torch.float16, 2)
+    _need(zeros4, "zeros4", torch.int32, 2)
+    M, K = Xp.shape
+    N = qpacked.shape[0]
+    g = _group(K, group)
+    if qpacked.shape[1] != packed_words_per_row(K, bits, group):
+        raise ValueError("qpacked has the wrong row length for (K, bits, group)")
+    if tuple(scales16.shape) != (N, K // g) or tuple(zeros4.shape) != (N, (K // g + 7) // 8):
+        raise ValueError("scales16 must be [N, K/group] and zeros4 [N, ceil(K/group / 8)]")
+    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
+    check(lib().awq_w4a16_matmul_compact(_ptr(Xp), _ptr(qpacked), _ptr(scales16), _ptr(zeros4), M,
+                                         N, K, bits, group, _ptr(y), kernel, _stream(stream)),
+          "awq_w4a16_matmul_compact")
     return y
 
 

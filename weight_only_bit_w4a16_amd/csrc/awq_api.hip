@@ -52,9 +52,9 @@ awq_status check_group(int K, int bits, int group, int* g_out) {
   return AWQ_OK;
 }
 
-awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const float* scales,
-                       const uint8_t* zeros, int M, int N, int K, int bits, int group, uint16_t* Y,
-                       void* stream, int kernel) {
+awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* scales,
+                       const void* zeros, int M, int N, int K, int bits, int group, uint16_t* Y,
+                       void* stream, int kernel, bool cs) {
   if (!X || !qpacked || !scales || !zeros || !Y) return AWQ_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(qpacked) || !aligned16(scales) || !aligned16(zeros) ||
@@ -80,23 +80,24 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const float* 
   hipError_t e;
   if (decode) {
     if (bits == 4)
-      e = awq::launch_gemv_w4(x, qpacked, scales, zeros, M, N, K, g, y, s, kernel == 2 ? 1 : 0);
+      e = awq::launch_gemv_w4(x, qpacked, scales, zeros, M, N, K, g, y, s, kernel == 2 ? 1 : 0,
+                              cs);
     else if (M == 1 && kernel == 0)
-      e = awq::launch_gemv_w3_m1(x, qpacked, scales, zeros, N, K, g, y, s);
+      e = awq::launch_gemv_w3_m1(x, qpacked, scales, zeros, N, K, g, y, s, cs);
     else
       e = hipErrorNotSupported;
     if (bits == 3 && e == hipErrorNotSupported) {
       (void)hipGetLastError();
-      e = awq::launch_gemv_w3(x, qpacked, scales, zeros, M, N, K, g, y, s);
+      e = awq::launch_gemv_w3(x, qpacked, scales, zeros, M, N, K, g, y, s, cs);
     }
     // a shape the decode kernel does not cover (its LDS budget) runs on the
     // prefill kernel when the caller let the library choose
     if (e == hipErrorNotSupported && kernel == 0) {
       (void)hipGetLastError();
-      e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s);
+      e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s, cs);
     }
   } else {
-    e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s);
+    e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s, cs);
   }
   return from_hip(e);
 }
@@ -188,13 +189,36 @@ awq_status awq_fold_inv_scale(const uint16_t* X, const float* s, int M, int K, u
 awq_status awq_w4a16_matmul(const uint16_t* X, const uint32_t* qpacked, const float* scales,
                             const uint8_t* zeros, int M, int N, int K, int bits, int group,
                             uint16_t* Y, void* stream) {
-  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, 0);
+  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, 0, false);
 }
 
 awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, const float* scales,
                                    const uint8_t* zeros, int M, int N, int K, int bits, int group,
                                    uint16_t* Y, int kernel, void* stream) {
-  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, kernel);
+  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, kernel, false);
+}
+
+awq_status awq_compact_group_params(const float* scales, const uint8_t* zeros, int N, int K,
+                                    int group, uint16_t* scales16, uint32_t* zeros4,
+                                    void* stream) {
+  if (!scales || !zeros || !scales16 || !zeros4) return AWQ_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(scales) || !aligned16(zeros) || !aligned16(scales16) || !aligned16(zeros4))
+    return AWQ_ERR_INVALID_ARG;
+  int g = 0;
+  awq_status st = check_group(K, 4, group, &g);
+  if (st != AWQ_OK) return st;
+  st = device_ready();
+  if (st != AWQ_OK) return st;
+  return from_hip(awq::launch_compact_params(scales, zeros, N, K / g, scales16, zeros4,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+awq_status awq_w4a16_matmul_compact(const uint16_t* X, const uint32_t* qpacked,
+                                    const uint16_t* scales16, const uint32_t* zeros4, int M, int N,
+                                    int K, int bits, int group, uint16_t* Y, int kernel,
+                                    void* stream) {
+  return matmul_impl(X, qpacked, scales16, zeros4, M, N, K, bits, group, Y, stream, kernel, true);
 }
 
 awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const float* sg,
@@ -220,7 +244,7 @@ awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const f
     e = bits == 4 ? awq::launch_gate_up_w4_m1(x, qg, sg, zg, qu, su, zu, N, K, g, y, s)
                   : awq::launch_gate_up_w3_m1(x, qg, sg, zg, qu, su, zu, N, K, g, y, s);
   else if (bits == 4 && M <= 16)
-    e = awq::launch_gemv_w4_mx(x, qg, sg, zg, M, N, K, g, y, s, qu, su, zu);
+    e = awq::launch_gemv_w4_mx(x, qg, sg, zg, M, N, K, g, y, s, qu, su, zu, false);
   if (e == hipErrorNotSupported) {
     (void)hipGetLastError();
     e = awq::launch_gemm_gate_up(x, qg, sg, zg, qu, su, zu, M, N, K, bits, g, y, s);

@@ -45,37 +45,41 @@ hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int 
                              hipStream_t st);
 hipError_t launch_fold(const __half* X, const float* s, int M, int K, __half* Y, hipStream_t st);
 
+// The product kernels read the group parameters in plain storage (float32
+// steps, uint8 zero points; cs = false) or compact storage (fp16 steps,
+// 4-bit zero points 8 per uint32 word, rows of ceil(groups / 8) words;
+// cs = true).
+//
 // decode, int4, M <= 16. variant 0 picks the fastest kernel for the shape;
 // variant 1 forces the exact-dequant kernel (kept selectable for tests).
-hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scales,
-                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                          hipStream_t st, int variant);
+hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const void* scales,
+                          const void* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st, int variant, bool cs);
 // decode, int3, M <= 4
-hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scales,
-                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                          hipStream_t st);
+hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const void* scales,
+                          const void* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st, bool cs);
 constexpr int kGemvW3MaxM = 4;
-// decode, int3, M = 1, group 128 (K up to 96 groups)
-hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* scales,
-                             const uint8_t* zeros, int N, int K, int group, __half* Y,
-                             hipStream_t st);
+// decode, int3, M = 1 (K up to 96 blocks of 128 codes)
+hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int N, int K, int group, __half* Y, hipStream_t st,
+                             bool cs);
 // prefill (any M)
-hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
-                       const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
-                       hipStream_t st);
-
-// gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)); M = 1 int4 / int3 decode
-// (K up to 96 groups), and the prefill kernel for any M
+hipError_t launch_gemm(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
+                       int M, int N, int K, int bits, int group, __half* Y, hipStream_t st,
+                       bool cs);
+// decode, int4, 2 <= M <= 16, K <= 8192 (NotSupported otherwise); with q2
+// set, the gated-MLP form silu(X Wq^T) * (X Wq2^T)
+hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st, const uint32_t* q2, const void* scales2,
+                             const void* zeros2, bool cs);
+// gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)), plain storage; M = 1 int4 /
+// int3 decode (K up to 96 blocks), and the prefill kernel for any M
 hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float* sg,
                                 const uint8_t* zg, const uint32_t* qu, const float* su,
                                 const uint8_t* zu, int N, int K, int group, __half* Y,
                                 hipStream_t st);
-// decode, int4, 2 <= M <= 16, K <= 8192 (NotSupported otherwise); with q2
-// set, the gated-MLP form silu(X Wq^T) * (X Wq2^T)
-hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* scales,
-                             const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                             hipStream_t st, const uint32_t* q2, const float* scales2,
-                             const uint8_t* zeros2);
 hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float* sg,
                                 const uint8_t* zg, const uint32_t* qu, const float* su,
                                 const uint8_t* zu, int N, int K, int group, __half* Y,
@@ -84,6 +88,9 @@ hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float*
                                const uint8_t* zg, const uint32_t* qu, const float* su,
                                const uint8_t* zu, int M, int N, int K, int bits, int group,
                                __half* Y, hipStream_t st);
+// plain -> compact group parameters
+hipError_t launch_compact_params(const float* scales, const uint8_t* zeros, int N, int ng,
+                                 uint16_t* scales16, uint32_t* zeros4, hipStream_t st);
 
 // scale search pieces
 size_t search_workspace_bytes(int N, int K, int T, int n_alpha, int bits, int group);

@@ -120,6 +120,26 @@ __device__ __forceinline__ float h2f(uint16_t b) {
   return __half2float(__ushort_as_half(b));
 }
 
+// Group parameters of row n, group g, for a row of ng groups. Plain storage
+// (CS = false): float32 steps and uint8 zero points, [N][ng] each. Compact
+// storage (CS = true): fp16 steps [N][ng] and 4-bit zero points, 8 per
+// uint32 word in group order, [N][ceil(ng / 8)].
+template <bool CS>
+__device__ __forceinline__ float group_scale(const void* S, size_t n, int ng, int g) {
+  if constexpr (CS)
+    return h2f(static_cast<const uint16_t*>(S)[n * ng + g]);
+  else
+    return static_cast<const float*>(S)[n * ng + g];
+}
+template <bool CS>
+__device__ __forceinline__ uint32_t group_zero(const void* Z, size_t n, int ng, int g) {
+  if constexpr (CS)
+    return (static_cast<const uint32_t*>(Z)[n * ((ng + 7) >> 3) + (g >> 3)] >> (4 * (g & 7))) &
+           15u;
+  else
+    return static_cast<const uint8_t*>(Z)[n * ng + g];
+}
+
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
   return __builtin_nontemporal_load(p);

@@ -106,17 +106,19 @@ struct Dq {
 // stores fp16(silu(g) u), silu(g) = g / (1 + e^-g), in fp32. A tile then
 // covers BN / 2 outputs.
 //
-// ZW: zero points are read as the aligned 32-bit word holding them (the
-// zero-point array is a whole number of words); otherwise byte by byte.
+// CS: compact group parameters (fp16 steps, 4-bit zero points 8 per word).
+// ZW (plain storage): zero points are read as the aligned 32-bit word
+// holding them (the zero-point array is a whole number of words); otherwise
+// byte by byte.
 // Word loads keep the loop-carried value 32 bits wide, so no byte
 // extension is scheduled ahead of the MFMAs (it would wait on the newest
 // loads).
-template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW, int NST>
+template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW, int NST, bool CS = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
-    const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
+    const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const void* __restrict__ S,
+    const void* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
     uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo,
-    const void* __restrict__ B2, const float* __restrict__ S2, const uint8_t* __restrict__ Z2,
+    const void* __restrict__ B2, const void* __restrict__ S2, const void* __restrict__ Z2,
     int nbase, int nend) {
   constexpr int NT = 64 * WGM * WGN;
   static_assert(NST == 2 || NST == 4, "register stages");
@@ -172,12 +174,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     return EPI == 2 ? min(n0 + 32 * (r >> 6) + (r & 31), N - 1) : min(n0 + r, N - 1);
   };
   auto bsel = [&](int r) { return EPI == 2 && ((r >> 5) & 1) != 0; };
-  auto load_zero = [&](const uint8_t* Zp, size_t idx, uint32_t& zw, uint32_t& zsh) {
-    if constexpr (ZW) {
-      zw = reinterpret_cast<const uint32_t*>(Zp)[idx >> 2];
+  // zero point of row n, group g = (zw >> zsh) & ZMASK
+  constexpr uint32_t ZMASK = CS ? 15u : 255u;
+  auto load_zero = [&](const void* Zp, size_t n, int g, uint32_t& zw, uint32_t& zsh) {
+    if constexpr (CS) {
+      zw = static_cast<const uint32_t*>(Zp)[n * ((ng + 7) >> 3) + (g >> 3)];
+      zsh = 4u * (uint32_t)(g & 7);
+    } else if constexpr (ZW) {
+      const size_t idx = n * ng + g;
+      zw = static_cast<const uint32_t*>(Zp)[idx >> 2];
       zsh = 8u * (uint32_t)(idx & 3);
     } else {
-      zw = Zp[idx];
+      zw = static_cast<const uint8_t*>(Zp)[n * ng + g];
       zsh = 0u;
     }
   };
@@ -214,8 +222,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const uint32_t* p = Q + (size_t)n * wpr + 8 * ks + w0;
       if constexpr (SZ.value) {
         const int g = (ks * BK) >> (7 + gshift);
-        st.d = (sel ? S2 : S)[(size_t)n * ng + g];
-        load_zero(sel ? Z2 : Z, (size_t)n * ng + g, st.zw, st.zsh);
+        st.d = group_scale<CS>(sel ? S2 : S, (size_t)n, ng, g);
+        load_zero(sel ? Z2 : Z, (size_t)n, g, st.zw, st.zsh);
       }
       if constexpr (C::BW == 4) {
         const u32x4 v = ld_nt(reinterpret_cast<const u32x4*>(p));
@@ -245,8 +253,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         const u32x4a4 v =
             ld_nt(reinterpret_cast<const u32x4a4*>(Q + (size_t)n * wpr + ks * 13 + w0));
         st.b[i] = u32x4{v[0], v[1], v[2], v[3]};
-        st.d[i] = (sel ? S2 : S)[(size_t)n * ng + (ks >> gshift)];
-        load_zero(sel ? Z2 : Z, (size_t)n * ng + (ks >> gshift), st.zw[i], st.zsh[i]);
+        st.d[i] = group_scale<CS>(sel ? S2 : S, (size_t)n, ng, ks >> gshift);
+        load_zero(sel ? Z2 : Z, (size_t)n, ks >> gshift, st.zw[i], st.zsh[i]);
       }
     }
   };
@@ -258,7 +266,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   Dq dq;  // int4: constants of the group of the last even step stored
   auto set_dq = [&](const St& st) {
     if constexpr (BMODE == 4) {
-      const uint32_t z = (st.zw >> st.zsh) & 0xffu;
+      const uint32_t z = (st.zw >> st.zsh) & ZMASK;
       dq.dh = h2{(_Float16)st.d, (_Float16)st.d};
       dq.ze = hv((0xE400u + z) * 0x00010001u);       // -(1024 + z)
       dq.zo = hv((0xD400u + 16u * z) * 0x00010001u);  // -(64 + z)
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const int id = tid + NT * i;
       const int r = id >> 2, qt = id & 3;
       const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
-      const float zf = (float)((st.zw[i] >> st.zsh[i]) & 0xffu);
+      const float zf = (float)((st.zw[i] >> st.zsh[i]) & ZMASK);
       const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
       h2 add[5];
 #pragma unroll
@@ -528,24 +536,24 @@ unsigned tiles_of(int M, int N, int bm, int bn) {
 }
 }  // namespace
 
-hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
-                       const uint8_t* zeros, int M, int N, int K, int bits, int group, __half* Y,
-                       hipStream_t st) {
+template <bool CS>
+hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
+                         int M, int N, int K, int bits, int group, __half* Y, hipStream_t st) {
   const int gshift = group_shift(group);
   const int wpr = words_per_row(K, bits, group);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   const unsigned cus = (unsigned)cu_n();
-  const bool zw = ((size_t)N * (size_t)(K / group)) % 4 == 0;
+  const bool zw = !CS && ((size_t)N * (size_t)(K / group)) % 4 == 0;
 #define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST, NB, NE)                                         \
   do {                                                                                          \
     if (zw)                                                                                     \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST>),                  \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST, CS>),              \
                          dim3(tiles_of(M, (NE) - (NB), BM, BN)), dim3(64 * WGM * WGN), 0, st, x, \
                          q, scales, zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr,        \
                          nullptr, nullptr, NB, NE);                                             \
     else                                                                                        \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST>),                 \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST, CS>),             \
                          dim3(tiles_of(M, (NE) - (NB), BM, BN)), dim3(64 * WGM * WGN), 0, st, x, \
                          q, scales, zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr,        \
                          nullptr, nullptr, NB, NE);                                             \
@@ -578,6 +586,13 @@ hipError_t launch_gemm(const __half* X, const uint32_t* q, const float* scales,
   }
 #undef AWQ_GEMM
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
+                       int M, int N, int K, int bits, int group, __half* Y, hipStream_t st,
+                       bool cs) {
+  return cs ? launch_gemm_t<true>(X, q, scales, zeros, M, N, K, bits, group, Y, st)
+            : launch_gemm_t<false>(X, q, scales, zeros, M, N, K, bits, group, Y, st);
 }
 
 // gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)), both products on one A tile

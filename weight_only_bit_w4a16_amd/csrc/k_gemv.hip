@@ -98,10 +98,10 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
-template <int MODE, int MP, int PF>
+template <int MODE, int MP, int PF, bool CS>
 __global__ __launch_bounds__(256) void gemv_w4_kernel(
-    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
+    const void* __restrict__ Z, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
     int rbw) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   extern __shared__ __align__(16) uint8_t smem[];
@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
       const int idx = min(base + (int)threadIdx.x + 256 * u, nsz - 1);
       const int r = idx / ngr, g = idx - r * ngr;
       const size_t n = (size_t)min((rb0 + (r >> 4)) * 16 + (r & 15), N - 1);
-      sv[u] = S[n * ngr + g];
-      zv[u] = Z[n * ngr + g];
+      sv[u] = group_scale<CS>(S, n, ngr, g);
+      zv[u] = (uint8_t)group_zero<CS>(Z, n, ngr, g);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -361,11 +361,11 @@ int cu_count() {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int SP, int RPF, bool FULL, bool DUAL>
+template <int SP, int RPF, bool FULL, bool DUAL, bool CS>
 __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
-    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
-    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int gshift) {
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
+    const void* __restrict__ Z, const uint32_t* __restrict__ Q2, const void* __restrict__ S2,
+    const void* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int gshift) {
   __shared__ u32x4 xs[SP][4][64];  // [piece][operand][lane]
   __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
   const int lane = threadIdx.x & 63;
@@ -535,15 +535,15 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
       }
       // refill the slots with the same pieces of the row RPF ahead
       const uint32_t* qn = (up2 ? qlane2 : qlane) + nn * wpr;
-      const float* sn = (up2 ? S2 : S) + nn * ngr;
-      const uint8_t* zn = (up2 ? Z2 : Z) + nn * ngr;
+      const void* sp = up2 ? S2 : S;
+      const void* zp = up2 ? Z2 : Z;
       // rows past this wavefront's last need no loads (uniform branch)
       if (row + RPF < items) {
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
           wb[r][s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
-          db[r][s] = sn[goff[s] >> gshift];
-          zb[r][s] = zn[goff[s] >> gshift];
+          db[r][s] = group_scale<CS>(sp, nn, ngr, goff[s] >> gshift);
+          zb[r][s] = group_zero<CS>(zp, nn, ngr, goff[s] >> gshift);
         }
       }
       // A no-op (wavefront-scope) fence after the loads: a memory-writing
@@ -589,11 +589,11 @@ __device__ __forceinline__ int w3_first_word(int jj) { return jj == 0 ? 0 : (jj 
 }  // namespace
 
 // DUAL: gate and up rows alternate in the ring as in the int4 kernel.
-template <int SP, int RPF, bool FULL, bool DUAL>
+template <int SP, int RPF, bool FULL, bool DUAL, bool CS>
 __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
-    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
-    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int wpr, int gshift) {
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
+    const void* __restrict__ Z, const uint32_t* __restrict__ Q2, const void* __restrict__ S2,
+    const void* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int wpr, int gshift) {
   __shared__ u32x4 xs[SP][5][64];  // [piece][operand][lane]
   __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
   const int lane = threadIdx.x & 63;
@@ -763,16 +763,16 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
         }
       }
       const uint32_t* qn = (up2 ? qlane2 : qlane) + nn * wpr;
-      const float* sn = (up2 ? S2 : S) + nn * ngr;
-      const uint8_t* zn = (up2 ? Z2 : Z) + nn * ngr;
+      const void* sp = up2 ? S2 : S;
+      const void* zp = up2 ? Z2 : Z;
       // rows past this wavefront's last need no loads (uniform branch)
       if (row + RPF < items) {
 #pragma unroll
         for (int s = 0; s < SP; ++s) {
           const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
           wb[r][s] = u32x4{v[0], v[1], v[2], v[3]};
-          db[r][s] = sn[goff[s] >> gshift];
-          zb[r][s] = zn[goff[s] >> gshift];
+          db[r][s] = group_scale<CS>(sp, nn, ngr, goff[s] >> gshift);
+          zb[r][s] = group_zero<CS>(zp, nn, ngr, goff[s] >> gshift);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -783,9 +783,10 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
   if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
 }
 
-hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* scales,
-                             const uint8_t* zeros, int N, int K, int group, __half* Y,
-                             hipStream_t st) {
+template <bool CS>
+hipError_t launch_gemv_w3_m1_t(const __half* X, const uint32_t* q, const void* scales,
+                               const void* zeros, int N, int K, int group, __half* Y,
+                               hipStream_t st) {
   const int nch = K / 128;
   const int sp = (nch + 15) / 16;
   if (sp > 6) return hipErrorNotSupported;
@@ -799,11 +800,11 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
 #define AWQ_W3(SM, RP)                                                                        \
   do {                                                                                        \
     if (full)                                                                                 \
-      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, false>), g1, block, 0, st, x, q,    \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, false, CS>), g1, block, 0, st, x, q, \
                          scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr, gshift);     \
     else                                                                                      \
-      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, false>), g1, block, 0, st, x, q,   \
-                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr, gshift);     \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, false, CS>), g1, block, 0, st, x,   \
+                         q, scales, zeros, nullptr, nullptr, nullptr, y, N, K, wpr, gshift);  \
   } while (0)
   switch (sp) {
     case 1: AWQ_W3(1, 4); break;
@@ -815,6 +816,13 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
   }
 #undef AWQ_W3
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int N, int K, int group, __half* Y, hipStream_t st,
+                             bool cs) {
+  return cs ? launch_gemv_w3_m1_t<true>(X, q, scales, zeros, N, K, group, Y, st)
+            : launch_gemv_w3_m1_t<false>(X, q, scales, zeros, N, K, group, Y, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -836,11 +844,11 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const float* sc
 // DUAL (gate and up of a gated MLP): the workgroup walks items 2j (gate row
 // block j, from Q/S/Z) and 2j + 1 (up row block j, from Q2/S2/Z2); the
 // gate sums wait in LDS and the up item stores fp16(silu(g) * u).
-template <int CPW, bool DUAL>
+template <int CPW, bool DUAL, bool CS>
 __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
-    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const float* __restrict__ S,
-    const uint8_t* __restrict__ Z, const uint32_t* __restrict__ Q2, const float* __restrict__ S2,
-    const uint8_t* __restrict__ Z2, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
+    const void* __restrict__ Z, const uint32_t* __restrict__ Q2, const void* __restrict__ S2,
+    const void* __restrict__ Z2, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
     int rbw) {
   static_assert(CPW % 4 == 0, "the ring of 4 chunks must tile a slice");
   extern __shared__ __align__(16) uint8_t smem[];
@@ -889,15 +897,15 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   float szv[SZI];
   uint8_t zzv[SZI];
   auto sz_load = [&](int it) {
-    const float* Sp = item_up(it) ? S2 : S;
-    const uint8_t* Zp = item_up(it) ? Z2 : Z;
+    const void* Sp = item_up(it) ? S2 : S;
+    const void* Zp = item_up(it) ? Z2 : Z;
 #pragma unroll
     for (int u = 0; u < SZI; ++u) {
       const int idx = min((int)threadIdx.x + (int)blockDim.x * u, szn - 1);
       const int r = idx / ngr, g = idx - r * ngr;
       const size_t n = (size_t)min(item_row(it) + r, N - 1);
-      szv[u] = Sp[n * ngr + g];
-      zzv[u] = Zp[n * ngr + g];
+      szv[u] = group_scale<CS>(Sp, n, ngr, g);
+      zzv[u] = (uint8_t)group_zero<CS>(Zp, n, ngr, g);
     }
   };
   auto sz_store = [&](int buf) {
@@ -1005,11 +1013,11 @@ constexpr size_t kLdsMax = 160 * 1024;  // LDS of one gfx950 compute unit
 constexpr int kGemvMaxRbw = 8;
 
 // raise a decode kernel's dynamic LDS limit once to the largest size used
-template <int MODE, int MP>
+template <int MODE, int MP, bool CS>
 hipError_t allow_lds(size_t lds) {
   static size_t allowed = 0;
   if (lds <= allowed) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute((const void*)gemv_w4_kernel<MODE, MP, kGemvPF>,
+  const hipError_t e = hipFuncSetAttribute((const void*)gemv_w4_kernel<MODE, MP, kGemvPF, CS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e == hipSuccess) allowed = lds;
   return e;
@@ -1017,10 +1025,11 @@ hipError_t allow_lds(size_t lds) {
 
 // 2 <= M <= 16: slices of CPW in {4, 8} chunks over at most 8 wavefronts
 // (K up to 8192; larger K does not fit the register budget)
-hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* scales,
-                             const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                             hipStream_t st, const uint32_t* q2, const float* scales2,
-                             const uint8_t* zeros2) {
+template <bool CS>
+hipError_t launch_gemv_w4_mx_t(const __half* X, const uint32_t* q, const void* scales,
+                               const void* zeros, int M, int N, int K, int group, __half* Y,
+                               hipStream_t st, const uint32_t* q2, const void* scales2,
+                               const void* zeros2) {
   const bool dual = q2 != nullptr;
   const int gshift = log2i(group / 128);
   const int nch = K / 128;
@@ -1037,9 +1046,9 @@ hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* sc
                      (dual ? 256 * 4 : 0) + (size_t)2 * 16 * ngr;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
-#define AWQ_MX(CP, DU)                                                                          \
-  hipLaunchKernelGGL((gemv_w4_mx_kernel<CP, DU>), grid, block, lds, st, x, q, scales, zeros, q2, \
-                     scales2, zeros2, y, M, N, K, gshift, rbw)
+#define AWQ_MX(CP, DU)                                                                        \
+  hipLaunchKernelGGL((gemv_w4_mx_kernel<CP, DU, CS>), grid, block, lds, st, x, q, scales, zeros, \
+                     q2, scales2, zeros2, y, M, N, K, gshift, rbw)
   if (cpw == 4) {
     if (dual) AWQ_MX(4, true);
     else AWQ_MX(4, false);
@@ -1051,9 +1060,20 @@ hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const float* sc
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scales,
-                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                          hipStream_t st, int variant) {
+hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st, const uint32_t* q2, const void* scales2,
+                             const void* zeros2, bool cs) {
+  return cs ? launch_gemv_w4_mx_t<true>(X, q, scales, zeros, M, N, K, group, Y, st, q2, scales2,
+                                        zeros2)
+            : launch_gemv_w4_mx_t<false>(X, q, scales, zeros, M, N, K, group, Y, st, q2, scales2,
+                                         zeros2);
+}
+
+template <bool CS>
+hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scales,
+                            const void* zeros, int M, int N, int K, int group, __half* Y,
+                            hipStream_t st, int variant) {
   const int gshift = log2i(group / 128);
   const int nrb = (N + 15) / 16;
   const int nch = K / 128;
@@ -1065,8 +1085,8 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   if (variant == 0 && M >= 2) {
-    const hipError_t e =
-        launch_gemv_w4_mx(X, q, scales, zeros, M, N, K, group, Y, st, nullptr, nullptr, nullptr);
+    const hipError_t e = launch_gemv_w4_mx_t<CS>(X, q, scales, zeros, M, N, K, group, Y, st,
+                                                 nullptr, nullptr, nullptr);
     if (e != hipErrorNotSupported) return e;
   }
   if (variant == 0 && M == 1) {
@@ -1082,11 +1102,11 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
 #define AWQ_M1(SM, RP)                                                                          \
   do {                                                                                          \
     if (full)                                                                                   \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, false>), g1, block, 0, st, x, q,     \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, false, CS>), g1, block, 0, st, x, q, \
                          scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);            \
     else                                                                                        \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, false>), g1, block, 0, st, x, q,    \
-                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);            \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, false, CS>), g1, block, 0, st, x,   \
+                         q, scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);         \
   } while (0)
     switch (sp) {
       case 1: AWQ_M1(1, 4); break;
@@ -1111,9 +1131,9 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
     if (lds <= kLdsMax) {
 #define AWQ_GV(MPV)                                                                              \
   do {                                                                                            \
-    const hipError_t ea = allow_lds<kOffset, MPV>(lds);                                          \
+    const hipError_t ea = allow_lds<kOffset, MPV, CS>(lds);                                      \
     if (ea != hipSuccess) return ea;                                                              \
-    hipLaunchKernelGGL((gemv_w4_kernel<kOffset, MPV, kGemvPF>), grid, block, lds, st, x, q,       \
+    hipLaunchKernelGGL((gemv_w4_kernel<kOffset, MPV, kGemvPF, CS>), grid, block, lds, st, x, q,   \
                        scales, zeros, y, M, N, K, gshift, rbw);                                   \
   } while (0)
       if (mp == 1) AWQ_GV(1);
@@ -1127,11 +1147,18 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const float* scale
   }
   const size_t lds = (size_t)rbw * 4 * 64 * 4 * 4 + sz;
   if (lds > kLdsMax) return hipErrorNotSupported;
-  const hipError_t ea = allow_lds<kExact, 16>(lds);
+  const hipError_t ea = allow_lds<kExact, 16, CS>(lds);
   if (ea != hipSuccess) return ea;
-  hipLaunchKernelGGL((gemv_w4_kernel<kExact, 16, kGemvPF>), grid, block, lds, st, x, q, scales,
-                     zeros, y, M, N, K, gshift, rbw);
+  hipLaunchKernelGGL((gemv_w4_kernel<kExact, 16, kGemvPF, CS>), grid, block, lds, st, x, q,
+                     scales, zeros, y, M, N, K, gshift, rbw);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const void* scales,
+                          const void* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st, int variant, bool cs) {
+  return cs ? launch_gemv_w4_t<true>(X, q, scales, zeros, M, N, K, group, Y, st, variant)
+            : launch_gemv_w4_t<false>(X, q, scales, zeros, M, N, K, group, Y, st, variant);
 }
 
 // Fused gate/up decode at M = 1, int4: Y = fp16(silu(X Wg^T) * (X Wu^T)).
@@ -1151,11 +1178,11 @@ hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float
 #define AWQ_GU(SM, RP)                                                                        \
   do {                                                                                        \
     if (full)                                                                                 \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, true>), g1, block, 0, st, x, qg, sg, \
-                         zg, qu, su, zu, y, N, K, gshift);                                    \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, true, false>), g1, block, 0, st, x,  \
+                         qg, sg, zg, qu, su, zu, y, N, K, gshift);                            \
     else                                                                                      \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, true>), g1, block, 0, st, x, qg,   \
-                         sg, zg, qu, su, zu, y, N, K, gshift);                                \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, true, false>), g1, block, 0, st, x, \
+                         qg, sg, zg, qu, su, zu, y, N, K, gshift);                            \
   } while (0)
   switch (sp) {
     case 1: AWQ_GU(1, 4); break;
@@ -1187,11 +1214,11 @@ hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float
 #define AWQ_GU3(SM, RP)                                                                       \
   do {                                                                                        \
     if (full)                                                                                 \
-      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, true>), g1, block, 0, st, x, qg,    \
-                         sg, zg, qu, su, zu, y, N, K, wpr, gshift);                           \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, true, true, false>), g1, block, 0, st, x,  \
+                         qg, sg, zg, qu, su, zu, y, N, K, wpr, gshift);                       \
     else                                                                                      \
-      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, true>), g1, block, 0, st, x, qg,   \
-                         sg, zg, qu, su, zu, y, N, K, wpr, gshift);                           \
+      hipLaunchKernelGGL((gemv_w3_m1_kernel<SM, RP, false, true, false>), g1, block, 0, st, x, \
+                         qg, sg, zg, qu, su, zu, y, N, K, wpr, gshift);                       \
   } while (0)
   switch (sp) {
     case 1: AWQ_GU3(1, 4); break;

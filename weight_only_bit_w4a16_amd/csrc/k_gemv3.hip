@@ -58,11 +58,11 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 }  // namespace
 
-template <int MR>
+template <int MR, bool CS>
 __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict__ X,
                                                       const uint32_t* __restrict__ Q,
-                                                      const float* __restrict__ S,
-                                                      const uint8_t* __restrict__ Z,
+                                                      const void* __restrict__ S,
+                                                      const void* __restrict__ Z,
                                                       uint16_t* __restrict__ Y, int M, int N,
                                                       int K, int wpr, int RB, int gshift) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -91,8 +91,8 @@ __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict
       const uint32_t* qg = Q + n * wpr + 13 * g;
 #pragma unroll
       for (int k = 0; k < 13; ++k) wv[u][k] = ld_nt(qg + k);
-      dl[u] = S[n * ngr + (g >> gshift)];
-      zl[u] = Z[n * ngr + (g >> gshift)];
+      dl[u] = group_scale<CS>(S, n, ngr, g >> gshift);
+      zl[u] = group_zero<CS>(Z, n, ngr, g >> gshift);
     }
   };
   // the first pass's weights are in flight while the activations are prepared
@@ -216,9 +216,10 @@ int cus() {
 }
 }  // namespace
 
-hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scales,
-                          const uint8_t* zeros, int M, int N, int K, int group, __half* Y,
-                          hipStream_t st) {
+template <bool CS>
+hipError_t launch_gemv_w3_t(const __half* X, const uint32_t* q, const void* scales,
+                            const void* zeros, int M, int N, int K, int group, __half* Y,
+                            hipStream_t st) {
   if (M > kGemvW3MaxM) return hipErrorNotSupported;
   const int gshift = group_shift(group);
   const int ng = K / 128;
@@ -234,15 +235,22 @@ hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const float* scale
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   if (mr == 1)
-    hipLaunchKernelGGL((gemv_w3_kernel<1>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
+    hipLaunchKernelGGL((gemv_w3_kernel<1, CS>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
                        wpr, RB, gshift);
   else if (mr == 2)
-    hipLaunchKernelGGL((gemv_w3_kernel<2>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
+    hipLaunchKernelGGL((gemv_w3_kernel<2, CS>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
                        wpr, RB, gshift);
   else
-    hipLaunchKernelGGL((gemv_w3_kernel<4>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
+    hipLaunchKernelGGL((gemv_w3_kernel<4, CS>), grid, block, lds, st, x, q, scales, zeros, y, M, N, K,
                        wpr, RB, gshift);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const void* scales,
+                          const void* zeros, int M, int N, int K, int group, __half* Y,
+                          hipStream_t st, bool cs) {
+  return cs ? launch_gemv_w3_t<true>(X, q, scales, zeros, M, N, K, group, Y, st)
+            : launch_gemv_w3_t<false>(X, q, scales, zeros, M, N, K, group, Y, st);
 }
 
 }  // namespace awq

@@ -240,6 +240,39 @@ hipError_t launch_quant_pack(const __half* W, const float* s, int N, int K, int 
 }
 
 // ---------------------------------------------------------------------------
+// Compact group parameters: steps rounded to fp16, zero points as 4-bit
+// fields, 8 per uint32 word in group order; one thread per zero-point word.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void compact_params_kernel(const float* __restrict__ S,
+                                                             const uint8_t* __restrict__ Z, int N,
+                                                             int ng, uint16_t* __restrict__ S16,
+                                                             uint32_t* __restrict__ Z4) {
+  const int zw = (ng + 7) >> 3;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)N * zw) return;
+  const size_t n = (size_t)(i / zw);
+  const int w = (int)(i % zw);
+  uint32_t word = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int g = 8 * w + u;
+    if (g < ng) {
+      word |= ((uint32_t)Z[n * ng + g] & 15u) << (4 * u);
+      S16[n * ng + g] = __half_as_ushort(__float2half_rn(S[n * ng + g]));
+    }
+  }
+  Z4[i] = word;
+}
+
+hipError_t launch_compact_params(const float* scales, const uint8_t* zeros, int N, int ng,
+                                 uint16_t* scales16, uint32_t* zeros4, hipStream_t st) {
+  const long items = (long)N * ((ng + 7) / 8);
+  hipLaunchKernelGGL(compact_params_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                     st, scales, zeros, N, ng, scales16, zeros4);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // X' = fp16(float32(X) / s), 8 elements per thread, the quotient correctly
 // rounded to fp32 and then to fp16. x * (1/s) with the hardware reciprocal is
 // within 2 ulp (fp32) of the correctly rounded quotient, so it rounds to the
