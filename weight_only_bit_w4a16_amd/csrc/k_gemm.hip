@@ -636,14 +636,36 @@ hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float*
 // ||A B^T||_F^2 as one float64 partial per workgroup tile; A is [M, K] fp16,
 // B is [N, K] fp16, or with hilo [N, 2K] holding hi and lo parts per
 // 128-wide k chunk (then the product is A (Bhi + Blo)^T)
+namespace {
+// 256 x 256 tiles when one round of them is shorter than the rounds of
+// 128 x 128 tiles it replaces (a big tile does 4 small tiles' work at about
+// 4/3 of their speed: half the operand traffic per flop)
+bool sqnorm_big(int M, int N) {
+  const unsigned cus = (unsigned)cu_n();
+  const unsigned big = tiles_of(M, N, 256, 256), small = tiles_of(M, N, 128, 128);
+  const double t_big = 3.0 * (double)((big + cus - 1) / cus);
+  const double t_small = 1.0 * (double)((small + cus - 1) / cus);
+  return t_big < t_small;
+}
+}  // namespace
+
 hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N, int K, bool hilo,
                              double* partial, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false, 2>), dim3(tiles_of(M, N, 128, 128)),
-                     dim3(256), 0, st, A, B, nullptr, nullptr, M, N, K, 0, 0, nullptr, partial,
-                     hilo ? 1 : 0, nullptr, nullptr, nullptr, 0, N);
+  if (sqnorm_big(M, N))
+    hipLaunchKernelGGL((gemm_kernel<0, 1, 256, 256, 2, 4, false, 2>),
+                       dim3(tiles_of(M, N, 256, 256)), dim3(512), 0, st, A, B, nullptr, nullptr,
+                       M, N, K, 0, 0, nullptr, partial, hilo ? 1 : 0, nullptr, nullptr, nullptr, 0,
+                       N);
+  else
+    hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false, 2>),
+                       dim3(tiles_of(M, N, 128, 128)), dim3(256), 0, st, A, B, nullptr, nullptr,
+                       M, N, K, 0, 0, nullptr, partial, hilo ? 1 : 0, nullptr, nullptr, nullptr, 0,
+                       N);
   return hipGetLastError();
 }
 
-unsigned sqnorm_abt_tiles(int M, int N) { return tiles_of(M, N, 128, 128); }
+unsigned sqnorm_abt_tiles(int M, int N) {
+  return sqnorm_big(M, N) ? tiles_of(M, N, 256, 256) : tiles_of(M, N, 128, 128);
+}
 
 }  // namespace awq
