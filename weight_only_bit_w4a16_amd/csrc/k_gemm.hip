@@ -65,6 +65,11 @@ struct Cfg {
   static constexpr int BCH = BN * BK / 8 / NT;         // 16-byte fp16 B chunks per thread
   static constexpr int BW = BN * 8 / NT;               // int4 B words per thread
   static constexpr int BIT = BN * 4 / NT;              // int3 B (row, quarter) items per thread
+  // every thread loads whole items of both operands
+  static_assert(BM * BK % (8 * NT) == 0 && ACH >= 1, "A chunks per thread");
+  static_assert(BMODE != 0 || (BN * BK % (8 * NT) == 0 && BCH >= 1), "fp16 B chunks per thread");
+  static_assert(BMODE != 4 || (BN * 8 % NT == 0 && BW >= 1), "int4 B words per thread");
+  static_assert(BMODE != 3 || (BN * 4 % NT == 0 && BIT >= 1), "int3 B items per thread");
 };
 
 // register staging of one K step
@@ -581,6 +586,11 @@ hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales,
     } else {
       AWQ_GEMM(4, 64, 64, 2, 2, 4, 0, N);
     }
+  } else if (tiles_of(M, N, 128, 128) * 2 >= cus) {
+    // 8 wavefronts of 32 x 64 (one B item per thread) once the 128 x 128
+    // tiles fill half the compute units (measured: 256 x 4096 x 11008 in
+    // 62 us against 77 us on 64 x 64 tiles; 2048 x 4096 x 11008 382 / 548 us)
+    AWQ_GEMM(3, 128, 128, 4, 2, 4, 0, N);
   } else {
     AWQ_GEMM(3, 64, 64, 2, 2, 4, 0, N);
   }
