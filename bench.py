@@ -141,7 +141,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    rec = {"search": [], "pack": [], "fold": [], "prefill": [], "decode": [], "decode_batch": []}
+    rec = {"search": [], "pack": [], "fold": [], "prefill": [], "decode_batch": []}
 
     def step(i, timed):
         e = {k: (ev(), ev()) for k in ("search", "pack", "fold", "prefill")}
@@ -160,30 +160,17 @@ def main():
         awq.w4a16_matmul(Xpf, *dst, w.bits, w.group, out=Yp)
         e["prefill"][1].record(stream)
         # decode on every copy but the one just written (cold in the caches):
-        # even steps replay a captured graph of DEC_REPS passes over the R-1
-        # copies between one event pair (the graph's own start-up is spread
-        # over that many launches), odd steps launch the R-1 calls one by one
-        # with an event pair each
-        dec = []
+        # a captured graph of DEC_REPS passes over the R-1 copies between one
+        # event pair (the graph's own start-up is spread over that many
+        # launches)
         ba, bb = ev(), ev()
         ba.record(stream)
-        if i % 2 == 0:
-            graphs[i % R].replay()
-        else:
-            for r in range(1, R):
-                q = copies[(i + r) % R]
-                a, b = ev(), ev()
-                a.record(stream)
-                awq.w4a16_matmul(X1f, *q, w.bits, w.group, out=Y1)
-                b.record(stream)
-                dec.append((a, b))
+        graphs[i % R].replay()
         bb.record(stream)
         if timed:
             for k in e:
                 rec[k].append(e[k])
-            rec["decode"].extend(dec)
-            if i % 2 == 0:
-                rec["decode_batch"].append((ba, bb))
+            rec["decode_batch"].append((ba, bb))
         return best
 
     if args.copy_calibration:
@@ -252,7 +239,6 @@ def main():
             return float("nan"), float("nan")
         return float(np.mean(v)), float(np.min(v))
 
-    dec_call_ms, dec_min = mean_ms("decode")
     dec_ms = mean_ms("decode_batch")[0] / (DEC_REPS * (R - 1))
     pre_ms, pre_min = mean_ms("prefill")
     search_ms, _ = mean_ms("search")
@@ -294,8 +280,6 @@ def main():
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "decode GEMV (M=1)", "bytes_per_launch": dec_bytes,
             "mean_us": round(dec_ms * 1e3, 2),
-            "per_call_event_mean_us": None if dec_call_ms != dec_call_ms else round(dec_call_ms * 1e3, 2),
-            "per_call_event_min_us": None if dec_min != dec_min else round(dec_min * 1e3, 2),
         },
         "roofline_prefill": {
             "bound": "mfma", "achieved": round(pre_tfs, 1), "peak": FP16_MFMA_PEAK_TF,
