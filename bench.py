@@ -213,6 +213,37 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # context, outside the timed steps: the same layer unquantized, torch's
+    # fp16 F.linear (hipBLASLt) on the fp16 W, as a black box. The pages'
+    # only speed figure is a >3x gain of 4-bit kernels over a 16-bit
+    # baseline; the ratio of the two decode times is its kernel-level analog.
+    # (One fp16 copy: part of it stays in the 256 MB cache between calls,
+    # which favours the fp16 side.)
+    Xh = X1.clone()
+    lin = torch.cuda.CUDAGraph()
+    for _ in range(3):
+        torch.nn.functional.linear(Xh, W)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(lin):
+        for _ in range(16):
+            torch.nn.functional.linear(Xh, W)
+    lin_dec = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record(stream)
+        lin.replay()
+        b.record(stream)
+        lin_dec.append((a, b))
+    lin_pre = []
+    for _ in range(3):
+        a, b = ev(), ev()
+        a.record(stream)
+        torch.nn.functional.linear(Xp, W)
+        b.record(stream)
+        lin_pre.append((a, b))
+    torch.cuda.synchronize()
+    del lin
+
     # fused gated-MLP product (gate and up of the same shape), outside the
     # timed steps: M = 1 on pairs of cold copies, then the prefill batch
     gu_dec, gu_pre = [], []
@@ -256,6 +287,8 @@ def main():
     gu_dec_ms = float(np.mean([a.elapsed_time(b) / n for a, b, n in gu_dec[1:]]))
     gu_pre_ms = float(np.mean([a.elapsed_time(b) / n for a, b, n in gu_pre[1:]]))
     gu_dec_bytes = 2 * packed_bytes + 2 * M_dec * w.K + 2 * M_dec * w.N
+    lin_dec_ms = float(np.mean([a.elapsed_time(b) / 16 for a, b in lin_dec[1:]]))
+    lin_pre_ms = float(np.mean([a.elapsed_time(b) for a, b in lin_pre[1:]]))
 
     out = {
         "metric": "W4A16 GEMV effective HBM GB/s (% peak) at M=1; prefill GEMM TFLOP/s (% MFMA)",
@@ -286,6 +319,13 @@ def main():
             "unit": "TFLOP/s", "frac": round(pre_tfs / FP16_MFMA_PEAK_TF, 4),
             "kernel": f"prefill GEMM (M={M_pre})", "flops_per_launch": pre_flops,
             "mean_us": round(pre_ms * 1e3, 1),
+        },
+        "context_fp16_linear": {
+            "what": "torch F.linear on the fp16 W of the same layer (hipBLASLt), black box",
+            "decode_M1_us": round(lin_dec_ms * 1e3, 2),
+            "decode_speedup_w4a16_over_fp16": round(lin_dec_ms / dec_ms, 2),
+            "prefill_us": round(lin_pre_ms * 1e3, 1),
+            "prefill_tflops": round(pre_flops / (lin_pre_ms * 1e-3) / 1e12, 1),
         },
         "gate_up_silu": {
             "what": "fp16(silu(X' Wg^T) * (X' Wu^T)), two matrices of the workload's shape",
