@@ -178,6 +178,38 @@ def test_decode_int4_larger_groups(group):
         assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, group, K))
 
 
+@pytest.mark.parametrize("M", [2, 5, 8, 16])
+@pytest.mark.parametrize("N,K,group", [(33, 8320, 128), (70, 11008, 128), (20, 16512, 128),
+                                       (18, 28672, 128), (40, 8704, 512), (24, 16384, 256)])
+def test_decode_int4_long_k(M, N, K, group):
+    """K over 8192 at 2 <= M <= 16: the decode kernel covers K in passes
+    (65, 86, 129 and 224 chunks: 2, 2, 3 and 4 passes; 68 chunks in groups
+    of 512: the second pass starts inside a group)."""
+    say("decode int4 long K", M, N, K, group)
+    W = datagen.random_f16((N, K), 0.02, seed=N + K)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 5)
+    X = datagen.random_f16((M, K), 1.0, seed=M + K)
+    q, sc, z = _packed(W, s, 4, group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group))
+    qo, so, zo = O.quantize_pack(W, s, 4, group)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, group, K))
+
+
+def test_decode_int4_long_k_many_row_blocks():
+    """Several row blocks per workgroup over two passes (N = 8200 gives 513
+    row blocks); every row of a sample checked."""
+    N, K, M = 8200, 11008, 8
+    say("decode int4 long K, many row blocks")
+    W = datagen.random_f16((N, K), 0.02, seed=3)
+    X = datagen.random_f16((M, K), 1.0, seed=4)
+    q, sc, z = _packed(W, None, 4, 128)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z))
+    rows = np.concatenate([np.arange(0, 48), sample_rows(N), np.arange(N - 40, N)])
+    rows = np.unique(rows)
+    qo, so, zo = O.quantize_pack(W[rows], None, 4, 128)
+    assert_rows_close(Y[:, rows], O.matmul(X, qo, so, zo, 4, 128, K))
+
+
 def test_decode_deterministic():
     W = datagen.random_f16((300, 4096), 0.02, seed=1)
     X = datagen.random_f16((1, 4096), 1.0, seed=2)

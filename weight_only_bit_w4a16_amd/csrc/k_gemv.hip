@@ -826,83 +826,101 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* sca
 }
 
 // ---------------------------------------------------------------------------
-// Decode, int4, 2 <= M <= 16 (gemv_w4_mx_kernel). A workgroup of WV <= 8
-// wavefronts splits K into WV slices of CPW 128-code chunks; wavefront s
-// keeps the activation operands of its slice (all token rows, MFMA A
-// layout, prepared once) in registers and streams row block after row block
-// (16 weight rows) against them, so the MFMA work does not grow with M and
-// the activations are read once per workgroup. Lane (n, q) = (l % 16, l / 16)
-// loads codes 32q .. 32q + 31 of a chunk of row n (16 bytes); the four
-// 16x16x32 MFMAs of a chunk take word t of every lane, so one chunk gives
-// the 16 rows x 16 token rows of one quantization group. Offset form as in
-// gemv_w4_kernel: even slots (1024 + c) and odd slots (1024 + 16 c) are
-// contracted separately, and C = 1024 sum(x even) + 64 sum(x odd) and
-// z * S, S = sum(x), are removed per chunk and token. Weights stream
-// through a 4-chunk register ring that runs across row blocks; the scales
-// and zero points of the next row block are staged in LDS meanwhile, and
-// the slices' partial sums of a row block are added in LDS in a fixed order.
-// DUAL (gate and up of a gated MLP): the workgroup walks items 2j (gate row
-// block j, from Q/S/Z) and 2j + 1 (up row block j, from Q2/S2/Z2); the
-// gate sums wait in LDS and the up item stores fp16(silu(g) * u).
-template <int CPW, bool DUAL, bool CS>
+// Decode, int4, 2 <= M <= 16 (gemv_w4_mx_kernel). K is covered in NP passes
+// of PC 128-code chunks (one pass unless K > 8192). In a pass a workgroup of
+// WV <= 8 wavefronts splits the pass's chunks into WV slices of CPW chunks;
+// wavefront s keeps the activation operands of its slice (all token rows,
+// MFMA A layout, prepared at the start of the pass) in registers and streams
+// row block after row block (16 weight rows) against them, so the MFMA work
+// does not grow with M and the activations are read once per workgroup.
+// Lane (n, q) = (l % 16, l / 16) loads codes 32q .. 32q + 31 of a chunk of
+// row n (16 bytes); the four 16x16x32 MFMAs of a chunk take word t of every
+// lane, so one chunk gives the 16 rows x 16 token rows of one quantization
+// group. Offset form as in gemv_w4_kernel: even slots (1024 + c) and odd
+// slots (1024 + 16 c) are contracted separately, and C = 1024 sum(x even) +
+// 64 sum(x odd) and z * S, S = sum(x), are removed per chunk and token.
+// Weights stream through a 4-chunk register ring that runs across row blocks
+// and passes; the scales and zero points of the next item are staged in LDS
+// meanwhile, and the slices' partial sums of a row block are added in LDS in
+// a fixed order (then, over the passes, in pass order).
+// DUAL (gate and up of a gated MLP, one pass): the workgroup walks items 2j
+// (gate row block j, from Q/S/Z) and 2j + 1 (up row block j, from
+// Q2/S2/Z2); the gate sums wait in LDS and the up item stores
+// fp16(silu(g) * u). MP: more than one pass (the single-pass form keeps the
+// pass logic out of the loop).
+template <int CPW, bool DUAL, bool CS, bool MP>
 __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
     const void* __restrict__ Z, const uint32_t* __restrict__ Q2, const void* __restrict__ S2,
     const void* __restrict__ Z2, uint16_t* __restrict__ Y, int M, int N, int K, int gshift,
-    int rbw) {
+    int rbw, int pc) {
   static_assert(CPW % 4 == 0, "the ring of 4 chunks must tile a slice");
+  static_assert(!(MP && DUAL), "the gated form runs in one pass");
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int WV = blockDim.x >> 6;
   const int nl = lane & 15, q = lane >> 4;
   const int nch = K >> 7;
+  const int np = MP ? (nch + pc - 1) / pc : 1;  // passes over K
   const int ngr = max(1, nch >> gshift);
+  // groups one pass touches at most (its first one is gbase(pass))
+  const int gpp = MP ? min(ngr, ((pc + (1 << gshift) - 1) >> gshift) + 1) : ngr;
   const int wpr = K >> 3;
   const int nrb = (N + 15) >> 4;
   const int rb0 = blockIdx.x * rbw;
   const int nj = min(rbw, nrb - rb0);
-  const int nit = DUAL ? 2 * nj : nj;  // items: row blocks, or gate/up row block pairs
-  const int cbeg = wave * CPW;
+  const int nb = DUAL ? 2 * nj : nj;  // items of a pass: row blocks, or gate/up pairs
+  const int nit = np * nb;
 
   float2* csx = reinterpret_cast<float2*>(smem);                  // [nch][16] (C, S)
-  float* szf = reinterpret_cast<float*>(csx + (size_t)nch * 16);  // [2][16][ngr] scales
-  float* part = szf + 2 * 16 * ngr;                               // [2][WV][4][64] partials
+  float* szf = reinterpret_cast<float*>(csx + (size_t)nch * 16);  // [2][16][gpp] scales
+  float* part = szf + 2 * 16 * gpp;                               // [2][WV][4][64] partials
   float* gsum = part + 2 * WV * 256;                              // [256] DUAL gate sums
-  uint8_t* szb = reinterpret_cast<uint8_t*>(gsum + (DUAL ? 256 : 0));  // [2][16][ngr] zeros
+  float* pacc = gsum + (DUAL ? 256 : 0);                          // [nj][256] earlier passes
+  uint8_t* szb = reinterpret_cast<uint8_t*>(pacc + (MP ? nj * 256 : 0));  // [2][16][gpp]
 
-  // first row of item it's row block, and whether it reads the up matrix
+  // item it (clamped to the last): pass, first row of its row block, and
+  // whether it reads the up matrix
+  auto item_pass = [&](int it) { return MP ? min(it, nit - 1) / nb : 0; };
   auto item_row = [&](int it) {
-    const int c = min(it, nit - 1);
+    const int c = MP ? min(it, nit - 1) % nb : min(it, nit - 1);
     return (rb0 + (DUAL ? c >> 1 : c)) * 16;
   };
   auto item_up = [&](int it) { return DUAL && (min(it, nit - 1) & 1) != 0; };
+  // chunks of pass p: [p pc, pend(p)); this wavefront's slice starts at cbeg(p)
+  auto pend = [&](int p) { return MP ? min((p + 1) * pc, nch) : nch; };
+  auto cbeg = [&](int p) { return (MP ? p * pc : 0) + wave * CPW; };
 
   // ---- weight ring: 4 chunks ahead, across items ----------------------------
+  // chunk i of the slice of item it; slots past the pass re-read its last chunk
   const uint32_t* qlane = Q + 4 * q;
   const uint32_t* qlane2 = DUAL ? Q2 + 4 * q : qlane;
-  auto wload = [&](int it, int i) {  // chunk i of the slice, item it
+  auto wload = [&](int it, int i) {
+    const int p = item_pass(it);
     const size_t n = (size_t)min(item_row(it) + nl, N - 1);
-    const int c = min(cbeg + i, nch - 1);
+    const int c = min(cbeg(p) + i, pend(p) - 1);
     return ld_nt(reinterpret_cast<const u32x4*>((item_up(it) ? qlane2 : qlane) + n * wpr + c * 16));
   };
   u32x4 ring[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) ring[i] = wload(0, i);
 
-  // ---- scales and zero points of row block j: loaded into registers, then
-  // stored to LDS buffer j & 1 ------------------------------------------------
-  const int szn = 16 * ngr;  // values per row block
-  constexpr int SZI = 3;     // per thread: 16 * 96 / 512 (K up to 12288)
+  // ---- scales and zero points of item it (the groups of its pass): loaded
+  // into registers, then stored to LDS buffer it & 1 --------------------------
+  const int szn = 16 * gpp;  // values per item
+  constexpr int SZI = 3;     // per thread (the launcher checks szn <= 3 * threads)
   float szv[SZI];
   uint8_t zzv[SZI];
   auto sz_load = [&](int it) {
     const void* Sp = item_up(it) ? S2 : S;
     const void* Zp = item_up(it) ? Z2 : Z;
+    const int gb = MP ? (item_pass(it) * pc) >> gshift : 0;
 #pragma unroll
     for (int u = 0; u < SZI; ++u) {
       const int idx = min((int)threadIdx.x + (int)blockDim.x * u, szn - 1);
-      const int r = idx / ngr, g = idx - r * ngr;
+      const int r = idx / gpp;
+      const int g = min(gb + idx - r * gpp, ngr - 1);
       const size_t n = (size_t)min(item_row(it) + r, N - 1);
       szv[u] = group_scale<CS>(Sp, n, ngr, g);
       zzv[u] = (uint8_t)group_zero<CS>(Zp, n, ngr, g);
@@ -920,29 +938,33 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   };
   sz_load(0);
 
-  // ---- activation operands of this slice (token row nl) and C, S ----------
+  // ---- activation operands of this slice of pass p (token row nl) and C, S
   u32x4 av[CPW][4];
+  auto prep = [&](int p) {
+    const int ce = pend(p);
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int c = cbeg + i;
-    const bool ok = c < nch && nl < M;
-    uint32_t d[16];
-    load_x32(X + (size_t)min(nl, M - 1) * K + min(c, nch - 1) * 128 + 32 * q, d);
+    for (int i = 0; i < CPW; ++i) {
+      const int c = cbeg(p) + i;
+      const bool ok = c < ce && nl < M;
+      uint32_t d[16];
+      load_x32(X + (size_t)min(nl, M - 1) * K + min(c, ce - 1) * 128 + 32 * q, d);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) d[t] = ok ? d[t] : 0u;
-    permute_x32(d, av[i][0], av[i][1], av[i][2], av[i][3]);
-    float se = 0.f, so = 0.f;
+      for (int t = 0; t < 16; ++t) d[t] = ok ? d[t] : 0u;
+      permute_x32(d, av[i][0], av[i][1], av[i][2], av[i][3]);
+      float se = 0.f, so = 0.f;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      se += h2f((uint16_t)(d[t] & 0xffffu));
-      so += h2f((uint16_t)(d[t] >> 16));
+      for (int t = 0; t < 16; ++t) {
+        se += h2f((uint16_t)(d[t] & 0xffffu));
+        so += h2f((uint16_t)(d[t] >> 16));
+      }
+      se += __shfl_xor(se, 16);
+      so += __shfl_xor(so, 16);
+      se += __shfl_xor(se, 32);
+      so += __shfl_xor(so, 32);
+      if (q == 0 && c < ce) csx[c * 16 + nl] = make_float2(1024.f * se + 64.f * so, se + so);
     }
-    se += __shfl_xor(se, 16);
-    so += __shfl_xor(so, 16);
-    se += __shfl_xor(se, 32);
-    so += __shfl_xor(so, 32);
-    if (q == 0 && c < nch) csx[c * 16 + nl] = make_float2(1024.f * se + 64.f * so, se + so);
-  }
+  };
+  prep(0);
   sz_store(0);
   __syncthreads();
 
@@ -950,15 +972,20 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nit; ++j) {  // j: item
     const int buf = j & 1;
+    const int p = MP ? j / nb : 0, jj = j - p * nb;
+    if (MP && jj == 0 && p > 0) {  // uniform: a new pass (csx of its chunks
+      prep(p);                     // is written and read by the same wavefront)
+    }
     if (j + 1 < nit) sz_load(j + 1);  // uniform
+    const int cb = cbeg(p), ce = pend(p), gb = MP ? (p * pc) >> gshift : 0;
     floatx4 y = zero4;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const u32x4 w = ring[i & 3];
-      // refill: chunk i + 4 of this row block or the next one's
+      // refill: chunk i + 4 of this item or the next one's
       ring[i & 3] = i + 4 < CPW ? wload(j, i + 4) : wload(j + 1, i + 4 - CPW);
-      const int c = cbeg + i;
-      if (c < nch) {  // uniform
+      const int c = cb + i;
+      if (c < ce) {  // uniform
         uint32_t e[8], o[8];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -973,7 +1000,7 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
                                   mfma16(av[i][0], u32x4{e[0], e[1], e[2], e[3]}, zero4));
         const floatx4 dd = mfma16(av[i][3], u32x4{o[4], o[5], o[6], o[7]},
                                   mfma16(av[i][2], u32x4{o[0], o[1], o[2], o[3]}, zero4));
-        const int gi = nl * ngr + (c >> gshift);
+        const int gi = nl * gpp + (c >> gshift) - gb;
         const float dl = szf[buf * szn + gi];
         const float zf = (float)szb[buf * szn + gi];
 #pragma unroll
@@ -988,12 +1015,21 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
     for (int r = 0; r < 4; ++r) part[((buf * WV + wave) * 4 + r) * 64 + lane] = y[r];
     if (j + 1 < nit) sz_store(buf ^ 1);
     __syncthreads();
-    // slices' partials of item j, added in slice order (thread t always
-    // handles the same entries, so a gate sum is read back by its writer)
+    // slices' partials of item j, added in slice order, then over the passes
+    // in pass order (thread t always handles the same entries, so gate sums
+    // and earlier passes' sums are read back by their writer)
     for (int t = threadIdx.x; t < 256; t += blockDim.x) {
       const int l = t & 63, r = t >> 6;
       float v = 0.f;
       for (int w = 0; w < WV; ++w) v += part[((buf * WV + w) * 4 + r) * 64 + l];
+      if constexpr (MP) {
+        float* pa = pacc + jj * 256 + t;
+        if (p > 0) v = *pa + v;
+        if (p < np - 1) {
+          *pa = v;
+          continue;
+        }
+      }
       const int m = 4 * (l >> 4) + r;
       const int n = item_row(j) + (l & 15);
       if constexpr (DUAL) {
@@ -1023,8 +1059,8 @@ hipError_t allow_lds(size_t lds) {
   return e;
 }
 
-// 2 <= M <= 16: slices of CPW in {4, 8} chunks over at most 8 wavefronts
-// (K up to 8192; larger K does not fit the register budget)
+// 2 <= M <= 16: passes of at most 64 chunks (K 8192), each in slices of
+// CPW in {4, 8} chunks over at most 8 wavefronts
 template <bool CS>
 hipError_t launch_gemv_w4_mx_t(const __half* X, const uint32_t* q, const void* scales,
                                const void* zeros, int M, int N, int K, int group, __half* Y,
@@ -1033,28 +1069,37 @@ hipError_t launch_gemv_w4_mx_t(const __half* X, const uint32_t* q, const void* s
   const bool dual = q2 != nullptr;
   const int gshift = log2i(group / 128);
   const int nch = K / 128;
-  const int cpw = 4 * (((nch + 7) / 8 + 3) / 4);
-  if (cpw > 8) return hipErrorNotSupported;
-  const int wv = (nch + cpw - 1) / cpw;
+  const int np = (nch + 63) / 64;
+  if (dual && np > 1) return hipErrorNotSupported;
+  const int pc = (nch + np - 1) / np;
+  const int cpw = pc <= 32 ? 4 : 8;
+  const int wv = (pc + cpw - 1) / cpw;
   const int ngr = max(1, nch >> gshift);
+  const int gpp = np > 1 ? min(ngr, ((pc + (1 << gshift) - 1) >> gshift) + 1) : ngr;
+  if (16 * gpp > 3 * 64 * wv) return hipErrorNotSupported;  // scale staging per thread
   const int nrb = (N + 15) / 16;
   // one workgroup of 8 wavefronts fills a compute unit at this register use
   const int resident = cu_count() * (wv <= 4 ? 8 / wv : 1);
   const int rbw = (nrb + resident - 1) / resident;
   const dim3 grid((unsigned)((nrb + rbw - 1) / rbw)), block((unsigned)(64 * wv));
-  const size_t lds = (size_t)nch * 16 * 8 + (size_t)2 * 16 * ngr * 4 + (size_t)2 * wv * 256 * 4 +
-                     (dual ? 256 * 4 : 0) + (size_t)2 * 16 * ngr;
+  const size_t lds = (size_t)nch * 16 * 8 + (size_t)2 * 16 * gpp * 4 + (size_t)2 * wv * 256 * 4 +
+                     (dual ? 256 * 4 : 0) + (np > 1 ? (size_t)rbw * 256 * 4 : 0) +
+                     (size_t)2 * 16 * gpp;
+  if (lds > 64 * 1024) return hipErrorNotSupported;  // the kernels' default LDS limit
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
-#define AWQ_MX(CP, DU)                                                                        \
-  hipLaunchKernelGGL((gemv_w4_mx_kernel<CP, DU, CS>), grid, block, lds, st, x, q, scales, zeros, \
-                     q2, scales2, zeros2, y, M, N, K, gshift, rbw)
-  if (cpw == 4) {
-    if (dual) AWQ_MX(4, true);
-    else AWQ_MX(4, false);
+#define AWQ_MX(CP, DU, MPV)                                                                      \
+  hipLaunchKernelGGL((gemv_w4_mx_kernel<CP, DU, CS, MPV>), grid, block, lds, st, x, q, scales,    \
+                     zeros, q2, scales2, zeros2, y, M, N, K, gshift, rbw, pc)
+  if (np > 1) {
+    if (cpw == 4) AWQ_MX(4, false, true);
+    else AWQ_MX(8, false, true);
+  } else if (cpw == 4) {
+    if (dual) AWQ_MX(4, true, false);
+    else AWQ_MX(4, false, false);
   } else {
-    if (dual) AWQ_MX(8, true);
-    else AWQ_MX(8, false);
+    if (dual) AWQ_MX(8, true, false);
+    else AWQ_MX(8, false, false);
   }
 #undef AWQ_MX
   return hipGetLastError();
