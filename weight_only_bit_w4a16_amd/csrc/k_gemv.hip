@@ -1139,8 +1139,9 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
     // wavefronts: all resident, at most 64 rows each; 2 per SIMD, or 3 when
     // the registers allow it (up to 4 pieces) and every wavefront still gets
     // 5 or more rows (measured: 3 per SIMD is 2-4% faster there and slower
-    // for fewer rows or longer rows)
-    const int wpc = sp <= 4 && N >= 5 * 8 * cu_count() ? 12 : 8;
+    // for fewer rows or longer rows); rows of 2 pieces: 4 per SIMD with a
+    // ring of one row (measured 10-12% faster than 2-3 per SIMD with two)
+    const int wpc = sp == 2 ? 16 : (sp <= 4 && N >= 5 * 8 * cu_count() ? 12 : 8);
     const int nw = max(cu_count() * wpc, (N + 63) / 64);
     const dim3 g1((unsigned)((min(N, nw) + 3) / 4));
     const bool full = nch % 16 == 0;
@@ -1155,7 +1156,7 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
   } while (0)
     switch (sp) {
       case 1: AWQ_M1(1, 4); break;
-      case 2: AWQ_M1(2, 2); break;
+      case 2: AWQ_M1(2, 1); break;
       case 3: AWQ_M1(3, 2); break;
       case 4: AWQ_M1(4, 1); break;
       case 5: AWQ_M1(5, 1); break;
