@@ -903,8 +903,6 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
     return ld_nt(reinterpret_cast<const u32x4*>((item_up(it) ? qlane2 : qlane) + n * wpr + c * 16));
   };
   u32x4 ring[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ring[i] = wload(0, i);
 
   // ---- scales and zero points of item it (the groups of its pass): loaded
   // into registers, then stored to LDS buffer it & 1 --------------------------
@@ -936,18 +934,34 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
       }
     }
   };
-  sz_load(0);
-
-  // ---- activation operands of this slice of pass p (token row nl) and C, S
+  // ---- activation operands of this slice of pass p (token row nl) and C, S:
+  // prep loads and permutes chunk by chunk (LD), or permutes in place the raw
+  // activations that xload put in av
   u32x4 av[CPW][4];
-  auto prep = [&](int p) {
+  auto xload = [&](int p) {
+    const int ce = pend(p);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = cbeg(p) + i;
+      const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)min(nl, M - 1) * K +
+                                                        min(c, ce - 1) * 128 + 32 * q);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) av[i][t] = src[t];
+    }
+  };
+  auto prep = [&](int p, auto LD) {
     const int ce = pend(p);
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = cbeg(p) + i;
       const bool ok = c < ce && nl < M;
       uint32_t d[16];
-      load_x32(X + (size_t)min(nl, M - 1) * K + min(c, ce - 1) * 128 + 32 * q, d);
+      if constexpr (LD.value) {
+        load_x32(X + (size_t)min(nl, M - 1) * K + min(c, ce - 1) * 128 + 32 * q, d);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) d[t] = av[i][t >> 2][t & 3];
+      }
 #pragma unroll
       for (int t = 0; t < 16; ++t) d[t] = ok ? d[t] : 0u;
       permute_x32(d, av[i][0], av[i][1], av[i][2], av[i][3]);
@@ -964,7 +978,20 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
       if (q == 0 && c < ce) csx[c * 16 + nl] = make_float2(1024.f * se + 64.f * so, se + so);
     }
   };
-  prep(0);
+  // one pass: the activations and the first item's scales first (the prep
+  // and the barrier wait for them; the weight ring streams meanwhile).
+  // Several passes: the ring first (that order needs fewer registers there)
+  if constexpr (!MP) {
+    xload(0);
+    sz_load(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ring[i] = wload(0, i);
+  if constexpr (MP) sz_load(0);
+  // keep the prep's arithmetic below every load (hoisted, it waits for the
+  // first chunk before the other loads are issued)
+  if constexpr (!MP) __builtin_amdgcn_sched_barrier(0);
+  prep(0, std::integral_constant<bool, MP>{});
   sz_store(0);
   __syncthreads();
 
@@ -974,7 +1001,7 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
     const int buf = j & 1;
     const int p = MP ? j / nb : 0, jj = j - p * nb;
     if (MP && jj == 0 && p > 0) {  // uniform: a new pass (csx of its chunks
-      prep(p);                     // is written and read by the same wavefront)
+      prep(p, std::true_type{});   // is written and read by the same wavefront)
     }
     if (j + 1 < nit) sz_load(j + 1);  // uniform
     const int cb = cbeg(p), ce = pend(p), gb = MP ? (p * pc) >> gshift : 0;
