@@ -166,6 +166,28 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
                                    const uint8_t* zeros, int M, int N, int K, int bits, int group,
                                    uint16_t* Y, int kernel, void* stream);
 
+/* Bytes of device workspace with which awq_w4a16_matmul_ws splits the K
+ * range of this product over several workgroups per output tile (0: the
+ * shape runs without splitting, or the arguments are invalid). Splitting is
+ * used when even the smallest prefill tiles leave compute units idle: M
+ * beyond the decode range with few output tiles (for example M = 17..256 on
+ * a 4096-wide layer). */
+size_t awq_w4a16_matmul_workspace_bytes(int M, int N, int K, int bits, int group);
+
+/* awq_w4a16_matmul with a workspace (same arithmetic contract). With a
+ * split, every split writes its float32 sums over its part of K to its own
+ * [M, N] plane of the workspace and a second kernel adds the planes in split
+ * order, so the result does not depend on timing. workspace: dev, 16-byte
+ * aligned, at least awq_w4a16_matmul_workspace_bytes(M, N, K, bits, group)
+ * bytes, any contents, owned by the caller; calls that share a workspace
+ * must be ordered on one stream. NULL runs without splitting; a non-NULL
+ * workspace that is too small returns AWQ_ERR_WORKSPACE. Asynchronous on
+ * `stream`. */
+awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                               const uint8_t* zeros, int M, int N, int K, int bits, int group,
+                               uint16_t* Y, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* The gate and up projections of a gated MLP fused into one call (hungho77
  * blog -- "Why the engine is part of the method": the speed-up comes from
  * kernels that fuse operators). Both projections read the same activation

@@ -99,6 +99,46 @@ def test_matmul_validation():
     assert _mm(kernel=1, bits=3, M=5) == E.AWQ_ERR_UNSUPPORTED
 
 
+def test_matmul_workspace_plan():
+    """The split plan on a 256-compute-unit part (the count assumed without a
+    device): tiles 128 wide and 32, 64 or 128 tall, split over K until about
+    one workgroup per unit; decode shapes and shapes that fill the part need
+    none. Bytes: one float32 [M, N] plane per split."""
+    h = awq.lib()
+    W = h.awq_w4a16_matmul_workspace_bytes
+    assert W(16, 4096, 4096, 4, 128) == 0  # decode kernel
+    assert W(4, 4096, 4096, 3, 128) == 0
+    assert W(2048, 28672, 8192, 4, 128) == 0  # whole rounds of big tiles
+    assert W(256, 11008, 4096, 3, 128) == 0  # 172 tiles of 128 x 128: no split
+    # int4, M = 32: 32 tiles of 32 x 128, 8 splits of 8 steps (64 codes each)
+    assert W(32, 4096, 4096, 4, 128) == 8 * 32 * 4096 * 4
+    # int3, M = 64: 32 tiles of 64 x 128; 86 steps of 128 codes in 8 splits
+    assert W(64, 4096, 11008, 3, 128) == 8 * 64 * 4096 * 4
+    # M = 256: 64 tiles of 128 x 128 in 4 splits
+    assert W(256, 4096, 11008, 3, 128) == 4 * 256 * 4096 * 4
+    # few steps: at least 8 per split (K = 512: 8 steps, no split)
+    assert W(32, 256, 512, 4, 128) == 0
+    assert W(32, 4096, 4096, 5, 128) == 0  # invalid
+    assert W(0, 4096, 4096, 4, 128) == 0
+
+
+def test_matmul_ws_validation():
+    h = awq.lib()
+    E = _lib
+    need = h.awq_w4a16_matmul_workspace_bytes(32, 4096, 4096, 4, 128)
+
+    def ws(w, nbytes, M=32):
+        return h.awq_w4a16_matmul_ws(P, P, P, P, M, 4096, 4096, 4, 128, P2, w, nbytes, NULL)
+
+    assert ws(P, need - 16) == E.AWQ_ERR_WORKSPACE
+    assert ws(MIS, need) == E.AWQ_ERR_INVALID_ARG
+    import torch
+    if not torch.cuda.is_available():  # valid requests: no device to run them
+        assert ws(P, need) == E.AWQ_ERR_NO_DEVICE
+        assert ws(NULL, 0) == E.AWQ_ERR_NO_DEVICE
+        assert ws(P, 0, M=8) == E.AWQ_ERR_NO_DEVICE  # decode shapes ignore the workspace
+
+
 def test_valid_calls_without_device_report_no_device():
     import torch
     if torch.cuda.is_available():

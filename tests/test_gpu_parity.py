@@ -305,6 +305,52 @@ def test_prefill_split_tail():
     assert_rows_close(Y[:, cols], O.matmul_rows(X, qo, so, zo, 4, 128, K, cols))
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("M,N,K,group", [(17, 4096, 4096, 128), (64, 1000, 4096, 128),
+                                         (100, 2048, 11008, 128), (32, 4096, 3072, 256),
+                                         (40, 3000, 4096, -1)])
+def test_prefill_split_k(bits, M, N, K, group):
+    """M x N too small to fill the compute units: the K range is split over
+    several workgroups per tile, whose float32 sums meet in a workspace
+    (ragged M and N, a last split shorter than the others, larger groups and
+    one group per row). Checked against the oracle, and repeated bit for bit
+    (the splits are added in a fixed order) on a workspace that held stale
+    values."""
+    say("prefill split K", bits, M, N, K, group)
+    g = K if group == -1 else group
+    W = datagen.random_f16((N, K), 0.02, seed=M + N + bits)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 7)
+    X = datagen.random_f16((M, K), 1.0, seed=M + 3)
+    q, sc, z = _packed(W, s, bits, group)
+    nb = awq.matmul_workspace_bytes(M, N, K, bits, group)
+    assert nb > 0
+    ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+    Y1 = host(awq.w4a16_matmul(dev(X), q, sc, z, bits, group, workspace=ws))
+    ws.fill_(0x5A)
+    Y2 = host(awq.w4a16_matmul(dev(X), q, sc, z, bits, group, workspace=ws))
+    assert_same_bits(Y1, Y2)
+    qo, so, zo = O.quantize_pack(W, s, bits, g)
+    assert_rows_close(Y1, O.matmul(X, qo, so, zo, bits, g, K))
+
+
+def test_prefill_split_k_then_other_shapes():
+    """One workspace serves calls of different shapes in a row (and the
+    automatic per-stream workspace of the binding too)."""
+    K = 4096
+    ws = torch.empty(awq.matmul_workspace_bytes(64, 4096, K, 4, 128), dtype=torch.uint8,
+                     device="cuda")
+    for M, N in [(64, 4096), (20, 1500), (64, 4096), (33, 640)]:
+        W = datagen.random_f16((N, K), 0.02, seed=N)
+        X = datagen.random_f16((M, K), 1.0, seed=M)
+        q, sc, z = _packed(W, None, 4, 128)
+        assert awq.matmul_workspace_bytes(M, N, K, 4, 128) <= ws.numel()
+        Y = host(awq.w4a16_matmul(dev(X), q, sc, z, workspace=ws))
+        Ya = host(awq.w4a16_matmul(dev(X), q, sc, z))
+        assert_same_bits(Y, Ya)
+        qo, so, zo = O.quantize_pack(W, None, 4, 128)
+        assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, 128, K))
+
+
 def _prefill_cases():
     return [(name, M) for name, w in datagen.WORKLOADS.items() for M in w.prefill_M]
 

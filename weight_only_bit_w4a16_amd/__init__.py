@@ -132,9 +132,35 @@ def fold_inv_scale(X, s, out=None, stream=None):
     return y
 
 
+_MATMUL_WS = {}
+
+
+def matmul_workspace_bytes(M: int, N: int, K: int, bits: int = 4, group: int = 128) -> int:
+    """Bytes of workspace with which the product splits K for this shape (0: no split)."""
+    return int(lib().awq_w4a16_matmul_workspace_bytes(M, N, K, bits, group))
+
+
+def _matmul_workspace(device, stream_handle, nbytes: int):
+    """A workspace of at least nbytes for calls on this device and stream,
+    kept for reuse."""
+    torch = _torch()
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           int(getattr(stream_handle, "value", stream_handle) or 0))
+    ws = _MATMUL_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _MATMUL_WS[key] = ws
+    return ws
+
+
 def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, out=None,
-                 kernel: int = KERNEL_AUTO, stream=None):
-    """Y = X' dequant(Q)^T (fp16 [M, N]) with X' already divided by s."""
+                 kernel: int = KERNEL_AUTO, stream=None, workspace=None):
+    """Y = X' dequant(Q)^T (fp16 [M, N]) with X' already divided by s.
+
+    With the automatic kernel choice, shapes that split K (small M x N
+    beyond the decode range) use `workspace` (a uint8 device tensor of at
+    least matmul_workspace_bytes(...) bytes, shared only by calls ordered on
+    one stream) or, when None, one kept per device and stream."""
     torch = _torch()
     _need(Xp, "Xp", torch.float16, 2)
     _need(qpacked, "qpacked", torch.int32, 2)
@@ -150,8 +176,15 @@ def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, ou
     y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
     st = _stream(stream)
     if kernel == KERNEL_AUTO:
-        r = lib().awq_w4a16_matmul(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M, N, K,
-                                   bits, group, _ptr(y), st)
+        nb = matmul_workspace_bytes(M, N, K, bits, group)
+        if nb:
+            ws = _matmul_workspace(Xp.device, st, nb) if workspace is None else workspace
+            _need(ws, "workspace", torch.uint8, 1)
+            r = lib().awq_w4a16_matmul_ws(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M,
+                                          N, K, bits, group, _ptr(y), _ptr(ws), ws.numel(), st)
+        else:
+            r = lib().awq_w4a16_matmul(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M, N,
+                                       K, bits, group, _ptr(y), st)
     else:
         r = lib().awq_w4a16_matmul_kernel(_ptr(Xp), _ptr(qpacked), _ptr(scales), _ptr(zeros), M,
                                           N, K, bits, group, _ptr(y), kernel, st)

@@ -52,9 +52,13 @@ awq_status check_group(int K, int bits, int group, int* g_out) {
   return AWQ_OK;
 }
 
+// whether the automatic choice runs this shape on a decode kernel
+bool auto_decode(int M, int bits) { return bits == 4 ? M <= 16 : M <= awq::kGemvW3MaxM; }
+
 awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* scales,
                        const void* zeros, int M, int N, int K, int bits, int group, uint16_t* Y,
-                       void* stream, int kernel, bool cs) {
+                       void* stream, int kernel, bool cs, void* ws = nullptr,
+                       size_t ws_bytes = 0) {
   if (!X || !qpacked || !scales || !zeros || !Y) return AWQ_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(qpacked) || !aligned16(scales) || !aligned16(zeros) ||
@@ -68,15 +72,16 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* s
   if ((kernel == 1 || kernel == 2) && (M > 16 || (bits == 3 && M > awq::kGemvW3MaxM)))
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == 2 && bits == 3) return AWQ_ERR_UNSUPPORTED;
+  if (ws != nullptr && !aligned16(ws)) return AWQ_ERR_INVALID_ARG;
+  const bool decode = kernel == 1 || kernel == 2 || (kernel == 0 && auto_decode(M, bits));
+  if (ws != nullptr && !decode && ws_bytes < awq::gemm_workspace_bytes(M, N, K, bits))
+    return AWQ_ERR_WORKSPACE;
   st = device_ready();
   if (st != AWQ_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const __half* x = reinterpret_cast<const __half*>(X);
   __half* y = reinterpret_cast<__half*>(Y);
-  const bool decode =
-      kernel == 1 || kernel == 2 ||
-      (kernel == 0 && (bits == 4 ? M <= 16 : M <= awq::kGemvW3MaxM));
   hipError_t e;
   if (decode) {
     if (bits == 4)
@@ -97,7 +102,7 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* s
       e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s, cs);
     }
   } else {
-    e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s, cs);
+    e = awq::launch_gemm(x, qpacked, scales, zeros, M, N, K, bits, g, y, s, cs, ws, ws_bytes);
   }
   return from_hip(e);
 }
@@ -196,6 +201,21 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
                                    const uint8_t* zeros, int M, int N, int K, int bits, int group,
                                    uint16_t* Y, int kernel, void* stream) {
   return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, kernel, false);
+}
+
+size_t awq_w4a16_matmul_workspace_bytes(int M, int N, int K, int bits, int group) {
+  int g = 0;
+  if (M <= 0 || N <= 0 || check_group(K, bits, group, &g) != AWQ_OK) return 0;
+  if (auto_decode(M, bits)) return 0;
+  return awq::gemm_workspace_bytes(M, N, K, bits);
+}
+
+awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const float* scales,
+                               const uint8_t* zeros, int M, int N, int K, int bits, int group,
+                               uint16_t* Y, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, 0, false,
+                     workspace, workspace_bytes);
 }
 
 awq_status awq_compact_group_params(const float* scales, const uint8_t* zeros, int N, int K,

@@ -67,7 +67,11 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* sca
 // prefill (any M)
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
                        int M, int N, int K, int bits, int group, __half* Y, hipStream_t st,
-                       bool cs);
+                       bool cs,
+                       void* ws = nullptr, size_t ws_bytes = 0);
+// bytes of workspace the prefill product uses to split K for this shape (0:
+// it does not split)
+size_t gemm_workspace_bytes(int M, int N, int K, int bits);
 // decode, int4, 2 <= M <= 16, K <= 8192 (NotSupported otherwise); with q2
 // set, the gated-MLP form silu(X Wq^T) * (X Wq2^T)
 hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const void* scales,

@@ -118,13 +118,14 @@ struct Dq {
 // Word loads keep the loop-carried value 32 bits wide, so no byte
 // extension is scheduled ahead of the MFMAs (it would wait on the newest
 // loads).
-template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW, int NST, bool CS = false>
+template <int BMODE, int EPI, int BM, int BN, int WGM, int WGN, bool ZW, int NST, bool CS = false,
+          bool SK = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const uint16_t* __restrict__ A, const void* __restrict__ Bsrc, const void* __restrict__ S,
     const void* __restrict__ Z, int M, int N, int K, int wpr, int gshift,
     uint16_t* __restrict__ Y, double* __restrict__ partial, int hilo,
     const void* __restrict__ B2, const void* __restrict__ S2, const void* __restrict__ Z2,
-    int nbase, int nend) {
+    int nbase, int nend, float* __restrict__ ws, int spl) {
   constexpr int NT = 64 * WGM * WGN;
   static_assert(NST == 2 || NST == 4, "register stages");
   using C = Cfg<BMODE, BM, BN, NT>;
@@ -157,7 +158,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // fp16 B with hilo set holds each term as a hi and a lo fp16 part,
   // [N][2K]: 256-wide block c = (hi of k 128c..128c+127 | lo of the same k),
   // so a 64-wide step s reads activations 128*(s/4) + 64*(s%2)
-  const int nsteps = BMODE == 0 && hilo ? 2 * (K / BK) : K / BK;
+  // split K (EPI 0, gridDim.y > 1): this workgroup takes steps
+  // [kofs, kofs + nsteps) of its tile; partial tiles meet in the workspace
+  const int nsteps_all = BMODE == 0 && hilo ? 2 * (K / BK) : K / BK;
+  static_assert(!SK || EPI == 0, "split K stores plain products");
+  const int nsplit = SK ? (int)gridDim.y : 1;
+  const int kofs = nsplit > 1 ? (int)blockIdx.y * spl : 0;
+  const int nsteps = nsplit > 1 ? min(spl, nsteps_all - kofs) : nsteps_all;
   const int ng = max(1, K >> (7 + gshift));  // quantization groups per row
 
   if (BMODE == 3) {
@@ -197,6 +204,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // load step ks into st; for int4, SZ says whether this (even) step also
   // loads its group's scale and zero point
   auto load_step = [&](St& st, int ks, auto SZ) {
+    ks += kofs;
     {
       const int ka = BMODE == 0 && hilo ? 128 * (ks >> 2) + 64 * (ks & 1) : BK * ks;
 #pragma unroll
@@ -470,6 +478,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // D layout of the 32x32 MFMA: lane l holds column l % 32, rows
   // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15
   if constexpr (EPI == 0) {
+    if (SK && nsplit > 1) {
+      // Split K: this split's float32 products go to plane blockIdx.y of the
+      // workspace ([split][M][N]); split_reduce_kernel adds the planes
+      float* plane = ws + (size_t)blockIdx.y * M * N;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + (BN / WGN) * wn + 32 * j + lr;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m =
+                m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (m < M && n < nend) plane[(size_t)m * N + n] = acc[i][j][v];
+          }
+        }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -541,36 +567,121 @@ unsigned tiles_of(int M, int N, int bm, int bn) {
 }
 }  // namespace
 
+namespace {
+// The launch plan of the W4A16 / W3A16 product. Without a workspace: the
+// largest tile that still gives every compute unit work (int4 256 x 256 with
+// a 128 x 256 tail, or 128 x 128, or 64 x 64; int3 128 x 128 or 64 x 64).
+// When even 128 x 128 tiles leave compute units idle (small M x N) and a
+// workspace is given, the K range splits over `splits` workgroups per tile
+// (`spl` steps each, at least 8) so that about one workgroup per compute unit
+// runs, on tiles as tall as M needs (32 (int4) or 64 rows, else 128) and 128
+// wide: a tile re-reads its activation rows for every 128 outputs instead of
+// every 64, and no rows past M are loaded and multiplied for nothing. Each
+// split writes its float32 products to its own [M, N] plane of the
+// workspace, and a second kernel adds the planes in split order.
+struct GemmPlan {
+  int bm, bn;    // tile
+  int splits;    // K splits (1: none)
+  int spl;       // steps per split
+  unsigned tiles;
+};
+
+GemmPlan gemm_plan(int M, int N, int K, int bits, bool can_split) {
+  const unsigned cus = (unsigned)cu_n();
+  GemmPlan p{64, 64, 1, 0, 0};
+  if (bits == 4) {
+    if (tiles_of(M, N, 256, 256) >= cus) p.bm = p.bn = 256;
+    else if (tiles_of(M, N, 128, 128) >= cus) p.bm = p.bn = 128;
+  } else if (tiles_of(M, N, 128, 128) * 2 >= cus) {
+    p.bm = p.bn = 128;
+  }
+  const int nsteps = K / (bits == 3 ? 128 : 64);
+  if (can_split && tiles_of(M, N, 128, 128) * 2 <= cus) {
+    const int bm = M <= 32 && bits == 4 ? 32 : (M <= 64 ? 64 : 128);
+    const unsigned tiles = tiles_of(M, N, bm, 128);
+    const int s = min((int)(cus / tiles), max(1, nsteps / 8));
+    if (s > 1) {
+      int spl = (nsteps + s - 1) / s;
+      if (bits == 4) spl = (spl + 1) & ~1;  // int4 splits start on a group
+      p = GemmPlan{bm, 128, (nsteps + spl - 1) / spl, spl, tiles};
+    }
+  }
+  if (p.splits == 1) p.tiles = tiles_of(M, N, p.bm, p.bn);
+  return p;
+}
+
+size_t plan_workspace_bytes(const GemmPlan& p, int M, int N) {
+  return p.splits <= 1 ? 0 : (size_t)p.splits * M * N * 4;
+}
+
+// Y = fp16(sum of the split planes), added in split order
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws, int S,
+                                                           size_t MN, uint16_t* __restrict__ Y) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= MN) return;
+  float sum = ws[e];
+  for (int sp = 1; sp < S; ++sp) sum += ws[(size_t)sp * MN + e];
+  Y[e] = __half_as_ushort(__float2half_rn(sum));
+}
+}  // namespace
+
+size_t gemm_workspace_bytes(int M, int N, int K, int bits) {
+  return plan_workspace_bytes(gemm_plan(M, N, K, bits, true), M, N);
+}
+
+namespace {
 template <bool CS>
 hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
-                         int M, int N, int K, int bits, int group, __half* Y, hipStream_t st) {
+                         int M, int N, int K, int bits, int group, __half* Y, hipStream_t st,
+                         void* ws, size_t ws_bytes) {
   const int gshift = group_shift(group);
   const int wpr = words_per_row(K, bits, group);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
   const unsigned cus = (unsigned)cu_n();
   const bool zw = !CS && ((size_t)N * (size_t)(K / group)) % 4 == 0;
-#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST, NB, NE)                                         \
+  const GemmPlan plan = gemm_plan(M, N, K, bits, ws != nullptr);
+  if (plan.splits > 1 && ws_bytes < plan_workspace_bytes(plan, M, N)) return hipErrorInvalidValue;
+  float* wsf = plan.splits > 1 ? static_cast<float*>(ws) : nullptr;
+  const unsigned nsp = (unsigned)plan.splits;
+#define AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, NB, NE, SKV)                                   \
   do {                                                                                          \
+    const dim3 grid(tiles_of(M, (NE) - (NB), BM, BN), nsp);                                     \
     if (zw)                                                                                     \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST, CS>),              \
-                         dim3(tiles_of(M, (NE) - (NB), BM, BN)), dim3(64 * WGM * WGN), 0, st, x, \
-                         q, scales, zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr,        \
-                         nullptr, nullptr, NB, NE);                                             \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST, CS, SKV>), grid,   \
+                         dim3(64 * WGM * WGN), 0, st, x, q, scales, zeros, M, N, K, wpr, gshift, \
+                         y, nullptr, 0, nullptr, nullptr, nullptr, NB, NE, wsf, plan.spl);      \
     else                                                                                        \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST, CS>),             \
-                         dim3(tiles_of(M, (NE) - (NB), BM, BN)), dim3(64 * WGM * WGN), 0, st, x, \
-                         q, scales, zeros, M, N, K, wpr, gshift, y, nullptr, 0, nullptr,        \
-                         nullptr, nullptr, NB, NE);                                             \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST, CS, SKV>), grid,  \
+                         dim3(64 * WGM * WGN), 0, st, x, q, scales, zeros, M, N, K, wpr, gshift, \
+                         y, nullptr, 0, nullptr, nullptr, nullptr, NB, NE, wsf, plan.spl);      \
   } while (0)
-  if (bits == 4) {
-    // the largest tile that still gives every compute unit work
-    const unsigned big = tiles_of(M, N, 256, 256);
-    if (big >= cus) {
+#define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST, NB, NE) \
+  AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, NB, NE, false)
+#define AWQ_GEMM_S(BMODE, BM, BN, WGM, WGN, NST) AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, 0, N, true)
+  if (plan.splits > 1) {
+    // split K: int4 32 x 128 (4 wavefronts of 32 x 32), 64 x 128 (2 x 2 of
+    // 32 x 64) or 128 x 128 tiles
+    if (bits == 4) {
+      if (plan.bm == 32) AWQ_GEMM_S(4, 32, 128, 1, 4, 4);
+      else if (plan.bm == 64) AWQ_GEMM_S(4, 64, 128, 2, 2, 4);
+      else AWQ_GEMM_S(4, 128, 128, 2, 2, 4);
+    } else {
+      // int3 on 8 wavefronts, one B item per thread (two put the register
+      // stages in scratch memory): 64 x 128 also serves M <= 32
+      if (plan.bm == 128) AWQ_GEMM_S(3, 128, 128, 4, 2, 4);
+      else AWQ_GEMM_S(3, 64, 128, 2, 4, 4);
+    }
+    const size_t mn = (size_t)M * N;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
+                       wsf, plan.splits, mn, y);
+  } else if (bits == 4) {
+    if (plan.bm == 256) {
       // Whole rounds of 256 x 256 tiles (one per compute unit each), and the
       // columns past them on 128 x 256 tiles when those fit in one round:
       // a partial last round of big tiles would leave compute units idle for
       // a whole tile time, the small tiles take about half of it.
+      const unsigned big = plan.tiles;
       const int mt = (M + 255) / 256;
       const int nsplit = (int)((big / cus) * cus / (unsigned)mt) * 256;
       const bool split = big % cus != 0 && nsplit > 0 && nsplit < N &&
@@ -581,12 +692,12 @@ hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales,
       } else {
         AWQ_GEMM(4, 256, 256, 2, 4, 2, 0, N);
       }
-    } else if (tiles_of(M, N, 128, 128) >= cus) {
+    } else if (plan.bm == 128) {
       AWQ_GEMM(4, 128, 128, 2, 2, 4, 0, N);
     } else {
       AWQ_GEMM(4, 64, 64, 2, 2, 4, 0, N);
     }
-  } else if (tiles_of(M, N, 128, 128) * 2 >= cus) {
+  } else if (plan.bm == 128) {
     // 8 wavefronts of 32 x 64 (one B item per thread) once the 128 x 128
     // tiles fill half the compute units (measured: 256 x 4096 x 11008 in
     // 62 us against 77 us on 64 x 64 tiles; 2048 x 4096 x 11008 382 / 548 us)
@@ -594,15 +705,18 @@ hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales,
   } else {
     AWQ_GEMM(3, 64, 64, 2, 2, 4, 0, N);
   }
+#undef AWQ_GEMM_S
 #undef AWQ_GEMM
+#undef AWQ_GEMM_K
   return hipGetLastError();
 }
+}  // namespace
 
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
                        int M, int N, int K, int bits, int group, __half* Y, hipStream_t st,
-                       bool cs) {
-  return cs ? launch_gemm_t<true>(X, q, scales, zeros, M, N, K, bits, group, Y, st)
-            : launch_gemm_t<false>(X, q, scales, zeros, M, N, K, bits, group, Y, st);
+                       bool cs, void* ws, size_t ws_bytes) {
+  return cs ? launch_gemm_t<true>(X, q, scales, zeros, M, N, K, bits, group, Y, st, ws, ws_bytes)
+            : launch_gemm_t<false>(X, q, scales, zeros, M, N, K, bits, group, Y, st, ws, ws_bytes);
 }
 
 // gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)), both products on one A tile
@@ -621,11 +735,11 @@ hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float*
     if (zw)                                                                                       \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 2, BM, BN, WGM, WGN, true, NST>),                    \
                          dim3(tiles_of(M, N, BM, BN / 2)), dim3(64 * WGM * WGN), 0, st, x, qg, sg, \
-                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N);              \
+                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N, nullptr, 0);  \
     else                                                                                          \
       hipLaunchKernelGGL((gemm_kernel<BMODE, 2, BM, BN, WGM, WGN, false, NST>),                   \
                          dim3(tiles_of(M, N, BM, BN / 2)), dim3(64 * WGM * WGN), 0, st, x, qg, sg, \
-                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N);              \
+                         zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N, nullptr, 0);  \
   } while (0)
   if (bits == 4) {
     if (tiles_of(M, N, 256, 128) >= cus)
@@ -665,12 +779,12 @@ hipError_t launch_sqnorm_abt(const uint16_t* A, const uint16_t* B, int M, int N,
     hipLaunchKernelGGL((gemm_kernel<0, 1, 256, 256, 2, 4, false, 2>),
                        dim3(tiles_of(M, N, 256, 256)), dim3(512), 0, st, A, B, nullptr, nullptr,
                        M, N, K, 0, 0, nullptr, partial, hilo ? 1 : 0, nullptr, nullptr, nullptr, 0,
-                       N);
+                       N, nullptr, 0);
   else
     hipLaunchKernelGGL((gemm_kernel<0, 1, 128, 128, 2, 2, false, 2>),
                        dim3(tiles_of(M, N, 128, 128)), dim3(256), 0, st, A, B, nullptr, nullptr,
                        M, N, K, 0, 0, nullptr, partial, hilo ? 1 : 0, nullptr, nullptr, nullptr, 0,
-                       N);
+                       N, nullptr, 0);
   return hipGetLastError();
 }
 
