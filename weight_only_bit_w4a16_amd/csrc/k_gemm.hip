@@ -94,6 +94,15 @@ struct Stage<3, BM, BN, NT> {
   uint32_t zw[Cfg<3, BM, BN, NT>::BIT], zsh[Cfg<3, BM, BN, NT>::BIT];
 };
 
+// f(integral_constant<int, i>) for i = I .. N-1, in order
+template <int I, int N, typename F>
+__device__ __forceinline__ void unroll_c(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll_c<I + 1, N>(f);
+  }
+}
+
 // int4 dequantization constants of one (row, group): fp16 delta and the
 // offsets -(1024 + z), -(64 + z) that turn magic-number halves into c - z
 struct Dq {
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const void* __restrict__ B2, const void* __restrict__ S2, const void* __restrict__ Z2,
     int nbase, int nend, float* __restrict__ ws, int spl) {
   constexpr int NT = 64 * WGM * WGN;
-  static_assert(NST == 2 || NST == 4, "register stages");
+  static_assert(NST == 2 || NST == 4 || NST == 8, "register stages");
   using C = Cfg<BMODE, BM, BN, NT>;
   using St = Stage<BMODE, BM, BN, NT>;
   constexpr int STR = C::STR;
@@ -440,12 +449,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     constexpr int i = decltype(I)::value;
     load_step(stg[i], min(i, last), std::integral_constant<bool, BMODE == 4 && i % 2 == 0>{});
   };
-  prime(std::integral_constant<int, 0>{});
-  prime(std::integral_constant<int, 1>{});
-  if constexpr (NST == 4) {
-    prime(std::integral_constant<int, 2>{});
-    prime(std::integral_constant<int, 3>{});
-  }
+  unroll_c<0, NST>(prime);
   set_dq(stg[0]);
   store_all(stg[0], 0);
   load_step(stg[0], min(NST, last), std::integral_constant<bool, BMODE == 4>{});
@@ -460,20 +464,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   // full groups: no branch inside the loop body, so the compiler keeps the
   // in-flight loads counted exactly across the back edge
   int ks = 0;
-  for (; ks + NST <= nsteps; ks += NST) {
-    sub(ks, std::integral_constant<int, 0>{});
-    sub(ks, std::integral_constant<int, 1>{});
-    if constexpr (NST == 4) {
-      sub(ks, std::integral_constant<int, 2>{});
-      sub(ks, std::integral_constant<int, 3>{});
-    }
-  }
+  for (; ks + NST <= nsteps; ks += NST) unroll_c<0, NST>([&](auto U) { sub(ks, U); });
   // the last nsteps % NST steps (uniform branches)
-  if (ks < nsteps) sub(ks, std::integral_constant<int, 0>{});
-  if constexpr (NST == 4) {
-    if (ks + 1 < nsteps) sub(ks, std::integral_constant<int, 1>{});
-    if (ks + 2 < nsteps) sub(ks, std::integral_constant<int, 2>{});
-  }
+  unroll_c<0, NST - 1>([&](auto U) {
+    if (ks + decltype(U)::value < nsteps) sub(ks, U);
+  });
 
   // D layout of the 32x32 MFMA: lane l holds column l % 32, rows
   // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15
@@ -571,7 +566,7 @@ namespace {
 // The launch plan of the W4A16 / W3A16 product. Without a workspace: the
 // largest tile that still gives every compute unit work (int4 256 x 256 with
 // a 128 x 256 tail, or 128 x 128, or 64 x 64; int3 128 x 128 or 64 x 64).
-// When even 128 x 128 tiles leave compute units idle (small M x N) and a
+// When the tiles leave compute units idle (small M x N; see gemm_plan) and a
 // workspace is given, the K range splits over `splits` workgroups per tile
 // (`spl` steps each, at least 8) so that about one workgroup per compute unit
 // runs, on tiles as tall as M needs (32 (int4) or 64 rows, else 128) and 128
@@ -596,7 +591,13 @@ GemmPlan gemm_plan(int M, int N, int K, int bits, bool can_split) {
     p.bm = p.bn = 128;
   }
   const int nsteps = K / (bits == 3 ? 128 : 64);
-  if (can_split && tiles_of(M, N, 128, 128) * 2 <= cus) {
+  // split when 64 x 64 tiles fill at most half the compute units, or for a
+  // long K (8192 or more) when 128 x 128 tiles do (measured with weights in
+  // HBM: 4096 x 4096 at M = 17-64 23 -> 15 us, 11008 x 4096 at M = 17-256
+  // 55-66 -> 23-45 us; 4096 x 11008 at M = 17-64, with 172 tiles of 64 x 64,
+  // got no faster)
+  if (can_split && (tiles_of(M, N, 64, 64) * 2 <= cus ||
+                    (K >= 8192 && tiles_of(M, N, 128, 128) * 2 <= cus))) {
     const int bm = M <= 32 && bits == 4 ? 32 : (M <= 64 ? 64 : 128);
     const unsigned tiles = tiles_of(M, N, bm, 128);
     const int s = min((int)(cus / tiles), max(1, nsteps / 8));
