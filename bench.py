@@ -52,6 +52,8 @@ def parse():
                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="approximate budget for the oracle's timed sample")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-configuration table")
     return p.parse_args()
 
 
@@ -93,6 +95,63 @@ def cpu_baseline(w, W, Xc, s_np, budget_s):
                    f"{t_pack:.2f} s ({rows * w.K * 2 / t_pack / 1e9:.3f} GB/s of fp16 W)"),
         "threads_env": os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS"),
     }
+
+
+def config_table(awq, torch, datagen, dev, stream):
+    """Every workload's product at each of its decode and prefill M, on
+    rotated copies of its packed weights (at least 512 MiB in all, at most
+    64 copies: the smallest layer stays partly in the 256 MB cache), timed
+    with HIP events around a replayed graph of back-to-back calls (two
+    passes over the copies). Weights ~ N(0, 0.02), activations ~ N(0, 1)."""
+    import numpy as np
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    table = []
+    for w in datagen.WORKLOADS.values():
+        Wt = torch.randn((w.N, w.K), generator=gen, device=dev).mul_(0.02).half()
+        q, sc, z = awq.quantize_pack(Wt, None, w.bits, w.group)
+        del Wt
+        packed = q.numel() * 4 + sc.numel() * 5
+        R = int(min(64, max(2, np.ceil(512 * 2**20 / packed))))
+        sets = [(q, sc, z)] + [(q.clone(), sc.clone(), z.clone()) for _ in range(R - 1)]
+        for M in w.all_M:
+            X = torch.randn((M, w.K), generator=gen, device=dev).half()
+            Y = torch.empty((M, w.N), dtype=torch.float16, device=dev)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for r in range(2):  # warm-up; allocates the split workspace, if any
+                    awq.w4a16_matmul(X, *sets[r], w.bits, w.group, out=Y)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(2):
+                    for r in range(R):
+                        awq.w4a16_matmul(X, *sets[r], w.bits, w.group, out=Y)
+            g.replay()
+            times = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                times.append((a, b))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3 / (2 * R)
+            del g
+            byt = packed + 2 * M * w.K + 2 * M * w.N
+            fl = 2.0 * M * w.N * w.K
+            row = {"workload": w.name, "M": M, "us": round(us, 2),
+                   "GB/s": round(byt / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 1)}
+            if M in w.decode_M:
+                row["hbm_frac"] = round(byt / us / 1e3 / HBM_PEAK_GBS, 4)
+            else:
+                row["mfma_frac"] = round(fl / us / 1e6 / FP16_MFMA_PEAK_TF, 4)
+            table.append(row)
+        del sets
+        torch.cuda.empty_cache()
+    return table
 
 
 def main():
@@ -343,6 +402,10 @@ def main():
             "fold_us": round(fold_ms * 1e3, 1),
         },
     }
+    if not args.no_configs:
+        del copies, graphs
+        torch.cuda.empty_cache()
+        out["configs"] = config_table(awq, torch, datagen, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, W_np, Xc_np, s0.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(out), flush=True)
