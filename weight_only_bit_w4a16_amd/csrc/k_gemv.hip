@@ -792,7 +792,11 @@ hipError_t launch_gemv_w3_m1_t(const __half* X, const uint32_t* q, const void* s
   if (sp > 6) return hipErrorNotSupported;
   const int gshift = group_shift(group);
   const int wpr = words_per_row(K, 3, group);
-  const int nw = max(cu_count() * 8, (N + 63) / 64);
+  // wavefronts per compute unit: 3 per SIMD for rows of two pieces, else 2
+  // (a kernel-trace sweep of 4-24 per CU and ring depths 1-3: 4096 x 11008
+  // 8.8 -> 7.9 us, and a ring of two rows on 11008-long rows 10.0 -> 9.6 us)
+  const int wpc = sp == 2 ? 12 : 8;
+  const int nw = max(cu_count() * wpc, (N + 63) / 64);
   const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
@@ -812,7 +816,7 @@ hipError_t launch_gemv_w3_m1_t(const __half* X, const uint32_t* q, const void* s
     case 3: AWQ_W3(3, 2); break;
     case 4: AWQ_W3(4, 1); break;
     case 5: AWQ_W3(5, 1); break;
-    default: AWQ_W3(6, 1); break;
+    default: AWQ_W3(6, 2); break;
   }
 #undef AWQ_W3
   return hipGetLastError();
@@ -1243,7 +1247,9 @@ hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float
   const int nch = K / 128;
   const int sp = (nch + 15) / 16;
   if (sp > 6) return hipErrorNotSupported;
-  const int nw = max(cu_count() * 8, (N + 63) / 64);
+  // 2 wavefronts per SIMD, 4 for rows of two pieces (a kernel-trace sweep
+  // of 8-16 per CU and ring depths 1-4: 2 x 4096 x 11008 12.9 -> 11.1 us)
+  const int nw = max(cu_count() * (sp == 2 ? 16 : 8), (N + 63) / 64);
   const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
   const bool full = nch % 16 == 0;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
