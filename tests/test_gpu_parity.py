@@ -351,6 +351,36 @@ def test_prefill_split_k_then_other_shapes():
         assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, 128, K))
 
 
+def test_prefill_split_k_workspace_contract():
+    """Without a workspace the same shape runs unsplit (within the contract
+    of the split result); a workspace one byte short is refused."""
+    import ctypes
+    from weight_only_bit_w4a16_amd import _lib
+    M, N, K = 33, 2048, 4096
+    W = datagen.random_f16((N, K), 0.02, seed=5)
+    X = datagen.random_f16((M, K), 1.0, seed=6)
+    q, sc, z = _packed(W, None, 4, 128)
+    Xd = dev(X)
+    Ys = host(awq.w4a16_matmul(Xd, q, sc, z))
+    Yu = host(awq.w4a16_matmul(Xd, q, sc, z, kernel=awq.KERNEL_PREFILL))
+    qo, so, zo = O.quantize_pack(W, None, 4, 128)
+    Yo = O.matmul(X, qo, so, zo, 4, 128, K)
+    assert_rows_close(Ys, Yo)
+    assert_rows_close(Yu, Yo)
+    nb = awq.matmul_workspace_bytes(M, N, K)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    h = awq.lib()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    r = h.awq_w4a16_matmul_ws(p(Xd), p(q), p(sc), p(z), M, N, K, 4, 128, p(y), p(ws), nb - 1, st)
+    assert r == _lib.AWQ_ERR_WORKSPACE
+    r = h.awq_w4a16_matmul_ws(p(Xd), p(q), p(sc), p(z), M, N, K, 4, 128, p(y), None, 0, st)
+    assert r == _lib.AWQ_OK
+    assert_same_bits(host(y), Yu)
+
+
 def _prefill_cases():
     return [(name, M) for name, w in datagen.WORKLOADS.items() for M in w.prefill_M]
 
