@@ -195,6 +195,40 @@ def test_decode_int4_long_k(M, N, K, group):
     assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, group, K))
 
 
+@pytest.mark.parametrize("N,K,group", [(37, 13824, 128), (64, 16384, 128), (21, 20480, 256),
+                                       (45, 22016, 128), (30, 24576, 256), (19, 26624, 128),
+                                       (70, 28672, 128), (33, 28672, 512), (18, 28672, -1),
+                                       (25, 30720, 128)])
+def test_decode_int4_m1_long_rows(N, K, group):
+    """M = 1 on rows of 7 to 15 pieces of 16 groups: one wavefront per row up
+    to 10 pieces, two per row (each half the pieces) from 11 to 14 (22016
+    and 26624 leave the last piece partial or empty), the generic kernel past
+    that."""
+    say("decode int4 M=1 long rows", N, K, group)
+    W = datagen.random_f16((N, K), 0.02, seed=N + 2 * K)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 7)
+    X = datagen.random_f16((1, K), 1.0, seed=K + 1)
+    g = K if group == -1 else group
+    q, sc, z = _packed(W, s, 4, group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group))
+    qo, so, zo = O.quantize_pack(W, s, 4, g)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, g, K))
+
+
+def test_decode_int4_m1_long_rows_many():
+    """Two wavefronts per row with several rows each (N = 4500 over the
+    row wavefronts of the grid); the first, last and a sample of rows."""
+    N, K = 4500, 28672
+    say("decode int4 M=1 long rows, many rows")
+    W = datagen.random_f16((N, K), 0.02, seed=11)
+    X = datagen.random_f16((1, K), 1.0, seed=12)
+    q, sc, z = _packed(W, None, 4, 128)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z))
+    rows = np.unique(np.concatenate([np.arange(0, 40), sample_rows(N), np.arange(N - 40, N)]))
+    qo, so, zo = O.quantize_pack(W[rows], None, 4, 128)
+    assert_rows_close(Y[:, rows], O.matmul(X, qo, so, zo, 4, 128, K))
+
+
 def test_decode_int4_long_k_many_row_blocks():
     """Several row blocks per workgroup over two passes (N = 8200 gives 513
     row blocks); every row of a sample checked."""

@@ -358,37 +358,47 @@ int cu_count() {
 // activation): the ring walks items 2i (gate row n_i, from Q/S/Z) and 2i + 1
 // (up row n_i, from Q2/S2/Z2); the gate sum waits in a register and the up
 // item stores fp16(silu(g) * u), silu(g) = g / (1 + e^-g), in fp32.
+//
+// SEG = 2 (long rows): the two wavefronts 2r and 2r + 1 of a workgroup read
+// the same rows, the first SP pieces and the rest; the second one's sums
+// pass through LDS and the first one adds them and stores.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int SP, int RPF, bool FULL, bool DUAL, bool CS>
+template <int SP, int RPF, bool FULL, bool DUAL, bool CS, int SEG = 1>
 __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
     const void* __restrict__ Z, const uint32_t* __restrict__ Q2, const void* __restrict__ S2,
     const void* __restrict__ Z2, uint16_t* __restrict__ Y, int N, int K, int gshift) {
-  __shared__ u32x4 xs[SP][4][64];  // [piece][operand][lane]
-  __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
+  static_assert(SEG == 1 || (SEG == 2 && !DUAL), "row segments: plain product, 2 per row");
+  constexpr int NP = SP * SEG;     // pieces of a row
+  __shared__ u32x4 xs[NP][4][64];  // [piece][operand][lane]
+  __shared__ float2 xcs[NP][16];   // (C, S) of group 16*piece + j
+  __shared__ float segp[SEG > 1 ? 4 : 1][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * 4 + wave;
-  const int NW = gridDim.x * 4;
+  const int seg = SEG > 1 ? wave % SEG : 0;  // pieces seg*SP .. seg*SP + SP - 1
+  const int gw = blockIdx.x * (4 / SEG) + wave / SEG;
+  const int NW = gridDim.x * (4 / SEG);
   const int j = lane & 15;
   const int jj = lane >> 4;
-  const int nch = K >> 7;  // groups of 128 codes per row; SP = ceil(nch / 16)
+  const int nch = K >> 7;  // groups of 128 codes per row; NP = ceil(nch / 16)
   const int ngr = max(1, nch >> gshift);
   const int wpr = K >> 3;
   const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
   const bool diag = jj == (j >> 2);
 
-  // this lane's group in every piece; without FULL the last piece may be
-  // partial: its missing groups read a valid group and get weight 0
+  // this lane's group in every piece of its segment; without FULL the last
+  // pieces may be partial or empty: their missing groups read a valid group
+  // and get weight 0
   int goff[SP];
   bool gval[SP];
 #pragma unroll
   for (int s = 0; s < SP; ++s) {
-    gval[s] = FULL || 16 * s + j < nch;
-    goff[s] = FULL ? 16 * s + j : min(16 * s + j, nch - 1);
+    const int g = 16 * (seg * SP + s) + j;
+    gval[s] = FULL || g < nch;
+    goff[s] = FULL ? g : min(g, nch - 1);
   }
 
   // operand prep: thread (piece s, lane l) of the workgroup permutes the
@@ -396,11 +406,11 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
   // loaded first; for long rows (SP >= 3) the prep runs after the first ring
   // loads are issued, so it overlaps their memory latency.
   constexpr bool kLatePrep = SP >= 3;
-  constexpr int XI = (SP * 64 + 255) / 256;  // prep items per thread
+  constexpr int XI = (NP * 64 + 255) / 256;  // prep items per thread
   uint32_t xd[XI][16];
 #pragma unroll
   for (int u = 0; u < XI; ++u) {
-    const int t = min((int)threadIdx.x + 256 * u, SP * 64 - 1);
+    const int t = min((int)threadIdx.x + 256 * u, NP * 64 - 1);
     const int g = min(16 * (t >> 6) + (t & 15), nch - 1);
     load_x32(X + g * 128 + 32 * ((t & 63) >> 4), xd[u]);
   }
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
       so += __shfl_xor(so, 16);
       se += __shfl_xor(se, 32);
       so += __shfl_xor(so, 32);
-      if (t < SP * 64) {  // wave-uniform: SP * 64 is a multiple of 64
+      if (t < NP * 64) {  // wave-uniform: NP * 64 is a multiple of 64
         xs[ps][0][pl] = o0;
         xs[ps][1][pl] = o1;
         xs[ps][2][pl] = o2;
@@ -442,7 +452,7 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < SP; ++s) {
-      const float2 v = xcs[s][j];
+      const float2 v = xcs[seg * SP + s][j];
       cC[s] = v.x;
       cS[s] = v.y;
     }
@@ -502,10 +512,11 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
             e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
             o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
           }
-          floatx4 acc = mfma16(xs[s][0][lane], u32x4{e[0], e[1], e[2], e[3]}, zero4);
-          acc = mfma16(xs[s][1][lane], u32x4{e[4], e[5], e[6], e[7]}, acc);
-          acc = mfma16(xs[s][2][lane], u32x4{o[0], o[1], o[2], o[3]}, acc);
-          acc = mfma16(xs[s][3][lane], u32x4{o[4], o[5], o[6], o[7]}, acc);
+          const int ps = seg * SP + s;
+          floatx4 acc = mfma16(xs[ps][0][lane], u32x4{e[0], e[1], e[2], e[3]}, zero4);
+          acc = mfma16(xs[ps][1][lane], u32x4{e[4], e[5], e[6], e[7]}, acc);
+          acc = mfma16(xs[ps][2][lane], u32x4{o[0], o[1], o[2], o[3]}, acc);
+          acc = mfma16(xs[ps][3][lane], u32x4{o[4], o[5], o[6], o[7]}, acc);
           float v = acc[0];
           v = rdiag == 1 ? acc[1] : v;
           v = rdiag == 2 ? acc[2] : v;
@@ -555,7 +566,12 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
     if constexpr (kLatePrep)
       if (i0 < 0) prep();
   }
-  if (lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
+  if constexpr (SEG > 1) {  // the row sums: segment 0 plus segment 1
+    segp[wave][lane] = outv;
+    __syncthreads();
+    if (seg == 0) outv += segp[wave + 1][lane];
+  }
+  if (seg == 0 && lane < cnt) Y[gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv));
 }
 
 // ---------------------------------------------------------------------------
@@ -1076,6 +1092,16 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
 }
 
 constexpr int kGemvPF = 8;
+// M = 1 kernel: rows of up to 14 pieces of 16 groups (K <= 28672; the
+// activation operands of a whole row sit in 64 KB of LDS); rows of
+// kM1SegMin or more pieces are read by two wavefronts each (timed on rows
+// of 7-14 pieces: one wavefront per row is as fast up to 10 pieces; at 14,
+// 28672 x 8192, one wavefront per row needs more than 256 registers and ran
+// at 36 us, two per row at 25 us)
+constexpr int kM1MaxPieces = 14;
+constexpr int kM1SegMin = 11;
+static_assert(kM1SegMin == 11 && kM1MaxPieces == 14,
+              "the launcher instantiates 1..10 pieces per row and 6..7 per half row");
 constexpr size_t kLdsMax = 160 * 1024;  // LDS of one gfx950 compute unit
 constexpr int kGemvMaxRbw = 8;
 
@@ -1165,37 +1191,49 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
                                                  nullptr, nullptr, nullptr);
     if (e != hipErrorNotSupported) return e;
   }
-  if (variant == 0 && M == 1) {
-    const int sp = (nch + 15) / 16;
+  if (variant == 0 && M == 1 && nch <= 16 * kM1MaxPieces) {
+    const int np = (nch + 15) / 16;           // pieces of a row
+    const int seg = np >= kM1SegMin ? 2 : 1;  // wavefronts per row
+    const int sp = (np + seg - 1) / seg;      // pieces per wavefront
     // wavefronts: all resident, at most 64 rows each; 2 per SIMD, or 3 when
     // the registers allow it (up to 4 pieces) and every wavefront still gets
     // 5 or more rows (measured: 3 per SIMD is 2-4% faster there and slower
     // for fewer rows or longer rows); rows of 2 pieces: 4 per SIMD with a
     // ring of one row (measured 10-12% faster than 2-3 per SIMD with two)
-    const int wpc = sp == 2 ? 16 : (sp <= 4 && N >= 5 * 8 * cu_count() ? 12 : 8);
-    const int nw = max(cu_count() * wpc, (N + 63) / 64);
-    const dim3 g1((unsigned)((min(N, nw) + 3) / 4));
-    const bool full = nch % 16 == 0;
-#define AWQ_M1(SM, RP)                                                                          \
+    const int wpc = sp == 2 && seg == 1 ? 16 : (sp <= 4 && N >= 5 * 8 * cu_count() ? 12 : 8);
+    const int nrw = min(N, max(cu_count() * wpc / seg, (N + 63) / 64));  // row wavefronts
+    const dim3 g1((unsigned)((nrw * seg + 3) / 4));
+    const bool full = nch == 16 * sp * seg;
+#define AWQ_M1S(SM, RP, SG)                                                                    \
   do {                                                                                          \
     if (full)                                                                                   \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, false, CS>), g1, block, 0, st, x, q, \
-                         scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);            \
-    else                                                                                        \
-      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, false, CS>), g1, block, 0, st, x,   \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, true, false, CS, SG>), g1, block, 0, st, x, \
                          q, scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);         \
+    else                                                                                        \
+      hipLaunchKernelGGL((gemv_w4_m1_kernel<SM, RP, false, false, CS, SG>), g1, block, 0, st,  \
+                         x, q, scales, zeros, nullptr, nullptr, nullptr, y, N, K, gshift);      \
   } while (0)
-    switch (sp) {
-      case 1: AWQ_M1(1, 4); break;
-      case 2: AWQ_M1(2, 1); break;
-      case 3: AWQ_M1(3, 2); break;
-      case 4: AWQ_M1(4, 1); break;
-      case 5: AWQ_M1(5, 1); break;
-      case 6: AWQ_M1(6, 1); break;
-      default: break;
+#define AWQ_M1(SM, RP) AWQ_M1S(SM, RP, 1)
+    if (seg == 1) {
+      switch (sp) {
+        case 1: AWQ_M1(1, 4); break;
+        case 2: AWQ_M1(2, 1); break;
+        case 3: AWQ_M1(3, 2); break;
+        case 4: AWQ_M1(4, 1); break;
+        case 5: AWQ_M1(5, 1); break;
+        case 6: AWQ_M1(6, 1); break;
+        case 7: AWQ_M1(7, 1); break;
+        case 8: AWQ_M1(8, 1); break;
+        case 9: AWQ_M1(9, 1); break;
+        default: AWQ_M1(10, 1); break;
+      }
+    } else {
+      if (sp <= 6) AWQ_M1S(6, 1, 2);  // 11 or 12 pieces
+      else AWQ_M1S(7, 1, 2);          // 13 or 14
     }
 #undef AWQ_M1
-    if (sp <= 6) return hipGetLastError();
+#undef AWQ_M1S
+    return hipGetLastError();
   }
   // LDS: activations in MFMA order and their C, S (offset form), the row
   // blocks' partial sums, and the staged scales and zero points
