@@ -229,6 +229,28 @@ def test_decode_int4_m1_long_rows_many():
     assert_rows_close(Y[:, rows], O.matmul(X, qo, so, zo, 4, 128, K))
 
 
+@pytest.mark.parametrize("M,N,K,group", [(2, 300, 6016, 128), (2, 129, 8192, 256),
+                                         (2, 5000, 8192, 128), (3, 6200, 3968, 128),
+                                         (3, 9300, 2048, -1), (4, 6150, 4096, 128),
+                                         (4, 9300, 1920, 128), (3, 77, 3968, 128),
+                                         (4, 1111, 1920, 128)])
+def test_decode_int4_few_token_rows(M, N, K, group):
+    """2 <= M <= 4 on rows of at most 8 / M pieces: one diagonal MFMA set per
+    token row over the contiguous pieces of a row, used at M = 2 and, with
+    three or more rows per wavefront (N of 6144 and more on 256 compute
+    units), at M = 3, 4; partial last pieces at K = 6016, 3968 and 1920. The
+    small-N cases at M = 3, 4 run the 16-row-block kernel."""
+    say("decode int4 few token rows", M, N, K, group)
+    W = datagen.random_f16((N, K), 0.02, seed=3 * N + K)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 9)
+    X = datagen.random_f16((M, K), 1.0, seed=M * K)
+    g = K if group == -1 else group
+    q, sc, z = _packed(W, s, 4, group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group))
+    qo, so, zo = O.quantize_pack(W, s, 4, g)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, g, K))
+
+
 def test_decode_int4_long_k_many_row_blocks():
     """Several row blocks per workgroup over two passes (N = 8200 gives 513
     row blocks); every row of a sample checked."""

@@ -575,6 +575,187 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Decode, int4, 2 <= M <= 4 on rows of few pieces (M x pieces <= 8): the
+// M = 1 streaming scheme with one set of diagonal MFMAs per token row. A
+// wavefront reads a row as contiguous 1 KB pieces, unpacks each piece once
+// and contracts it with the activation operands of every token row; those
+// are prepared in LDS once per workgroup and then held in registers by every
+// wavefront (16 VGPRs per token row and piece), so the loop reads no LDS.
+// MT x 4 MFMAs per piece (MT = M): at M = 4, 16 per KB of weights, within
+// the matrix cores' rate at full HBM bandwidth.
+// ---------------------------------------------------------------------------
+template <int MT, int SP, bool FULL, bool CS>
+__global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
+    const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int gshift) {
+  __shared__ u32x4 xs[MT][SP][4][64];  // [token][piece][operand][lane]
+  __shared__ float2 xcs[MT][SP][16];   // (C, S) of token row, group 16*piece + j
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wave;
+  const int NW = gridDim.x * 4;
+  const int j = lane & 15;
+  const int jj = lane >> 4;
+  const int nch = K >> 7;
+  const int ngr = max(1, nch >> gshift);
+  const int wpr = K >> 3;
+  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int rdiag = j & 3;
+  const bool diag = jj == (j >> 2);
+
+  int goff[SP];
+  bool gval[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    gval[s] = FULL || 16 * s + j < nch;
+    goff[s] = FULL ? 16 * s + j : min(16 * s + j, nch - 1);
+  }
+
+  // operand prep: item t = (token row, piece, lane) as in the M = 1 kernel,
+  // then every wavefront copies all operands and its groups' C, S to registers
+  constexpr int NI = MT * SP * 64;
+  constexpr int XI = (NI + 255) / 256;
+  constexpr bool kLatePrep = MT * SP >= 3;
+  u32x4 av[MT][SP][4];
+  float cC[MT][SP], cS[MT][SP];
+  auto prep = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+      const int t = (int)threadIdx.x + 256 * u;
+      if (t < NI) {  // wave-uniform: NI is a multiple of 64
+        const int tk = t / (SP * 64), ps = (t >> 6) % SP, pl = t & 63;
+        const int g = min(16 * ps + (pl & 15), nch - 1);
+        uint32_t d[16];
+        load_x32(X + (size_t)tk * K + g * 128 + 32 * (pl >> 4), d);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {  // odd slots: x / 16 rounded to fp16
+          const float od = h2f((uint16_t)(d[i] >> 16)) * 0.0625f;
+          d[i] = (d[i] & 0xffffu) | ((uint32_t)__half_as_ushort(__float2half_rn(od)) << 16);
+        }
+        u32x4 o0, o1, o2, o3;
+        permute_x32(d, o0, o1, o2, o3);
+        float se = 0.f, so = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          se += h2f((uint16_t)(d[i] & 0xffffu));
+          so += h2f((uint16_t)(d[i] >> 16));
+        }
+        se += __shfl_xor(se, 16);
+        so += __shfl_xor(so, 16);
+        se += __shfl_xor(se, 32);
+        so += __shfl_xor(so, 32);
+        xs[tk][ps][0][pl] = o0;
+        xs[tk][ps][1][pl] = o1;
+        xs[tk][ps][2][pl] = o2;
+        xs[tk][ps][3][pl] = o3;
+        if (pl < 16) xcs[tk][ps][pl] = make_float2(1024.f * (se + so), se + 16.f * so);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tk = 0; tk < MT; ++tk)
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) av[tk][s][k] = xs[tk][s][k][lane];
+        const float2 v = xcs[tk][s][j];
+        cC[tk][s] = v.x;
+        cS[tk][s] = v.y;
+      }
+  };
+  if constexpr (!kLatePrep) prep();
+
+  // a ring of one row; the loop starts one row early with an empty ring (no
+  // prologue loads, as in the M = 1 kernel)
+  u32x4 wb[SP];
+  float db[SP];
+  uint32_t zb[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    wb[s] = u32x4{0, 0, 0, 0};
+    db[s] = 0.f;
+    zb[s] = 0u;
+  }
+  const uint32_t magic = kMagic2;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* qlane = Q + 16 * j + 4 * jj;
+  float outv[MT];
+#pragma unroll
+  for (int tk = 0; tk < MT; ++tk) outv[tk] = 0.f;
+  for (int row = -1; row < cnt; ++row) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (row >= 0) {  // uniform
+      float y[MT];
+#pragma unroll
+      for (int tk = 0; tk < MT; ++tk) y[tk] = 0.f;
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        const u32x4 w = wb[s];
+        const float d = gval[s] ? db[s] : 0.f;
+        const float zf = (float)zb[s];
+        uint32_t e[8], o[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t x = w[t];
+          const uint32_t x8 = x >> 8;
+          e[2 * t] = and_or(x, 0x000F000Fu, magic);
+          o[2 * t] = and_or(x, 0x00F000F0u, magic);
+          e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
+          o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
+        }
+#pragma unroll
+        for (int tk = 0; tk < MT; ++tk) {
+          floatx4 acc = mfma16(av[tk][s][0], u32x4{e[0], e[1], e[2], e[3]}, zero4);
+          acc = mfma16(av[tk][s][1], u32x4{e[4], e[5], e[6], e[7]}, acc);
+          acc = mfma16(av[tk][s][2], u32x4{o[0], o[1], o[2], o[3]}, acc);
+          acc = mfma16(av[tk][s][3], u32x4{o[4], o[5], o[6], o[7]}, acc);
+          float v = acc[0];
+          v = rdiag == 1 ? acc[1] : v;
+          v = rdiag == 2 ? acc[2] : v;
+          v = rdiag == 3 ? acc[3] : v;
+          const float zs = __builtin_fmaf(zf, cS[tk][s], cC[tk][s]);
+          y[tk] = __builtin_fmaf(d, v - zs, y[tk]);
+        }
+      }
+      // row done: per token row, the 16 diagonal lanes (quads 0, 5, 10, 15)
+      // added with DPP within quads, then the 4 quads
+#pragma unroll
+      for (int tk = 0; tk < MT; ++tk) {
+        float v = diag ? y[tk] : 0.f;
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0xB1, 0xF, 0xF, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0x4E, 0xF, 0xF, true));
+        const float sum =
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
+        outv[tk] = (row & 63) == lane ? sum : outv[tk];
+      }
+    }
+    if (row + 1 < cnt) {  // uniform: refill with the next row's pieces
+      const size_t nn = (size_t)gw + (size_t)(row + 1) * NW;
+      const uint32_t* qn = qlane + nn * wpr;
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        wb[s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
+        db[s] = group_scale<CS>(S, nn, ngr, goff[s] >> gshift);
+        zb[s] = group_zero<CS>(Z, nn, ngr, goff[s] >> gshift);
+      }
+    }
+    // keeps the refill loads out of the loop head (see the M = 1 kernel)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    if constexpr (kLatePrep)
+      if (row < 0) prep();  // uniform: after the first row's loads are issued
+  }
+#pragma unroll
+  for (int tk = 0; tk < MT; ++tk)
+    if (lane < cnt)
+      Y[(size_t)tk * N + gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv[tk]));
+}
+
+// ---------------------------------------------------------------------------
 // Decode, int3, M = 1, group 128. The same streaming scheme as the int4
 // kernel above: a wavefront reads one row at a time in pieces of 16 groups
 // (16 x 13 words = 832 contiguous bytes) and contracts each piece with
@@ -1099,6 +1280,8 @@ constexpr int kGemvPF = 8;
 // 28672 x 8192, one wavefront per row needs more than 256 registers and ran
 // at 36 us, two per row at 25 us)
 constexpr int kM1MaxPieces = 14;
+// 2 <= M <= 4 on short rows: token rows x pieces held in registers
+constexpr int kMtMaxItems = 8;
 constexpr int kM1SegMin = 11;
 static_assert(kM1SegMin == 11 && kM1MaxPieces == 14,
               "the launcher instantiates 1..10 pieces per row and 6..7 per half row");
@@ -1186,6 +1369,45 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
   const dim3 grid((nrb + rbw - 1) / rbw), block(256);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
   uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  // 2 <= M <= 4 on short rows: the M = 1 scheme per token row (gemv_w4_mt_kernel).
+  // Timed with kernel traces against gemv_w4_mx_kernel over rotated weights:
+  // M = 2 faster on every shape (4096x4096 7.7 -> 6.6 us, 4096x11008 12.8 ->
+  // 9.4, 6144x6144 13.6 -> 9.4, 8192x28672 35.2 -> 27.4); M = 3 and 4 only
+  // once every wavefront gets three or more rows (4096x11008 M = 4 13.2 ->
+  // 12.6 us, while 4096 rows at M = 4 went from 7.9 to 8.1). 3 wavefronts
+  // per SIMD at up to 4 token-row pieces (128-136 registers; 4096x11008
+  // M = 2 10.2 -> 9.4 us), else 2.
+  const int mtsp = (nch + 15) / 16;
+  const int mtw = cu_count() * (M * mtsp <= 4 ? 12 : 8);
+  if (variant == 0 && M >= 2 && M <= 4 && M * mtsp <= kMtMaxItems && (M == 2 || N >= 3 * mtw)) {
+    const int sp = mtsp;
+    const int nw = max(mtw, (N + 63) / 64);
+    const dim3 g1((unsigned)((min(N, nw) + 3) / 4));
+    const bool full = nch % 16 == 0;
+#define AWQ_MT(MV, SM)                                                                          \
+  do {                                                                                          \
+    if (full)                                                                                   \
+      hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, true, CS>), g1, block, 0, st, x, q, scales, \
+                         zeros, y, N, K, gshift);                                               \
+    else                                                                                        \
+      hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, false, CS>), g1, block, 0, st, x, q,       \
+                         scales, zeros, y, N, K, gshift);                                       \
+  } while (0)
+    if (M == 2) {
+      if (sp == 1) AWQ_MT(2, 1);
+      else if (sp == 2) AWQ_MT(2, 2);
+      else if (sp == 3) AWQ_MT(2, 3);
+      else AWQ_MT(2, 4);
+    } else if (M == 3) {
+      if (sp == 1) AWQ_MT(3, 1);
+      else AWQ_MT(3, 2);
+    } else {
+      if (sp == 1) AWQ_MT(4, 1);
+      else AWQ_MT(4, 2);
+    }
+#undef AWQ_MT
+    return hipGetLastError();
+  }
   if (variant == 0 && M >= 2) {
     const hipError_t e = launch_gemv_w4_mx_t<CS>(X, q, scales, zeros, M, N, K, group, Y, st,
                                                  nullptr, nullptr, nullptr);
