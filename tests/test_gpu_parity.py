@@ -233,13 +233,18 @@ def test_decode_int4_m1_long_rows_many():
                                          (2, 5000, 8192, 128), (3, 6200, 3968, 128),
                                          (3, 9300, 2048, -1), (4, 6150, 4096, 128),
                                          (4, 9300, 1920, 128), (3, 77, 3968, 128),
-                                         (4, 1111, 1920, 128)])
+                                         (4, 1111, 1920, 128), (2, 700, 10240, 128),
+                                         (2, 2000, 12288, 256), (3, 3100, 8192, 128),
+                                         (3, 3333, 8192, -1), (4, 3500, 6016, 128),
+                                         (4, 3072, 8192, 256)])
 def test_decode_int4_few_token_rows(M, N, K, group):
     """2 <= M <= 4 on rows of at most 8 / M pieces: one diagonal MFMA set per
     token row over the contiguous pieces of a row, used at M = 2 and, with
     three or more rows per wavefront (N of 6144 and more on 256 compute
-    units), at M = 3, 4; partial last pieces at K = 6016, 3968 and 1920. The
-    small-N cases at M = 3, 4 run the 16-row-block kernel."""
+    units), at M = 3, 4; partial last pieces at K = 6016, 3968 and 1920. Two
+    wavefronts per row at M = 2 on 5-6 pieces (K = 10240 with an empty last
+    piece, 12288). The small-N cases at M = 3, 4 and the longer rows at
+    M = 3, 4 run the 16-row-block kernel."""
     say("decode int4 few token rows", M, N, K, group)
     W = datagen.random_f16((N, K), 0.02, seed=3 * N + K)
     s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 9)

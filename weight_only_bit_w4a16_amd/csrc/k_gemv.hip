@@ -582,18 +582,30 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
 // are prepared in LDS once per workgroup and then held in registers by every
 // wavefront (16 VGPRs per token row and piece), so the loop reads no LDS.
 // MT x 4 MFMAs per piece (MT = M): at M = 4, 16 per KB of weights, within
-// the matrix cores' rate at full HBM bandwidth.
+// the matrix cores' rate at full HBM bandwidth. SEG = 2: as in the M = 1
+// kernel, wavefronts 2r and 2r + 1 read the first SP pieces of the same rows
+// and the rest, and the first adds the second's sums (through LDS).
+// Dynamic LDS: mt_lds_bytes(MT, SP * SEG, SEG).
 // ---------------------------------------------------------------------------
-template <int MT, int SP, bool FULL, bool CS>
+constexpr size_t mt_lds_bytes(int mt, int np, int seg) {
+  return (size_t)mt * np * (4 * 64 * 16 + 16 * 8) + (seg > 1 ? (size_t)4 * mt * 64 * 4 : 0);
+}
+
+template <int MT, int SP, bool FULL, bool CS, int SEG>
 __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
     const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int gshift) {
-  __shared__ u32x4 xs[MT][SP][4][64];  // [token][piece][operand][lane]
-  __shared__ float2 xcs[MT][SP][16];   // (C, S) of token row, group 16*piece + j
+  static_assert(SEG == 1 || SEG == 2, "one or two wavefronts per row");
+  constexpr int NP = SP * SEG;  // pieces of a row
+  extern __shared__ __align__(16) uint8_t smem[];
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);                         // [MT][NP][4][64]
+  float2* xcs = reinterpret_cast<float2*>(xs + MT * NP * 4 * 64);     // [MT][NP][16]: (C, S)
+  float* segp = reinterpret_cast<float*>(xcs + MT * NP * 16);         // [4][MT][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * 4 + wave;
-  const int NW = gridDim.x * 4;
+  const int seg = SEG > 1 ? wave % SEG : 0;  // pieces seg*SP .. seg*SP + SP - 1
+  const int gw = blockIdx.x * (4 / SEG) + wave / SEG;
+  const int NW = gridDim.x * (4 / SEG);
   const int j = lane & 15;
   const int jj = lane >> 4;
   const int nch = K >> 7;
@@ -607,13 +619,15 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
   bool gval[SP];
 #pragma unroll
   for (int s = 0; s < SP; ++s) {
-    gval[s] = FULL || 16 * s + j < nch;
-    goff[s] = FULL ? 16 * s + j : min(16 * s + j, nch - 1);
+    const int g = 16 * (seg * SP + s) + j;
+    gval[s] = FULL || g < nch;
+    goff[s] = FULL ? g : min(g, nch - 1);
   }
 
   // operand prep: item t = (token row, piece, lane) as in the M = 1 kernel,
-  // then every wavefront copies all operands and its groups' C, S to registers
-  constexpr int NI = MT * SP * 64;
+  // then every wavefront copies its pieces' operands and its groups' C, S to
+  // registers
+  constexpr int NI = MT * NP * 64;
   constexpr int XI = (NI + 255) / 256;
   constexpr bool kLatePrep = MT * SP >= 3;
   u32x4 av[MT][SP][4];
@@ -623,7 +637,7 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     for (int u = 0; u < XI; ++u) {
       const int t = (int)threadIdx.x + 256 * u;
       if (t < NI) {  // wave-uniform: NI is a multiple of 64
-        const int tk = t / (SP * 64), ps = (t >> 6) % SP, pl = t & 63;
+        const int tk = t / (NP * 64), ps = (t >> 6) % NP, pl = t & 63;
         const int g = min(16 * ps + (pl & 15), nch - 1);
         uint32_t d[16];
         load_x32(X + (size_t)tk * K + g * 128 + 32 * (pl >> 4), d);
@@ -644,11 +658,12 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
         so += __shfl_xor(so, 16);
         se += __shfl_xor(se, 32);
         so += __shfl_xor(so, 32);
-        xs[tk][ps][0][pl] = o0;
-        xs[tk][ps][1][pl] = o1;
-        xs[tk][ps][2][pl] = o2;
-        xs[tk][ps][3][pl] = o3;
-        if (pl < 16) xcs[tk][ps][pl] = make_float2(1024.f * (se + so), se + 16.f * so);
+        u32x4* xo = xs + (size_t)(tk * NP + ps) * 4 * 64 + pl;
+        xo[0] = o0;
+        xo[64] = o1;
+        xo[128] = o2;
+        xo[192] = o3;
+        if (pl < 16) xcs[(tk * NP + ps) * 16 + pl] = make_float2(1024.f * (se + so), se + 16.f * so);
       }
     }
     __syncthreads();
@@ -656,9 +671,10 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     for (int tk = 0; tk < MT; ++tk)
 #pragma unroll
       for (int s = 0; s < SP; ++s) {
+        const int ps = tk * NP + seg * SP + s;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) av[tk][s][k] = xs[tk][s][k][lane];
-        const float2 v = xcs[tk][s][j];
+        for (int k = 0; k < 4; ++k) av[tk][s][k] = xs[(size_t)(ps * 4 + k) * 64 + lane];
+        const float2 v = xcs[ps * 16 + j];
         cC[tk][s] = v.x;
         cS[tk][s] = v.y;
       }
@@ -749,9 +765,18 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     if constexpr (kLatePrep)
       if (row < 0) prep();  // uniform: after the first row's loads are issued
   }
+  if constexpr (SEG > 1) {  // the row sums: segment 0 plus segment 1
+#pragma unroll
+    for (int tk = 0; tk < MT; ++tk) segp[(wave * MT + tk) * 64 + lane] = outv[tk];
+    __syncthreads();
+    if (seg == 0) {
+#pragma unroll
+      for (int tk = 0; tk < MT; ++tk) outv[tk] += segp[((wave + 1) * MT + tk) * 64 + lane];
+    }
+  }
 #pragma unroll
   for (int tk = 0; tk < MT; ++tk)
-    if (lane < cnt)
+    if (seg == 0 && lane < cnt)
       Y[(size_t)tk * N + gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv[tk]));
 }
 
@@ -1377,35 +1402,55 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
   // 12.6 us, while 4096 rows at M = 4 went from 7.9 to 8.1). 3 wavefronts
   // per SIMD at up to 4 token-row pieces (128-136 registers; 4096x11008
   // M = 2 10.2 -> 9.4 us), else 2.
-  const int mtsp = (nch + 15) / 16;
-  const int mtw = cu_count() * (M * mtsp <= 4 ? 12 : 8);
-  if (variant == 0 && M >= 2 && M <= 4 && M * mtsp <= kMtMaxItems && (M == 2 || N >= 3 * mtw)) {
-    const int sp = mtsp;
-    const int nw = max(mtw, (N + 63) / 64);
-    const dim3 g1((unsigned)((min(N, nw) + 3) / 4));
-    const bool full = nch % 16 == 0;
-#define AWQ_MT(MV, SM)                                                                          \
-  do {                                                                                          \
-    if (full)                                                                                   \
-      hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, true, CS>), g1, block, 0, st, x, q, scales, \
-                         zeros, y, N, K, gshift);                                               \
-    else                                                                                        \
-      hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, false, CS>), g1, block, 0, st, x, q,       \
-                         scales, zeros, y, N, K, gshift);                                       \
+  const int mtnp = (nch + 15) / 16;                 // pieces of a row
+  const int mtseg = M * mtnp <= kMtMaxItems ? 1 : 2;  // wavefronts per row
+  const int mtsp = (mtnp + mtseg - 1) / mtseg;      // pieces per wavefront
+  const int mtrw = cu_count() * (M * mtsp <= 4 ? 12 : 8) / mtseg;  // row wavefronts
+  // Two wavefronts per row only at M = 2 on 5-6 pieces (11008x4096 18.9 ->
+  // 12.2 us): at 7-8 pieces they would need more than 256 registers, and at
+  // M = 3, 4 (16 and 12 MFMAs plus about 40 VALU instructions per KB) they
+  // were slower than the 16-row-block kernel (8192x28672 M = 4 37.8 -> 50 us).
+  if (variant == 0 && M >= 2 && M <= 4 && M * mtsp <= kMtMaxItems &&
+      (mtseg == 1 || (M == 2 && mtsp <= 3)) && (M == 2 || N >= 3 * mtrw)) {
+    const int sp = mtsp, seg = mtseg;
+    const int nrw = min(N, max(mtrw, (N + 63) / 64));
+    const dim3 g1((unsigned)((nrw * seg + 3) / 4));
+    const bool full = nch == 16 * sp * seg;
+    const size_t lds = mt_lds_bytes(M, sp * seg, seg);
+#define AWQ_MTF(MV, SM, F, SG)                                                                 \
+  do {                                                                                         \
+    const void* fn = (const void*)gemv_w4_mt_kernel<MV, SM, F, CS, SG>;                        \
+    if (lds > 64 * 1024) {                                                                     \
+      const hipError_t ea =                                                                    \
+          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);       \
+      if (ea != hipSuccess) return ea;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, F, CS, SG>), g1, block, lds, st, x, q,       \
+                       scales, zeros, y, N, K, gshift);                                        \
   } while (0)
-    if (M == 2) {
-      if (sp == 1) AWQ_MT(2, 1);
-      else if (sp == 2) AWQ_MT(2, 2);
-      else if (sp == 3) AWQ_MT(2, 3);
-      else AWQ_MT(2, 4);
-    } else if (M == 3) {
-      if (sp == 1) AWQ_MT(3, 1);
-      else AWQ_MT(3, 2);
-    } else {
-      if (sp == 1) AWQ_MT(4, 1);
-      else AWQ_MT(4, 2);
+#define AWQ_MT(MV, SM, SG)                \
+  do {                                    \
+    if (full) AWQ_MTF(MV, SM, true, SG);  \
+    else AWQ_MTF(MV, SM, false, SG);      \
+  } while (0)
+    if (seg == 1) {
+      if (M == 2) {
+        if (sp == 1) AWQ_MT(2, 1, 1);
+        else if (sp == 2) AWQ_MT(2, 2, 1);
+        else if (sp == 3) AWQ_MT(2, 3, 1);
+        else AWQ_MT(2, 4, 1);
+      } else if (M == 3) {
+        if (sp == 1) AWQ_MT(3, 1, 1);
+        else AWQ_MT(3, 2, 1);
+      } else {
+        if (sp == 1) AWQ_MT(4, 1, 1);
+        else AWQ_MT(4, 2, 1);
+      }
+    } else {  // two wavefronts per row: M = 2, 5 or 6 pieces
+      AWQ_MT(2, 3, 2);
     }
 #undef AWQ_MT
+#undef AWQ_MTF
     return hipGetLastError();
   }
   if (variant == 0 && M >= 2) {
