@@ -254,6 +254,34 @@ def test_decode_int4_few_token_rows(M, N, K, group):
     Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group))
     qo, so, zo = O.quantize_pack(W, s, 4, g)
     assert_rows_close(Y, O.matmul(X, qo, so, zo, 4, g, K))
+    for _ in range(3):  # the same bits on every call
+        assert_same_bits(host(awq.w4a16_matmul(dev(X), q, sc, z, 4, group)), Y)
+
+
+@pytest.mark.parametrize("M,N,K,group", [(2, 300, 1920, 128), (2, 517, 4096, 128),
+                                         (2, 129, 6016, 128), (2, 700, 8192, 256),
+                                         (2, 333, 11008, 128), (3, 250, 4096, -1),
+                                         (3, 411, 6144, 128), (3, 260, 11008, 128),
+                                         (4, 300, 2048, 128), (4, 200, 4096, 512),
+                                         (4, 150, 8192, 128), (4, 123, 16384, 128),
+                                         (3, 100, 14336, 128), (2, 5000, 4096, 128)])
+def test_decode_int3_few_token_rows(M, N, K, group):
+    """int3 at 2 <= M <= 4: all token rows in one launch while M x pieces per
+    wavefront stays within 6 (one wavefront per row, or two from 4096, 6144
+    and 8192 on; partial and empty last pieces), pairs of token rows and an
+    M = 1 launch for the rest past that (11008 at M = 3, 8192 at M = 4), and
+    the generic kernels past 6 pieces per wavefront (16384, 14336)."""
+    say("decode int3 few token rows", M, N, K, group)
+    W = datagen.random_f16((N, K), 0.02, seed=7 * N + K)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 11)
+    X = datagen.random_f16((M, K), 1.0, seed=M * K + 3)
+    g = K if group == -1 else group
+    q, sc, z = _packed(W, s, 3, group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 3, group))
+    qo, so, zo = O.quantize_pack(W, s, 3, g)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 3, g, K))
+    for _ in range(3):  # the same bits on every call
+        assert_same_bits(host(awq.w4a16_matmul(dev(X), q, sc, z, 3, group)), Y)
 
 
 def test_decode_int4_long_k_many_row_blocks():

@@ -89,6 +89,8 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* s
                               cs);
     else if (M == 1 && kernel == 0)
       e = awq::launch_gemv_w3_m1(x, qpacked, scales, zeros, N, K, g, y, s, cs);
+    else if (kernel == 0)
+      e = awq::launch_gemv_w3_mt(x, qpacked, scales, zeros, M, N, K, g, y, s, cs);
     else
       e = hipErrorNotSupported;
     if (bits == 3 && e == hipErrorNotSupported) {

@@ -60,6 +60,11 @@ hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const void* scales
                           const void* zeros, int M, int N, int K, int group, __half* Y,
                           hipStream_t st, bool cs);
 constexpr int kGemvW3MaxM = 4;
+// decode, int3, 2 <= M <= 4 on rows of up to 8 pieces of 16 blocks
+// (hipErrorNotSupported, with nothing launched, otherwise)
+hipError_t launch_gemv_w3_mt(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st, bool cs);
 // decode, int3, M = 1 (K up to 96 blocks of 128 codes)
 hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* scales,
                              const void* zeros, int N, int K, int group, __half* Y, hipStream_t st,

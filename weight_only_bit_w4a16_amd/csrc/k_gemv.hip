@@ -1052,6 +1052,317 @@ hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* sca
 }
 
 // ---------------------------------------------------------------------------
+// Decode, int3, 2 <= M <= 4 on rows of few pieces (M x pieces <= 8): the
+// int3 M = 1 scheme (pieces of 16 groups x 13 words, five diagonal MFMAs
+// per piece) with one set of MFMAs per token row, the activation operands
+// of every token row held in registers (20 VGPRs per token row and piece)
+// after a prep in LDS shared by the workgroup. SEG = 2: two wavefronts per
+// row (first SP pieces and the rest), joined through LDS as in the int4
+// kernels. Dynamic LDS: w3mt_lds_bytes(MT, SP * SEG, SEG).
+// ---------------------------------------------------------------------------
+constexpr size_t w3mt_lds_bytes(int mt, int np, int seg) {
+  return (size_t)mt * np * (5 * 64 * 16 + 16 * 8) + (seg > 1 ? (size_t)4 * mt * 64 * 4 : 0);
+}
+
+template <int MT, int SP, bool FULL, bool CS, int SEG>
+__global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
+    const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int wpr, int gshift) {
+  static_assert(SEG == 1 || SEG == 2, "one or two wavefronts per row");
+  constexpr int NP = SP * SEG;  // pieces of a row
+  extern __shared__ __align__(16) uint8_t smem[];
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);                      // [MT][NP][5][64]
+  float2* xcs = reinterpret_cast<float2*>(xs + MT * NP * 5 * 64);  // [MT][NP][16]: (C, S)
+  float* segp = reinterpret_cast<float*>(xcs + MT * NP * 16);      // [4][MT][64]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int seg = SEG > 1 ? wave % SEG : 0;
+  const int gw = blockIdx.x * (4 / SEG) + wave / SEG;
+  const int NW = gridDim.x * (4 / SEG);
+  const int j = lane & 15;
+  const int jj = lane >> 4;
+  const int nch = K >> 7;
+  const int ngr = max(1, nch >> gshift);
+  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int rdiag = j & 3;
+  const bool diag = jj == (j >> 2);
+  const int woff = w3_first_word(jj);
+
+  int goff[SP];
+  bool gval[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    const int g = 16 * (seg * SP + s) + j;
+    gval[s] = FULL || g < nch;
+    goff[s] = FULL ? g : min(g, nch - 1);
+  }
+
+  // operand prep: item t = (token row, piece, lane) builds that lane's 40
+  // activation slots as in the int3 M = 1 kernel. It runs before the row
+  // loop: run after the first ring loads (as in the other decode kernels),
+  // the form with 2 token rows, 2 pieces per wavefront, two wavefronts per
+  // row and whole pieces gave wrong, run-to-run varying sums for the first
+  // token row; no cause was found in its LDS addressing, barriers or waits.
+  constexpr int NI = MT * NP * 64;
+  constexpr int XI = (NI + 255) / 256;
+  u32x4 av[MT][SP][5];
+  float cC[MT][SP], cS[MT][SP];
+  auto prep = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+      const int t = (int)threadIdx.x + 256 * u;
+      if (t < NI) {  // wave-uniform: NI is a multiple of 64
+        const int tk = t / (NP * 64), ps = (t >> 6) % NP, pl = t & 63;
+        const int pq = pl >> 4;
+        const int g = min(16 * ps + (pl & 15), nch - 1);
+        const int pw = w3_first_word(pq);
+        // dwords 5 pw .. 5 pw + 19 of the group's 64 (codes 10 pw .. 10 pw + 39)
+        const uint32_t* xg = reinterpret_cast<const uint32_t*>(X + (size_t)tk * K + (size_t)g * 128);
+        uint32_t xd[20];
+#pragma unroll
+        for (int i = 0; i < 20; ++i) xd[i] = xg[min(5 * pw + i, 63)];
+        const int wlo = pq == 3 ? 1 : 0, whi = pq == 1 || pq == 2 ? 3 : 4;  // used words
+        uint32_t ap[20];
+        float cs = 0.f, ss = 0.f;
+#pragma unroll
+        for (int P = 0; P < 20; ++P) {
+          const int w = P / 5, p = P % 5;
+          const bool use = w >= wlo && w < whi;
+          const int cl = 10 * w + kW3Lo[p], ch = 10 * w + kW3Hi[p];
+          const float xl = h2f((uint16_t)(xd[cl >> 1] >> (16 * (cl & 1))));
+          const float xh = h2f((uint16_t)(xd[ch >> 1] >> (16 * (ch & 1))));
+          // a code past the group's 128 only occurs for word 12 (c8, c9)
+          const bool lo_ok = use && 10 * (pw + w) + kW3Lo[p] < 128;
+          const bool hi_ok = use && 10 * (pw + w) + kW3Hi[p] < 128;
+          const __half al = __float2half_rn(lo_ok ? xl * kW3InvLo[p] : 0.f);
+          const __half ah = __float2half_rn(hi_ok ? xh * kW3InvHi[p] : 0.f);
+          ap[P] = (uint32_t)__half_as_ushort(al) | ((uint32_t)__half_as_ushort(ah) << 16);
+          const float fl = __half2float(al), fh = __half2float(ah);
+          cs += fl + fh;
+          ss += fl * (1.f / kW3InvLo[p]) + fh * (1.f / kW3InvHi[p]);
+        }
+        cs += __shfl_xor(cs, 16);
+        ss += __shfl_xor(ss, 16);
+        cs += __shfl_xor(cs, 32);
+        ss += __shfl_xor(ss, 32);
+        u32x4* xo = xs + (size_t)(tk * NP + ps) * 5 * 64 + pl;
+#pragma unroll
+        for (int o = 0; o < 5; ++o)
+          xo[64 * o] = u32x4{ap[4 * o], ap[4 * o + 1], ap[4 * o + 2], ap[4 * o + 3]};
+        if (pl < 16) xcs[(tk * NP + ps) * 16 + pl] = make_float2(1024.f * cs, ss);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tk = 0; tk < MT; ++tk)
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        const int ps = tk * NP + seg * SP + s;
+#pragma unroll
+        for (int o = 0; o < 5; ++o) av[tk][s][o] = xs[(size_t)(ps * 5 + o) * 64 + lane];
+        const float2 v = xcs[ps * 16 + j];
+        cC[tk][s] = v.x;
+        cS[tk][s] = v.y;
+      }
+  };
+  prep();
+
+  // a ring of one row, no prologue loads (see the int4 M = 1 kernel)
+  u32x4 wb[SP];
+  float db[SP];
+  uint32_t zb[SP];
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    wb[s] = u32x4{0, 0, 0, 0};
+    db[s] = 0.f;
+    zb[s] = 0u;
+  }
+  const uint32_t magic = kMagic2;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* qlane = Q + woff;
+  float outv[MT];
+#pragma unroll
+  for (int tk = 0; tk < MT; ++tk) outv[tk] = 0.f;
+  for (int row = -1; row < cnt; ++row) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (row >= 0) {  // uniform
+      float y[MT];
+#pragma unroll
+      for (int tk = 0; tk < MT; ++tk) y[tk] = 0.f;
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        const u32x4 w = wb[s];
+        const float dd = gval[s] ? db[s] : 0.f;
+        const float zf = (float)zb[s];
+        uint32_t pr[20];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t x = w[q];
+          const uint32_t t8 = x >> 8, u1 = x << 1;
+          pr[5 * q + 0] = and_or(x, 0x001C0007u, magic);
+          pr[5 * q + 1] = and_or(x, 0x00E00038u, magic);
+          pr[5 * q + 2] = and_or(t8, 0x0007000Eu, magic);
+          pr[5 * q + 3] = and_or(t8, 0x00380070u, magic);
+          pr[5 * q + 4] = and_or(u1, 0x00070380u, magic);
+        }
+#pragma unroll
+        for (int tk = 0; tk < MT; ++tk) {
+          floatx4 acc = mfma16(av[tk][s][0], u32x4{pr[0], pr[1], pr[2], pr[3]}, zero4);
+          acc = mfma16(av[tk][s][1], u32x4{pr[4], pr[5], pr[6], pr[7]}, acc);
+          acc = mfma16(av[tk][s][2], u32x4{pr[8], pr[9], pr[10], pr[11]}, acc);
+          acc = mfma16(av[tk][s][3], u32x4{pr[12], pr[13], pr[14], pr[15]}, acc);
+          acc = mfma16(av[tk][s][4], u32x4{pr[16], pr[17], pr[18], pr[19]}, acc);
+          float v = acc[0];
+          v = rdiag == 1 ? acc[1] : v;
+          v = rdiag == 2 ? acc[2] : v;
+          v = rdiag == 3 ? acc[3] : v;
+          const float zs = __builtin_fmaf(zf, cS[tk][s], cC[tk][s]);
+          y[tk] = __builtin_fmaf(dd, v - zs, y[tk]);
+        }
+      }
+#pragma unroll
+      for (int tk = 0; tk < MT; ++tk) {
+        float v = diag ? y[tk] : 0.f;
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0xB1, 0xF, 0xF, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                0x4E, 0xF, 0xF, true));
+        const float sum =
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
+            (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
+        outv[tk] = (row & 63) == lane ? sum : outv[tk];
+      }
+    }
+    if (row + 1 < cnt) {  // uniform: refill with the next row's pieces
+      const size_t nn = (size_t)gw + (size_t)(row + 1) * NW;
+      const uint32_t* qn = qlane + nn * wpr;
+#pragma unroll
+      for (int s = 0; s < SP; ++s) {
+        const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
+        wb[s] = u32x4{v[0], v[1], v[2], v[3]};
+        db[s] = group_scale<CS>(S, nn, ngr, goff[s] >> gshift);
+        zb[s] = group_zero<CS>(Z, nn, ngr, goff[s] >> gshift);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+  if constexpr (SEG > 1) {  // the row sums: segment 0 plus segment 1
+#pragma unroll
+    for (int tk = 0; tk < MT; ++tk) segp[(wave * MT + tk) * 64 + lane] = outv[tk];
+    __syncthreads();
+    if (seg == 0) {
+#pragma unroll
+      for (int tk = 0; tk < MT; ++tk) outv[tk] += segp[((wave + 1) * MT + tk) * 64 + lane];
+    }
+  }
+#pragma unroll
+  for (int tk = 0; tk < MT; ++tk)
+    if (seg == 0 && lane < cnt)
+      Y[(size_t)tk * N + gw + (size_t)lane * NW] = __half_as_ushort(__float2half_rn(outv[tk]));
+}
+
+// 2 <= M <= 4, int3: all token rows in one launch when their operands fit
+// the registers (M x pieces per wavefront <= kW3MtMaxItems, with two
+// wavefronts per row past that; 8 would need 268-324 registers), else in
+// launches of two token rows and a last single row (each reading the
+// weights once).
+constexpr int kW3MtMaxItems = 6;
+
+template <bool CS>
+hipError_t launch_gemv_w3_mt_one(const uint16_t* x, const uint32_t* q, const void* scales,
+                                 const void* zeros, int M, int N, int K, int wpr, int gshift,
+                                 uint16_t* y, hipStream_t st, int sp, int seg) {
+  const int nch = K / 128;
+  const int nrw = min(N, max(cu_count() * 8 / seg, (N + 63) / 64));  // row wavefronts
+  const dim3 g1((unsigned)((nrw * seg + 3) / 4)), block(256);
+  const bool full = nch == 16 * sp * seg;
+  const size_t lds = w3mt_lds_bytes(M, sp * seg, seg);
+#define AWQ_W3MTF(MV, SM, F, SG)                                                               \
+  do {                                                                                         \
+    const void* fn = (const void*)gemv_w3_mt_kernel<MV, SM, F, CS, SG>;                        \
+    if (lds > 64 * 1024) {                                                                     \
+      const hipError_t ea =                                                                    \
+          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);       \
+      if (ea != hipSuccess) return ea;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((gemv_w3_mt_kernel<MV, SM, F, CS, SG>), g1, block, lds, st, x, q,       \
+                       scales, zeros, y, N, K, wpr, gshift);                                   \
+  } while (0)
+#define AWQ_W3MT(MV, SM, SG)                \
+  do {                                      \
+    if (full) AWQ_W3MTF(MV, SM, true, SG);  \
+    else AWQ_W3MTF(MV, SM, false, SG);      \
+  } while (0)
+  if (seg == 1) {
+    if (M == 2) {
+      if (sp == 1) AWQ_W3MT(2, 1, 1);
+      else if (sp == 2) AWQ_W3MT(2, 2, 1);
+      else AWQ_W3MT(2, 3, 1);
+    } else if (M == 3) {
+      if (sp == 1) AWQ_W3MT(3, 1, 1);
+      else AWQ_W3MT(3, 2, 1);
+    } else {
+      AWQ_W3MT(4, 1, 1);
+    }
+  } else {
+    if (M == 2) {
+      if (sp == 2) AWQ_W3MT(2, 2, 2);
+      else AWQ_W3MT(2, 3, 2);
+    } else if (M == 3) {
+      AWQ_W3MT(3, 2, 2);
+    } else {
+      AWQ_W3MT(4, 1, 2);
+    }
+  }
+#undef AWQ_W3MT
+#undef AWQ_W3MTF
+  return hipGetLastError();
+}
+
+template <bool CS>
+hipError_t launch_gemv_w3_mt_t(const __half* X, const uint32_t* q, const void* scales,
+                               const void* zeros, int M, int N, int K, int group, __half* Y,
+                               hipStream_t st) {
+  if (M < 2 || M > 4) return hipErrorNotSupported;
+  const int nch = K / 128;
+  const int np = (nch + 15) / 16;  // pieces of a row
+  // wavefronts per row and pieces per wavefront for m token rows, or false
+  auto shape = [&](int m, int& sp, int& seg) {
+    seg = m * np <= kW3MtMaxItems ? 1 : 2;
+    sp = (np + seg - 1) / seg;
+    return m * sp <= kW3MtMaxItems;
+  };
+  const int gshift = group_shift(group);
+  const int wpr = words_per_row(K, 3, group);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  int sp = 0, seg = 1;
+  if (shape(M, sp, seg))
+    return launch_gemv_w3_mt_one<CS>(x, q, scales, zeros, M, N, K, wpr, gshift, y, st, sp, seg);
+  // pairs of token rows, and the M = 1 kernel for an odd last row (decided
+  // before anything is launched)
+  if (!shape(2, sp, seg) || ((M & 1) != 0 && np > 6)) return hipErrorNotSupported;
+  for (int m0 = 0; m0 + 1 < M; m0 += 2) {
+    const hipError_t e = launch_gemv_w3_mt_one<CS>(x + (size_t)m0 * K, q, scales, zeros, 2, N, K,
+                                                   wpr, gshift, y + (size_t)m0 * N, st, sp, seg);
+    if (e != hipSuccess) return e;
+  }
+  if ((M & 1) != 0)
+    return launch_gemv_w3_m1_t<CS>(X + (size_t)(M - 1) * K, q, scales, zeros, N, K, group,
+                                   Y + (size_t)(M - 1) * N, st);
+  return hipSuccess;
+}
+
+hipError_t launch_gemv_w3_mt(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st, bool cs) {
+  return cs ? launch_gemv_w3_mt_t<true>(X, q, scales, zeros, M, N, K, group, Y, st)
+            : launch_gemv_w3_mt_t<false>(X, q, scales, zeros, M, N, K, group, Y, st);
+}
+
+// ---------------------------------------------------------------------------
 // Decode, int4, 2 <= M <= 16 (gemv_w4_mx_kernel). K is covered in NP passes
 // of PC 128-code chunks (one pass unless K > 8192). In a pass a workgroup of
 // WV <= 8 wavefronts splits the pass's chunks into WV slices of CPW chunks;
