@@ -32,7 +32,7 @@ def test_compact_params_exact(bits, group, K):
 
 
 CASES = [(4, 128, 4096, 300), (4, 256, 2048, 130), (4, -1, 4096, 130), (3, 128, 4096, 130),
-         (3, -1, 11008, 64), (4, 128, 11008, 64), (4, 128, 28672, 40)]
+         (3, -1, 11008, 64), (4, 128, 11008, 64), (4, 128, 28672, 40), (3, 128, 28672, 40)]
 
 
 @pytest.mark.parametrize("bits,group,K,N", CASES)

@@ -284,6 +284,23 @@ def test_decode_int3_few_token_rows(M, N, K, group):
         assert_same_bits(host(awq.w4a16_matmul(dev(X), q, sc, z, 3, group)), Y)
 
 
+@pytest.mark.parametrize("N,K,group", [(37, 14336, 128), (64, 16384, 256), (21, 20480, 128),
+                                       (30, 24576, -1), (19, 26624, 128), (70, 28672, 128),
+                                       (33, 28672, 512), (25, 30720, 128)])
+def test_decode_int3_m1_long_rows(N, K, group):
+    """int3 at M = 1 on rows of 7 to 15 pieces of 16 groups: two wavefronts
+    per row (an empty last piece at 26624), the prefill kernel past 14."""
+    say("decode int3 M=1 long rows", N, K, group)
+    W = datagen.random_f16((N, K), 0.02, seed=N + 3 * K)
+    s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 13)
+    X = datagen.random_f16((1, K), 1.0, seed=K + 5)
+    g = K if group == -1 else group
+    q, sc, z = _packed(W, s, 3, group)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z, 3, group))
+    qo, so, zo = O.quantize_pack(W, s, 3, g)
+    assert_rows_close(Y, O.matmul(X, qo, so, zo, 3, g, K))
+
+
 def test_decode_int4_long_k_many_row_blocks():
     """Several row blocks per workgroup over two passes (N = 8200 gives 513
     row blocks); every row of a sample checked."""

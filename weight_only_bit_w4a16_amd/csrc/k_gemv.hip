@@ -1006,12 +1006,17 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
 }
 
 template <bool CS>
+hipError_t launch_gemv_w3_m1_long(const __half* X, const uint32_t* q, const void* scales,
+                                  const void* zeros, int N, int K, int group, __half* Y,
+                                  hipStream_t st);
+
+template <bool CS>
 hipError_t launch_gemv_w3_m1_t(const __half* X, const uint32_t* q, const void* scales,
                                const void* zeros, int N, int K, int group, __half* Y,
                                hipStream_t st) {
   const int nch = K / 128;
   const int sp = (nch + 15) / 16;
-  if (sp > 6) return hipErrorNotSupported;
+  if (sp > 6) return launch_gemv_w3_m1_long<CS>(X, q, scales, zeros, N, K, group, Y, st);
   const int gshift = group_shift(group);
   const int wpr = words_per_row(K, 3, group);
   // wavefronts per compute unit: 3 per SIMD for rows of two pieces, else 2
@@ -1275,7 +1280,10 @@ hipError_t launch_gemv_w3_mt_one(const uint16_t* x, const uint32_t* q, const voi
                                  const void* zeros, int M, int N, int K, int wpr, int gshift,
                                  uint16_t* y, hipStream_t st, int sp, int seg) {
   const int nch = K / 128;
-  const int nrw = min(N, max(cu_count() * 8 / seg, (N + 63) / 64));  // row wavefronts
+  // 2 wavefronts per SIMD; 1 past 6 token-row pieces (M = 1 on 13-14
+  // pieces: 253-270 registers)
+  const int wpc = M * sp > 6 ? 4 : 8;
+  const int nrw = min(N, max(cu_count() * wpc / seg, (N + 63) / 64));  // row wavefronts
   const dim3 g1((unsigned)((nrw * seg + 3) / 4)), block(256);
   const bool full = nch == 16 * sp * seg;
   const size_t lds = w3mt_lds_bytes(M, sp * seg, seg);
@@ -1295,7 +1303,12 @@ hipError_t launch_gemv_w3_mt_one(const uint16_t* x, const uint32_t* q, const voi
     if (full) AWQ_W3MTF(MV, SM, true, SG);  \
     else AWQ_W3MTF(MV, SM, false, SG);      \
   } while (0)
-  if (seg == 1) {
+  if (M == 1) {  // rows of 7-14 pieces, two wavefronts per row
+    if (sp == 4) AWQ_W3MT(1, 4, 2);
+    else if (sp == 5) AWQ_W3MT(1, 5, 2);
+    else if (sp == 6) AWQ_W3MT(1, 6, 2);
+    else AWQ_W3MT(1, 7, 2);
+  } else if (seg == 1) {
     if (M == 2) {
       if (sp == 1) AWQ_W3MT(2, 1, 1);
       else if (sp == 2) AWQ_W3MT(2, 2, 1);
@@ -1353,6 +1366,19 @@ hipError_t launch_gemv_w3_mt_t(const __half* X, const uint32_t* q, const void* s
     return launch_gemv_w3_m1_t<CS>(X + (size_t)(M - 1) * K, q, scales, zeros, N, K, group,
                                    Y + (size_t)(M - 1) * N, st);
   return hipSuccess;
+}
+
+// M = 1 on rows of 7-14 pieces (K up to 28672): the few-token kernel with
+// one token row and two wavefronts per row (the M = 1 kernel holds 6 pieces)
+template <bool CS>
+hipError_t launch_gemv_w3_m1_long(const __half* X, const uint32_t* q, const void* scales,
+                                  const void* zeros, int N, int K, int group, __half* Y,
+                                  hipStream_t st) {
+  const int np = (K / 128 + 15) / 16;
+  if (np < 7 || np > 14) return hipErrorNotSupported;
+  return launch_gemv_w3_mt_one<CS>(reinterpret_cast<const uint16_t*>(X), q, scales, zeros, 1, N,
+                                   K, words_per_row(K, 3, group), group_shift(group),
+                                   reinterpret_cast<uint16_t*>(Y), st, (np + 1) / 2, 2);
 }
 
 hipError_t launch_gemv_w3_mt(const __half* X, const uint32_t* q, const void* scales,
