@@ -264,13 +264,15 @@ def test_decode_int4_few_token_rows(M, N, K, group):
                                          (3, 411, 6144, 128), (3, 260, 11008, 128),
                                          (4, 300, 2048, 128), (4, 200, 4096, 512),
                                          (4, 150, 8192, 128), (4, 123, 16384, 128),
-                                         (3, 100, 14336, 128), (2, 5000, 4096, 128)])
+                                         (3, 100, 14336, 128), (2, 5000, 4096, 128),
+                                         (2, 90, 28672, 256)])
 def test_decode_int3_few_token_rows(M, N, K, group):
     """int3 at 2 <= M <= 4: all token rows in one launch while M x pieces per
     wavefront stays within 6 (one wavefront per row, or two from 4096, 6144
     and 8192 on; partial and empty last pieces), pairs of token rows and an
     M = 1 launch for the rest past that (11008 at M = 3, 8192 at M = 4), and
-    the generic kernels past 6 pieces per wavefront (16384, 14336)."""
+    one M = 1 launch per token row on rows of 7 or more pieces (16384,
+    14336)."""
     say("decode int3 few token rows", M, N, K, group)
     W = datagen.random_f16((N, K), 0.02, seed=7 * N + K)
     s = datagen.random_f32_positive(K, 0.3, 4.0, seed=K + 11)

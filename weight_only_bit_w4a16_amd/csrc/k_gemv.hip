@@ -1271,8 +1271,8 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
 // 2 <= M <= 4, int3: all token rows in one launch when their operands fit
 // the registers (M x pieces per wavefront <= kW3MtMaxItems, with two
 // wavefronts per row past that; 8 would need 268-324 registers), else in
-// launches of two token rows and a last single row (each reading the
-// weights once).
+// launches of two token rows and a last single row, or of single token rows
+// (each launch reading the weights once).
 constexpr int kW3MtMaxItems = 6;
 
 template <bool CS>
@@ -1354,17 +1354,26 @@ hipError_t launch_gemv_w3_mt_t(const __half* X, const uint32_t* q, const void* s
   int sp = 0, seg = 1;
   if (shape(M, sp, seg))
     return launch_gemv_w3_mt_one<CS>(x, q, scales, zeros, M, N, K, wpr, gshift, y, st, sp, seg);
-  // pairs of token rows, and the M = 1 kernel for an odd last row (decided
-  // before anything is launched)
-  if (!shape(2, sp, seg) || ((M & 1) != 0 && np > 6)) return hipErrorNotSupported;
-  for (int m0 = 0; m0 + 1 < M; m0 += 2) {
-    const hipError_t e = launch_gemv_w3_mt_one<CS>(x + (size_t)m0 * K, q, scales, zeros, 2, N, K,
-                                                   wpr, gshift, y + (size_t)m0 * N, st, sp, seg);
+  // pairs of token rows and an M = 1 launch for an odd last row, or one M = 1
+  // launch per token row on longer rows (decided before anything is launched;
+  // the M = 1 launches cover rows of up to 14 pieces)
+  const bool single = np <= 14;
+  const bool pairs = shape(2, sp, seg) && ((M & 1) == 0 || single);
+  if (!pairs && !single) return hipErrorNotSupported;
+  int m0 = 0;
+  if (pairs) {
+    for (; m0 + 1 < M; m0 += 2) {
+      const hipError_t e = launch_gemv_w3_mt_one<CS>(x + (size_t)m0 * K, q, scales, zeros, 2, N,
+                                                     K, wpr, gshift, y + (size_t)m0 * N, st, sp,
+                                                     seg);
+      if (e != hipSuccess) return e;
+    }
+  }
+  for (; m0 < M; ++m0) {
+    const hipError_t e = launch_gemv_w3_m1_t<CS>(X + (size_t)m0 * K, q, scales, zeros, N, K,
+                                                 group, Y + (size_t)m0 * N, st);
     if (e != hipSuccess) return e;
   }
-  if ((M & 1) != 0)
-    return launch_gemv_w3_m1_t<CS>(X + (size_t)(M - 1) * K, q, scales, zeros, N, K, group,
-                                   Y + (size_t)(M - 1) * N, st);
   return hipSuccess;
 }
 
