@@ -73,6 +73,25 @@ def test_gate_up_small(bits, M, N, K):
     assert_gate_up_close(_run(X, g, u, bits, 128), X, g, u, bits, 128, K)
 
 
+@pytest.mark.parametrize("bits,M,N,K", [(4, 2, 70, 2048), (4, 2, 6200, 4096), (4, 2, 300, 8192),
+                                        (4, 3, 6200, 4096), (4, 4, 33, 4096), (3, 2, 129, 6016),
+                                        (3, 3, 77, 3968), (3, 4, 300, 2048), (3, 4, 90, 4096),
+                                        (3, 3, 60, 6016), (3, 3, 40, 8192), (3, 3, 50, 11008)])
+def test_gate_up_few_token_rows(bits, M, N, K):
+    """2 <= M <= 4: the few-token kernels in their gated form (gate and up
+    rows alternate; int4 at M = 2, int3 at M = 2-4 while the operands fit),
+    partial last pieces, int3 pairs of token rows (4096 at M = 4) and an
+    M = 1 launch for an odd last row (6016 at M = 3), the prefill kernel past
+    that (8192, 11008 at M = 3) and the 16-row-block kernel for int4 at
+    M = 3, 4."""
+    say("gate_up few token rows", bits, M, N, K)
+    g, u, _ = _pair(N, K, bits, 128, seed=N + 3 * K)
+    X = datagen.random_f16((M, K), 1.0, seed=M + K)
+    Y = _run(X, g, u, bits, 128)
+    assert_gate_up_close(Y, X, g, u, bits, 128, K)
+    assert np.array_equal(_run(X, g, u, bits, 128).view(np.uint16), Y.view(np.uint16))
+
+
 @pytest.mark.parametrize("group", [256, 512])
 @pytest.mark.parametrize("M", [1, 33])
 def test_gate_up_int4_larger_groups(group, M):

@@ -265,8 +265,12 @@ awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const f
   if (M == 1)
     e = bits == 4 ? awq::launch_gate_up_w4_m1(x, qg, sg, zg, qu, su, zu, N, K, g, y, s)
                   : awq::launch_gate_up_w3_m1(x, qg, sg, zg, qu, su, zu, N, K, g, y, s);
-  else if (bits == 4 && M <= 16)
+  else if (M <= 4)
+    e = awq::launch_gate_up_mt(x, qg, sg, zg, qu, su, zu, M, N, K, bits, g, y, s);
+  if (e == hipErrorNotSupported && bits == 4 && M >= 2 && M <= 16) {
+    (void)hipGetLastError();
     e = awq::launch_gemv_w4_mx(x, qg, sg, zg, M, N, K, g, y, s, qu, su, zu, false);
+  }
   if (e == hipErrorNotSupported) {
     (void)hipGetLastError();
     e = awq::launch_gemm_gate_up(x, qg, sg, zg, qu, su, zu, M, N, K, bits, g, y, s);

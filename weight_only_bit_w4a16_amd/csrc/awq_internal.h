@@ -85,6 +85,12 @@ hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const void* sca
                              const void* zeros2, bool cs);
 // gated MLP: Y = fp16(silu(X Wg^T) * (X Wu^T)), plain storage; M = 1 int4 /
 // int3 decode (K up to 96 blocks), and the prefill kernel for any M
+// fused gate/up, 2 <= M <= 4 on rows of few pieces (hipErrorNotSupported,
+// with nothing launched, otherwise)
+hipError_t launch_gate_up_mt(const __half* X, const uint32_t* qg, const float* sg,
+                             const uint8_t* zg, const uint32_t* qu, const float* su,
+                             const uint8_t* zu, int M, int N, int K, int bits, int group,
+                             __half* Y, hipStream_t st);
 hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float* sg,
                                 const uint8_t* zg, const uint32_t* qu, const float* su,
                                 const uint8_t* zu, int N, int K, int group, __half* Y,

@@ -591,10 +591,12 @@ constexpr size_t mt_lds_bytes(int mt, int np, int seg) {
   return (size_t)mt * np * (4 * 64 * 16 + 16 * 8) + (seg > 1 ? (size_t)4 * mt * 64 * 4 : 0);
 }
 
-template <int MT, int SP, bool FULL, bool CS, int SEG>
+template <int MT, int SP, bool FULL, bool CS, int SEG, bool DUAL = false>
 __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
-    const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int gshift) {
+    const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int gshift,
+    const uint32_t* __restrict__ Q2, const void* __restrict__ S2, const void* __restrict__ Z2) {
+  static_assert(!DUAL || SEG == 1, "the gated form: one wavefront per row");
   static_assert(SEG == 1 || SEG == 2, "one or two wavefronts per row");
   constexpr int NP = SP * SEG;  // pieces of a row
   extern __shared__ __align__(16) uint8_t smem[];
@@ -695,10 +697,15 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
   const uint32_t magic = kMagic2;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + 16 * j + 4 * jj;
+  const uint32_t* qlane2 = DUAL ? Q2 + (qlane - Q) : qlane;
+  const int items = DUAL ? 2 * cnt : cnt;  // rows, or gate/up row pairs
+  float gsum[MT];  // DUAL: the gate sums of the current row
+#pragma unroll
+  for (int tk = 0; tk < MT; ++tk) gsum[tk] = 0.f;
   float outv[MT];
 #pragma unroll
   for (int tk = 0; tk < MT; ++tk) outv[tk] = 0.f;
-  for (int row = -1; row < cnt; ++row) {
+  for (int row = -1; row < items; ++row) {  // row: item
     __builtin_amdgcn_sched_barrier(0);
     if (row >= 0) {  // uniform
       float y[MT];
@@ -747,17 +754,30 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
             (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
-        outv[tk] = (row & 63) == lane ? sum : outv[tk];
+        if constexpr (DUAL) {
+          if ((row & 1) == 0) {  // uniform: the gate item waits for its up item
+            gsum[tk] = sum;
+          } else {
+            const float val = silu_f(gsum[tk]) * sum;
+            outv[tk] = ((row >> 1) & 63) == lane ? val : outv[tk];
+          }
+        } else {
+          outv[tk] = (row & 63) == lane ? sum : outv[tk];
+        }
       }
     }
-    if (row + 1 < cnt) {  // uniform: refill with the next row's pieces
-      const size_t nn = (size_t)gw + (size_t)(row + 1) * NW;
-      const uint32_t* qn = qlane + nn * wpr;
+    if (row + 1 < items) {  // uniform: refill with the next item's pieces
+      const int nit = row + 1;
+      const bool up = DUAL && (nit & 1) != 0;
+      const size_t nn = (size_t)gw + (size_t)(DUAL ? nit >> 1 : nit) * NW;
+      const uint32_t* qn = (up ? qlane2 : qlane) + nn * wpr;
+      const void* Sp = up ? S2 : S;
+      const void* Zp = up ? Z2 : Z;
 #pragma unroll
       for (int s = 0; s < SP; ++s) {
         wb[s] = ld_nt(reinterpret_cast<const u32x4*>(qn + 16 * (goff[s] - j)));
-        db[s] = group_scale<CS>(S, nn, ngr, goff[s] >> gshift);
-        zb[s] = group_zero<CS>(Z, nn, ngr, goff[s] >> gshift);
+        db[s] = group_scale<CS>(Sp, nn, ngr, goff[s] >> gshift);
+        zb[s] = group_zero<CS>(Zp, nn, ngr, goff[s] >> gshift);
       }
     }
     // keeps the refill loads out of the loop head (see the M = 1 kernel)
@@ -1069,10 +1089,12 @@ constexpr size_t w3mt_lds_bytes(int mt, int np, int seg) {
   return (size_t)mt * np * (5 * 64 * 16 + 16 * 8) + (seg > 1 ? (size_t)4 * mt * 64 * 4 : 0);
 }
 
-template <int MT, int SP, bool FULL, bool CS, int SEG>
+template <int MT, int SP, bool FULL, bool CS, int SEG, bool DUAL = false>
 __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
-    const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int wpr, int gshift) {
+    const void* __restrict__ Z, uint16_t* __restrict__ Y, int N, int K, int wpr, int gshift,
+    const uint32_t* __restrict__ Q2, const void* __restrict__ S2, const void* __restrict__ Z2) {
+  static_assert(!DUAL || SEG == 1, "the gated form: one wavefront per row");
   static_assert(SEG == 1 || SEG == 2, "one or two wavefronts per row");
   constexpr int NP = SP * SEG;  // pieces of a row
   extern __shared__ __align__(16) uint8_t smem[];
@@ -1185,10 +1207,15 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
   const uint32_t magic = kMagic2;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + woff;
+  const uint32_t* qlane2 = DUAL ? Q2 + (qlane - Q) : qlane;
+  const int items = DUAL ? 2 * cnt : cnt;  // rows, or gate/up row pairs
+  float gsum[MT];  // DUAL: the gate sums of the current row
+#pragma unroll
+  for (int tk = 0; tk < MT; ++tk) gsum[tk] = 0.f;
   float outv[MT];
 #pragma unroll
   for (int tk = 0; tk < MT; ++tk) outv[tk] = 0.f;
-  for (int row = -1; row < cnt; ++row) {
+  for (int row = -1; row < items; ++row) {  // row: item
     __builtin_amdgcn_sched_barrier(0);
     if (row >= 0) {  // uniform
       float y[MT];
@@ -1237,18 +1264,31 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 20))) +
             (__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 40)) +
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 60)));
-        outv[tk] = (row & 63) == lane ? sum : outv[tk];
+        if constexpr (DUAL) {
+          if ((row & 1) == 0) {  // uniform: the gate item waits for its up item
+            gsum[tk] = sum;
+          } else {
+            const float val = silu_f(gsum[tk]) * sum;
+            outv[tk] = ((row >> 1) & 63) == lane ? val : outv[tk];
+          }
+        } else {
+          outv[tk] = (row & 63) == lane ? sum : outv[tk];
+        }
       }
     }
-    if (row + 1 < cnt) {  // uniform: refill with the next row's pieces
-      const size_t nn = (size_t)gw + (size_t)(row + 1) * NW;
-      const uint32_t* qn = qlane + nn * wpr;
+    if (row + 1 < items) {  // uniform: refill with the next item's pieces
+      const int nit = row + 1;
+      const bool up = DUAL && (nit & 1) != 0;
+      const size_t nn = (size_t)gw + (size_t)(DUAL ? nit >> 1 : nit) * NW;
+      const uint32_t* qn = (up ? qlane2 : qlane) + nn * wpr;
+      const void* Sp = up ? S2 : S;
+      const void* Zp = up ? Z2 : Z;
 #pragma unroll
       for (int s = 0; s < SP; ++s) {
         const u32x4a4 v = ld_nt(reinterpret_cast<const u32x4a4*>(qn + 13 * goff[s]));
         wb[s] = u32x4{v[0], v[1], v[2], v[3]};
-        db[s] = group_scale<CS>(S, nn, ngr, goff[s] >> gshift);
-        zb[s] = group_zero<CS>(Z, nn, ngr, goff[s] >> gshift);
+        db[s] = group_scale<CS>(Sp, nn, ngr, goff[s] >> gshift);
+        zb[s] = group_zero<CS>(Zp, nn, ngr, goff[s] >> gshift);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1296,7 +1336,7 @@ hipError_t launch_gemv_w3_mt_one(const uint16_t* x, const uint32_t* q, const voi
       if (ea != hipSuccess) return ea;                                                         \
     }                                                                                          \
     hipLaunchKernelGGL((gemv_w3_mt_kernel<MV, SM, F, CS, SG>), g1, block, lds, st, x, q,       \
-                       scales, zeros, y, N, K, wpr, gshift);                                   \
+                       scales, zeros, y, N, K, wpr, gshift, nullptr, nullptr, nullptr);        \
   } while (0)
 #define AWQ_W3MT(MV, SM, SG)                \
   do {                                      \
@@ -1772,7 +1812,7 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
       if (ea != hipSuccess) return ea;                                                         \
     }                                                                                          \
     hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, F, CS, SG>), g1, block, lds, st, x, q,       \
-                       scales, zeros, y, N, K, gshift);                                        \
+                       scales, zeros, y, N, K, gshift, nullptr, nullptr, nullptr);             \
   } while (0)
 #define AWQ_MT(MV, SM, SG)                \
   do {                                    \
@@ -1923,6 +1963,99 @@ hipError_t launch_gate_up_w4_m1(const __half* X, const uint32_t* qg, const float
     default: AWQ_GU(6, 2); break;
   }
 #undef AWQ_GU
+  return hipGetLastError();
+}
+
+// Fused gate/up decode at 2 <= M <= 4 on rows of few pieces: the few-token
+// kernels in their gated form (one wavefront per row; items alternate gate
+// and up rows). int4 at M = 2 only (event timing over rotated weights:
+// 2 x 4096 x 11008 18.9 -> 17.8 us, 2 x 8192 x 28672 66 -> 58 us at M = 2,
+// while M = 3, 4 got slower than the 16-row-block kernel: 18.9 -> 20.6,
+// 20.0 -> 22.5 us); int3 whenever the operands fit (2 x 4096 x 11008 M = 2
+// 56.8 -> 18.8 us, M = 3 54.8 -> 20.6 us against the prefill kernel), else
+// in pairs of token rows and an M = 1 launch.
+hipError_t launch_gate_up_w3_m1(const __half* X, const uint32_t* qg, const float* sg,
+                                const uint8_t* zg, const uint32_t* qu, const float* su,
+                                const uint8_t* zu, int N, int K, int group, __half* Y,
+                                hipStream_t st);
+
+hipError_t launch_gate_up_mt(const __half* X, const uint32_t* qg, const float* sg,
+                             const uint8_t* zg, const uint32_t* qu, const float* su,
+                             const uint8_t* zu, int M, int N, int K, int bits, int group,
+                             __half* Y, hipStream_t st) {
+  if (M < 2 || M > 4 || (bits == 4 && M != 2)) return hipErrorNotSupported;
+  const int nch = K / 128;
+  const int np = (nch + 15) / 16;
+  const int cap = bits == 4 ? kMtMaxItems : kW3MtMaxItems;
+  if (M * np > cap) {
+    // int3: pairs of token rows and an M = 1 launch (decided before anything
+    // is launched; the M = 1 gated kernel holds 6 pieces)
+    if (bits != 3 || 2 * np > cap || ((M & 1) != 0 && np > 6)) return hipErrorNotSupported;
+    for (int m0 = 0; m0 + 1 < M; m0 += 2) {
+      const hipError_t e = launch_gate_up_mt(X + (size_t)m0 * K, qg, sg, zg, qu, su, zu, 2, N, K,
+                                             bits, group, Y + (size_t)m0 * N, st);
+      if (e != hipSuccess) return e;
+    }
+    if ((M & 1) != 0)
+      return launch_gate_up_w3_m1(X + (size_t)(M - 1) * K, qg, sg, zg, qu, su, zu, N, K, group,
+                                  Y + (size_t)(M - 1) * N, st);
+    return hipSuccess;
+  }
+  const int wpc = bits == 4 && M * np <= 4 ? 12 : 8;
+  const int nw = max(cu_count() * wpc, (N + 63) / 64);
+  const dim3 g1((unsigned)((min(N, nw) + 3) / 4)), block(256);
+  const bool full = nch == 16 * np;
+  const int gshift = group_shift(group);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(X);
+  uint16_t* y = reinterpret_cast<uint16_t*>(Y);
+  if (bits == 4) {
+    const size_t lds = mt_lds_bytes(M, np, 1);
+#define AWQ_GUMT(MV, SM)                                                                         \
+  do {                                                                                           \
+    if (full)                                                                                    \
+      hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, true, false, 1, true>), g1, block, lds, st, \
+                         x, qg, sg, zg, y, N, K, gshift, qu, su, zu);                            \
+    else                                                                                         \
+      hipLaunchKernelGGL((gemv_w4_mt_kernel<MV, SM, false, false, 1, true>), g1, block, lds,    \
+                         st, x, qg, sg, zg, y, N, K, gshift, qu, su, zu);                        \
+  } while (0)
+    if (M == 2) {
+      if (np == 1) AWQ_GUMT(2, 1);
+      else if (np == 2) AWQ_GUMT(2, 2);
+      else if (np == 3) AWQ_GUMT(2, 3);
+      else AWQ_GUMT(2, 4);
+    } else if (M == 3) {
+      if (np == 1) AWQ_GUMT(3, 1);
+      else AWQ_GUMT(3, 2);
+    } else {
+      if (np == 1) AWQ_GUMT(4, 1);
+      else AWQ_GUMT(4, 2);
+    }
+#undef AWQ_GUMT
+  } else {
+    const int wpr = words_per_row(K, 3, group);
+    const size_t lds = w3mt_lds_bytes(M, np, 1);
+#define AWQ_GUMT3(MV, SM)                                                                        \
+  do {                                                                                           \
+    if (full)                                                                                    \
+      hipLaunchKernelGGL((gemv_w3_mt_kernel<MV, SM, true, false, 1, true>), g1, block, lds, st, \
+                         x, qg, sg, zg, y, N, K, wpr, gshift, qu, su, zu);                       \
+    else                                                                                         \
+      hipLaunchKernelGGL((gemv_w3_mt_kernel<MV, SM, false, false, 1, true>), g1, block, lds,    \
+                         st, x, qg, sg, zg, y, N, K, wpr, gshift, qu, su, zu);                   \
+  } while (0)
+    if (M == 2) {
+      if (np == 1) AWQ_GUMT3(2, 1);
+      else if (np == 2) AWQ_GUMT3(2, 2);
+      else AWQ_GUMT3(2, 3);
+    } else if (M == 3) {
+      if (np == 1) AWQ_GUMT3(3, 1);
+      else AWQ_GUMT3(3, 2);
+    } else {
+      AWQ_GUMT3(4, 1);
+    }
+#undef AWQ_GUMT3
+  }
   return hipGetLastError();
 }
 
