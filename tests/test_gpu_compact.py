@@ -36,7 +36,7 @@ CASES = [(4, 128, 4096, 300), (4, 256, 2048, 130), (4, -1, 4096, 130), (3, 128, 
 
 
 @pytest.mark.parametrize("bits,group,K,N", CASES)
-@pytest.mark.parametrize("M,kernel", [(1, awq.KERNEL_AUTO), (3, awq.KERNEL_AUTO),
+@pytest.mark.parametrize("M,kernel", [(1, awq.KERNEL_AUTO), (2, awq.KERNEL_AUTO), (3, awq.KERNEL_AUTO),
                                       (8, awq.KERNEL_AUTO), (40, awq.KERNEL_AUTO),
                                       (5, awq.KERNEL_DECODE_EXACT), (2, awq.KERNEL_DECODE),
                                       (16, awq.KERNEL_PREFILL)])
