@@ -12,6 +12,20 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// A value in an SGPR (in_sgpr) or a VGPR (in_vgpr) that the compiler cannot
+// see through: the empty asm emits no instruction, so the register is
+// written by the compiler's own move. Used to give three-operand VALU
+// instructions their constants in registers, since a VOP3 encoding takes no
+// literal on gfx950.
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t c) {
+  asm("" : "=s"(c) : "0"(c));
+  return c;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  asm("" : "=v"(c) : "0"(c));
+  return c;
+}
+
 // fp16 bit pattern of 1024.0: OR-ing a code c << e (e + bits <= 10) into its
 // mantissa gives the fp16 value 1024 + c * 2^e exactly.
 constexpr uint32_t kMagic2 = 0x64006400u;

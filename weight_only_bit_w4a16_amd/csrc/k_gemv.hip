@@ -92,10 +92,15 @@ __device__ __forceinline__ void load_x32(const uint16_t* p, uint32_t* d) {
 // ---------------------------------------------------------------------------
 enum { kOffset = 0, kExact = 1 };
 
+// (a & m) | o as one v_and_or_b32, with the mask in an SGPR (and the caller's
+// o in a VGPR, see in_vgpr): a VOP3 instruction takes no literal on gfx950,
+// so with both constants visible the compiler would emit an AND and an OR.
+// The instruction itself is the compiler's, not inline asm: only then does
+// it keep the wait states gfx950 requires between a VALU write and an MFMA
+// reading the result (it does not track writes made by inline asm, and an
+// MFMA issued right after such a write can read the register's old value).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-  return r;
+  return (a & in_sgpr(m)) | o;
 }
 
 template <int MODE, int MP, int PF, bool CS>
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
   }
   __syncthreads();
 
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint16_t* xlane = X + (size_t)xr * K + 32 * jj;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
     }
   const int items = DUAL ? 2 * cnt : cnt;  // ring items (rows, or gate/up row pairs)
   const int last = max(items - 1, 0);
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + 16 * j + 4 * jj;
   const uint32_t* qlane2 = DUAL ? Q2 + 16 * j + 4 * jj : qlane;
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     db[s] = 0.f;
     zb[s] = 0u;
   }
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + 16 * j + 4 * jj;
   const uint32_t* qlane2 = DUAL ? Q2 + (qlane - Q) : qlane;
@@ -941,7 +946,7 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
     }
   const int items = DUAL ? 2 * cnt : cnt;  // ring items (rows, or gate/up row pairs)
   const int last = max(items - 1, 0);
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + woff;
   const uint32_t* qlane2 = DUAL ? Q2 + woff : qlane;
@@ -1204,7 +1209,7 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
     db[s] = 0.f;
     zb[s] = 0u;
   }
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + woff;
   const uint32_t* qlane2 = DUAL ? Q2 + (qlane - Q) : qlane;
@@ -1607,7 +1612,7 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   sz_store(0);
   __syncthreads();
 
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nit; ++j) {  // j: item
     const int buf = j & 1;

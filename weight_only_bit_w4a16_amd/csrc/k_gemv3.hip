@@ -39,10 +39,15 @@ constexpr int GSTR = 13 * WSTR;
 __device__ __constant__ int kPairLo[5] = {0, 1, 3, 4, 2};
 __device__ __constant__ int kPairHi[5] = {6, 7, 8, 9, 5};
 
+// (a & m) | o as one v_and_or_b32, with the mask in an SGPR (and the caller's
+// o in a VGPR, see in_vgpr): a VOP3 instruction takes no literal on gfx950,
+// so with both constants visible the compiler would emit an AND and an OR.
+// The instruction itself is the compiler's, not inline asm: only then does
+// it keep the wait states gfx950 requires between a VALU write and an MFMA
+// reading the result (it does not track writes made by inline asm, and an
+// MFMA issued right after such a write can read the register's old value).
 __device__ __forceinline__ uint32_t and_or3(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-  return r;
+  return (a & in_sgpr(m)) | o;
 }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict
   }
   __syncthreads();
 
-  const uint32_t magic = kMagic2;
+  const uint32_t magic = in_vgpr(kMagic2);
   for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
     const int items = min(RB, N - rb * RB) * ng;
 #pragma unroll
