@@ -114,17 +114,3 @@ def test_joint_one_layer_is_the_plain_search():
     s2, b2, l2 = awq.scale_search_joint([dev(W)], dev(Xc), grid, 4, 128)
     assert b1 == b2 and np.array_equal(l1, l2)
     assert_same_bits(host(s1), host(s2))
-
-
-def test_joint_search_gate_up_workload():
-    """Gate and up of the 4096 x 11008 MLP at full size on the device; the
-    oracle recomputes alpha = 0, the argmin and the last grid point on 2048
-    sampled rows of each (so the device runs on the same sampled rows)."""
-    w = datagen.WORKLOADS["llama7b_mlp_up_4096x11008_int4"]
-    say("joint search gate/up", w.name)
-    rows = sample_rows(w.N, count=2048)
-    Wu = datagen.weight(w)[rows]
-    Wg = datagen.gate_weight(w)[rows]
-    Xc = datagen.calibration(w)
-    check_joint([Wg, Wu], Xc, datagen.alpha_grid(w.n_alpha), w.bits, w.group,
-                oracle_idx=[0, w.n_alpha - 1])

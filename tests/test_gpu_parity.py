@@ -547,20 +547,6 @@ def test_search_tiny_workload_full_grid():
     assert loss[best] < loss[0]
 
 
-@pytest.mark.parametrize("name", [n for n in datagen.WORKLOADS if n != datagen.SMALL])
-def test_search_workload_sampled(name):
-    """Full-size search on the device; the oracle recomputes alpha = 0, the
-    device's argmin and the last grid point (each one a full float64 pass)."""
-    w = datagen.WORKLOADS[name]
-    say("search workload", name)
-    W, Xc = workload_host(name)
-    grid = datagen.alpha_grid(w.n_alpha)
-    if w.N * w.K > 50_000_000:
-        rows = sample_rows(w.N, count=2048)
-        W = W[rows]
-    check_search(W, Xc, grid, w.bits, w.group, oracle_idx=[0, len(grid) - 1])
-
-
 def test_full_pipeline_tiny():
     """search -> quantize-pack -> fold -> decode, every step on the device."""
     w = datagen.WORKLOADS[datagen.SMALL]

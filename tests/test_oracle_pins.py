@@ -741,3 +741,30 @@ def test_compact_roundtrip_and_product(bits, group, K):
     bound = 2.0 ** -11 * (np.abs(X.astype(np.float64)) @ np.abs(O.dequantize(
         O.unpack(qp, bits, group, K), sc, z, group)).T)
     assert np.all(np.abs(Yc - Y) <= bound * (1 + 1e-9))
+
+
+def test_workload_search_golden_matches_oracle():
+    """tests/golden/workload_search.json holds the oracle's full loss curves
+    (written by make_workload_search.py from the oracle alone); the
+    512 x 512 layer's curve is recomputed here and must agree exactly, and
+    every stored curve has the default grid and its first minimum recorded."""
+    import json
+    import os
+    with open(os.path.join(GOLDEN, "workload_search.json")) as f:
+        doc = json.load(f)
+    entries = {(e["kind"], e["workload"]): e for e in doc["entries"]}
+    for name in datagen.WORKLOADS:
+        assert ("single", name) in entries
+    for e in doc["entries"]:
+        grid = datagen.alpha_grid(20)
+        assert np.array_equal(np.asarray(e["alpha_grid"], np.float32), grid)
+        L = np.asarray(e["losses"])
+        assert len(L) == 20 and np.all(L > 0)
+        assert e["best_index"] == int(np.argmin(L))
+        assert L[e["best_index"]] < L[0]  # the outlier channels make scaling pay
+    w = datagen.WORKLOADS[datagen.SMALL]
+    _, best, losses = O.scale_search(datagen.weight(w), datagen.calibration(w),
+                                     datagen.alpha_grid(w.n_alpha), w.bits, w.group)
+    e = entries[("single", w.name)]
+    assert best == e["best_index"]
+    assert np.array_equal(losses, np.asarray(e["losses"]))
