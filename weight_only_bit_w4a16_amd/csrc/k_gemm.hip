@@ -11,9 +11,21 @@
 //
 // K steps: 64 codes (half a group) for int4 and fp16 B, one whole 128-code
 // group for int3 (an int3 group is 13 words; 64 codes would split a word).
-// B tiles are dequantized to fp16 (q - z) * fp16(delta). For int4 a group
-// spans two steps: the scale and zero point are loaded with the even step
-// only and reused for the odd one.
+// B tiles are dequantized to fp16 (q - z) * fp16(delta * 2^e_n). For int4 a
+// group spans two steps: the scale and zero point are loaded with the even
+// step only and reused for the odd one.
+//
+// Row exponent e_n. Before its K loop a workgroup finds, for each weight row
+// n of its tile, the largest step of the row and picks the power of two that
+// puts it in [2^10, 2^11); the epilogue multiplies the row's float32 sums by
+// 2^-e_n. Multiplying by a power of two is exact in fp16 and float32 while
+// the values stay in the normal range, so a row whose steps are ordinary
+// gives the same bits as without it. A row whose steps lie below fp16's
+// normal range (delta < 2^-14: small weights, or channels with a small
+// activation statistic at large alpha) would otherwise be rounded to fp16
+// subnormals (several percent off, or zero); with the exponent every group
+// within 2^-24 of the row's largest step keeps fp16's full precision, and
+// dequantized values stay below 15 * 2^11 < 65504.
 //
 // Code order in LDS. The packed words are unpacked with the fp16 magic-number
 // trick, which yields codes in pairs that are not adjacent in k. For int4 the
@@ -47,11 +59,15 @@ __device__ __forceinline__ uint32_t plo(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t phi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
-// v_and_or_b32: (a & m) | o in one instruction (the mask stays scalar)
+// (a & m) | o as one v_and_or_b32, with the mask in an SGPR (and the caller's
+// o in a VGPR, see in_vgpr): a VOP3 instruction takes no literal on gfx950,
+// so with both constants visible the compiler would emit an AND and an OR.
+// The instruction itself is the compiler's, not inline asm: only then does
+// it keep the wait states gfx950 requires between a VALU write and an MFMA
+// reading the result (it does not track writes made by inline asm, and an
+// MFMA issued right after such a write can read the register's old value).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-  return r;
+  return (a & in_sgpr(m)) | o;
 }
 __device__ __forceinline__ uint32_t hbits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 hv(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -147,6 +163,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   constexpr int BNO = EPI == 2 ? BN / 2 : BN;  // outputs per tile along N
   __shared__ __align__(16) uint16_t lds_a[2][BM * STR];
   __shared__ __align__(16) uint16_t lds_b[2][BN * STR];
+  // per tile row of B: e_n (dequantization) and 2^-e_n (epilogue)
+  __shared__ int row_exp[BMODE != 0 ? BN : 1];
+  __shared__ float row_post[BMODE != 0 ? BN : 1];
+  // e_n of this thread's B rows (int4: one row; int3: one per item)
+  int rexp[BMODE == 3 ? C::BIT : 1];
+  // fp16 step delta * 2^e of a row: exact (a power-of-two product) unless it
+  // leaves fp16's range; compact storage holds delta in fp16 already, and
+  // v_ldexp_f16 scales it without a round trip through float32
+  auto row_step = [](float d, int e) -> _Float16 {
+    if constexpr (CS)
+      return __builtin_amdgcn_ldexph((_Float16)d, e);
+    else
+      return (_Float16)__builtin_ldexpf(d, e);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,7 +319,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   auto set_dq = [&](const St& st) {
     if constexpr (BMODE == 4) {
       const uint32_t z = (st.zw >> st.zsh) & ZMASK;
-      dq.dh = h2{(_Float16)st.d, (_Float16)st.d};
+      const _Float16 dh = row_step(st.d, rexp[0]);
+      dq.dh = h2{dh, dh};
       dq.ze = hv((0xE400u + z) * 0x00010001u);       // -(1024 + z)
       dq.zo = hv((0xD400u + 16u * z) * 0x00010001u);  // -(64 + z)
     }
@@ -314,6 +345,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   };
   auto store_b = [&](const St& st, int buf, int i) {
     uint16_t* lb = lds_b[buf];
+    const uint32_t magic = in_vgpr(kMagic2);
     if constexpr (BMODE == 0) {
       const int id = tid + NT * i;
       const int r = id / (BK / 8), c8 = id % (BK / 8);
@@ -323,12 +355,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
       const uint32_t w = st.b[i];
       const uint32_t w8 = w >> 8;
-      const h2 e0 = (hv(and_or(w, 0x000F000Fu, kMagic2)) + dq.ze) * dq.dh;
-      const h2 e1 = (hv(and_or(w8, 0x000F000Fu, kMagic2)) + dq.ze) * dq.dh;
+      const h2 e0 = (hv(and_or(w, 0x000F000Fu, magic)) + dq.ze) * dq.dh;
+      const h2 e1 = (hv(and_or(w8, 0x000F000Fu, magic)) + dq.ze) * dq.dh;
       const h2 o0 =
-          __builtin_elementwise_fma(hv(and_or(w, 0x00F000F0u, kMagic2)), sixteenth, dq.zo) * dq.dh;
+          __builtin_elementwise_fma(hv(and_or(w, 0x00F000F0u, magic)), sixteenth, dq.zo) * dq.dh;
       const h2 o1 =
-          __builtin_elementwise_fma(hv(and_or(w8, 0x00F000F0u, kMagic2)), sixteenth, dq.zo) * dq.dh;
+          __builtin_elementwise_fma(hv(and_or(w8, 0x00F000F0u, magic)), sixteenth, dq.zo) * dq.dh;
       *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * (w0 + i)]) =
           u32x4{hbits(e0), hbits(e1), hbits(o0), hbits(o1)};
     } else {
@@ -345,7 +377,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const int r = id >> 2, qt = id & 3;
       const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
       const float zf = (float)((st.zw[i] >> st.zsh[i]) & ZMASK);
-      const h2 dh = {(_Float16)st.d[i], (_Float16)st.d[i]};
+      const _Float16 d16 = row_step(st.d[i], rexp[i]);
+      const h2 dh = {d16, d16};
       h2 add[5];
 #pragma unroll
       for (int p = 0; p < 5; ++p) add[p] = h2{(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
@@ -356,9 +389,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         const bool use = qt == 0 || (qt == 3 ? u > 0 : u < 3);
         const uint32_t w = st.b[i][u];
         const uint32_t t8 = w >> 8, u1 = w << 1;
-        const uint32_t raw[5] = {and_or(w, 0x001C0007u, kMagic2), and_or(w, 0x00E00038u, kMagic2),
-                                 and_or(t8, 0x0007000Eu, kMagic2), and_or(t8, 0x00380070u, kMagic2),
-                                 and_or(u1, 0x00070380u, kMagic2)};
+        const uint32_t raw[5] = {and_or(w, 0x001C0007u, magic), and_or(w, 0x00E00038u, magic),
+                                 and_or(t8, 0x0007000Eu, magic), and_or(t8, 0x00380070u, magic),
+                                 and_or(u1, 0x00070380u, magic)};
         uint32_t pr[5];  // (c0,c6) (c1,c7) (c3,c8) (c4,c9) (c2,c5) as c - z times delta
 #pragma unroll
         for (int p = 0; p < 5; ++p)
@@ -449,6 +482,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     constexpr int i = decltype(I)::value;
     load_step(stg[i], min(i, last), std::integral_constant<bool, BMODE == 4 && i % 2 == 0>{});
   };
+  if constexpr (BMODE != 0) {
+    // row exponents: the TPR threads of tile row r (adjacent lanes) scan the
+    // row's steps 16 at a time, all loads of a batch in flight together
+    constexpr int TPR = NT / BN;
+    static_assert(NT % BN == 0 && (TPR & (TPR - 1)) == 0 && TPR <= 64, "threads per tile row");
+    const int r = tid / TPR, sub = tid % TPR;
+    const size_t n = (size_t)brow_n(r);
+    const void* Sp = bsel(r) ? S2 : S;
+    float dmax = 0.f;
+    for (int g0 = 16 * sub; g0 < ng; g0 += 16 * TPR) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = group_scale<CS>(Sp, n, ng, min(g0 + u, ng - 1));
+#pragma unroll
+      for (int u = 0; u < 16; ++u) dmax = fmaxf(dmax, v[u]);
+    }
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, off));
+    if (sub == 0) {
+      // dmax = f 2^x with f in [1/2, 1): e = 11 - x; a zero or non-finite
+      // maximum (nothing to scale) keeps e = 0
+      int e = 0;
+      if (dmax > 0.f && dmax <= 3.4e38f) e = 11 - __builtin_amdgcn_frexp_expf(dmax);
+      e = max(-126, min(126, e));
+      row_exp[r] = e;
+      row_post[r] = __builtin_ldexpf(1.0f, -e);
+    }
+    __syncthreads();
+    if constexpr (BMODE == 4) {
+      rexp[0] = row_exp[(tid * C::BW) / 8];
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::BIT; ++i) rexp[i] = row_exp[(tid + NT * i) >> 2];
+    }
+  }
   unroll_c<0, NST>(prime);
   set_dq(stg[0]);
   store_all(stg[0], 0);
@@ -482,11 +550,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int n = n0 + (BN / WGN) * wn + 32 * j + lr;
+          const float post = BMODE != 0 ? row_post[(BN / WGN) * wn + 32 * j + lr] : 1.0f;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int m =
                 m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (m < M && n < nend) plane[(size_t)m * N + n] = acc[i][j][v];
+            if (m < M && n < nend) plane[(size_t)m * N + n] = acc[i][j][v] * post;
           }
         }
       return;
@@ -496,12 +565,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + (BN / WGN) * wn + 32 * j + lr;
+        const float post = BMODE != 0 ? row_post[(BN / WGN) * wn + 32 * j + lr] : 1.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m =
               m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (m < M && n < nend)
-            Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][v]));
+            Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][v] * post));
         }
       }
   } else if constexpr (EPI == 2) {
@@ -511,12 +581,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 #pragma unroll
       for (int j = 0; j < TN; j += 2) {
         const int n = n0 + (BNO / WGN) * wn + 32 * (j >> 1) + lr;
+        const float pg = row_post[(BN / WGN) * wn + 32 * j + lr];
+        const float pu = row_post[(BN / WGN) * wn + 32 * (j + 1) + lr];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m =
               m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const float g = acc[i][j][v];
-          const float val = g / (1.0f + __expf(-g)) * acc[i][j + 1][v];
+          const float g = acc[i][j][v] * pg;
+          const float val = g / (1.0f + __expf(-g)) * (acc[i][j + 1][v] * pu);
           if (m < M && n < nend) Y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(val));
         }
       }
