@@ -198,9 +198,12 @@ awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const
  * X': dev fp16 [M, K], already divided by the scale s both matrices were
  * quantized with (one s per activation: gate and up share their input);
  * (qg, sg, zg) and (qu, su, zu): two [N, K] matrices packed as by
- * awq_quantize_pack(_ex); Y: dev fp16 [M, N]. M = 1
- * (int4) runs the decode kernel, other M the prefill kernel, both reading
- * X' once for the two matrices. Asynchronous on `stream`. */
+ * awq_quantize_pack(_ex); Y: dev fp16 [M, N]. Kernel choice, every one
+ * reading X' once for the two matrices: M = 1 (int4 and int3) the M = 1
+ * decode kernels; 2 <= M <= 4 the few-token decode kernels where their
+ * operands fit (int4 at M = 2, int3 at M = 2-4); int4 up to M = 16 the
+ * 16-row-block decode kernel; anything else the prefill kernel.
+ * Asynchronous on `stream`. */
 awq_status awq_w4a16_gate_up_silu(const uint16_t* X, const uint32_t* qg, const float* sg,
                                   const uint8_t* zg, const uint32_t* qu, const float* su,
                                   const uint8_t* zu, int M, int N, int K, int bits, int group,

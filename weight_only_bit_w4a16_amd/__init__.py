@@ -59,6 +59,26 @@ def _need(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _same_device(dev, *named):
+    """Every tensor in (name, tensor) pairs sits on `dev` (the kernels read
+    all operands on one device)."""
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+
+
+def _out(t, name, dtype, shape, device):
+    """A caller-provided output: right dtype, exact shape, contiguous, on
+    `device` (the library writes exactly shape's elements through its
+    pointer)."""
+    _need(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    return t
+
+
 def _group(K, group):
     return K if group == -1 else group
 
@@ -85,6 +105,7 @@ def scale_candidates(m, alpha, stream=None):
     torch = _torch()
     _need(m, "m", torch.float64, 1)
     _need(alpha, "alpha", torch.float32, 1)
+    _same_device(m.device, ("alpha", alpha))
     s = torch.empty((alpha.numel(), m.numel()), dtype=torch.float32, device=m.device)
     check(lib().awq_scale_candidates(_ptr(m), m.numel(), _ptr(alpha), alpha.numel(), _ptr(s),
                                      _stream(stream)), "awq_scale_candidates")
@@ -106,6 +127,7 @@ def quantize_pack(W, s=None, bits: int = 4, group: int = 128, out=None, stream=N
         _need(s, "s", torch.float32, 1)
         if s.numel() != K:
             raise ValueError("s must have K entries")
+        _same_device(W.device, ("s", s))
     g = _group(K, group)
     wpr = packed_words_per_row(K, bits, group)
     if out is None:
@@ -114,6 +136,9 @@ def quantize_pack(W, s=None, bits: int = 4, group: int = 128, out=None, stream=N
         z = torch.empty((N, K // g), dtype=torch.uint8, device=W.device)
     else:
         q, sc, z = out
+        _out(q, "out qpacked", torch.int32, (N, wpr), W.device)
+        _out(sc, "out scales", torch.float32, (N, K // g), W.device)
+        _out(z, "out zeros", torch.uint8, (N, K // g), W.device)
     check(lib().awq_quantize_pack_ex(_ptr(W), _ptr(s), N, K, bits, group, int(bool(zero_point)),
                                      _ptr(q), _ptr(sc), _ptr(z), _stream(stream)),
           "awq_quantize_pack_ex")
@@ -126,7 +151,10 @@ def fold_inv_scale(X, s, out=None, stream=None):
     _need(X, "X", torch.float16, 2)
     _need(s, "s", torch.float32, 1)
     M, K = X.shape
-    y = torch.empty_like(X) if out is None else out
+    if s.numel() != K:
+        raise ValueError("s must have K entries")
+    _same_device(X.device, ("s", s))
+    y = torch.empty_like(X) if out is None else _out(out, "out", torch.float16, (M, K), X.device)
     check(lib().awq_fold_inv_scale(_ptr(X), _ptr(s), M, K, _ptr(y), _stream(stream)),
           "awq_fold_inv_scale")
     return y
@@ -173,7 +201,10 @@ def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, ou
         raise ValueError("qpacked has the wrong row length for (K, bits, group)")
     if tuple(scales.shape) != (N, K // g) or tuple(zeros.shape) != (N, K // g):
         raise ValueError("scales/zeros must be [N, K/group]")
-    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
+    _same_device(Xp.device, ("qpacked", qpacked), ("scales", scales), ("zeros", zeros),
+                 ("workspace", workspace))
+    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else \
+        _out(out, "out", torch.float16, (M, N), Xp.device)
     st = _stream(stream)
     if kernel == KERNEL_AUTO:
         nb = matmul_workspace_bytes(M, N, K, bits, group)
@@ -201,6 +232,7 @@ def compact_group_params(scales, zeros, K: int, group: int = 128, stream=None):
     N, ng = scales.shape
     if tuple(zeros.shape) != (N, ng) or ng != K // _group(K, group):
         raise ValueError("scales and zeros must be [N, K/group]")
+    _same_device(scales.device, ("zeros", zeros))
     s16 = torch.empty((N, ng), dtype=torch.float16, device=scales.device)
     z4 = torch.empty((N, (ng + 7) // 8), dtype=torch.int32, device=scales.device)
     check(lib().awq_compact_group_params(_ptr(scales), _ptr(zeros), N, K, group, _ptr(s16),
@@ -223,7 +255,9 @@ def w4a16_matmul_compact(Xp, qpacked, scales16, zeros4, bits: int = 4, group: in
         raise ValueError("qpacked has the wrong row length for (K, bits, group)")
     if tuple(scales16.shape) != (N, K // g) or tuple(zeros4.shape) != (N, (K // g + 7) // 8):
         raise ValueError("scales16 must be [N, K/group] and zeros4 [N, ceil(K/group / 8)]")
-    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
+    _same_device(Xp.device, ("qpacked", qpacked), ("scales16", scales16), ("zeros4", zeros4))
+    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else \
+        _out(out, "out", torch.float16, (M, N), Xp.device)
     check(lib().awq_w4a16_matmul_compact(_ptr(Xp), _ptr(qpacked), _ptr(scales16), _ptr(zeros4), M,
                                          N, K, bits, group, _ptr(y), kernel, _stream(stream)),
           "awq_w4a16_matmul_compact")
@@ -247,7 +281,10 @@ def gate_up_silu(Xp, gate, up, bits: int = 4, group: int = 128, out=None, stream
             raise ValueError(f"{name} qpacked must be [N, words_per_row]")
         if tuple(sc.shape) != (N, K // g) or tuple(z.shape) != (N, K // g):
             raise ValueError(f"{name} scales/zeros must be [N, K/group]")
-    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else out
+        _same_device(Xp.device, (f"{name} qpacked", q), (f"{name} scales", sc),
+                     (f"{name} zeros", z))
+    y = torch.empty((M, N), dtype=torch.float16, device=Xp.device) if out is None else \
+        _out(out, "out", torch.float16, (M, N), Xp.device)
     check(lib().awq_w4a16_gate_up_silu(_ptr(Xp), _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]),
                                        _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), M, N, K, bits,
                                        group, _ptr(y), _stream(stream)),
@@ -274,6 +311,7 @@ def scale_search(W, xcal, alpha_grid=None, bits: int = 4, group: int = 128, work
     T = xcal.shape[0]
     if xcal.shape[1] != K:
         raise ValueError("xcal must be [T, K]")
+    _same_device(W.device, ("xcal", xcal), ("workspace", workspace))
     if alpha_grid is None:
         alpha_grid = (np.arange(20, dtype=np.float64) / 20).astype(np.float32)
     a = np.ascontiguousarray(np.asarray(alpha_grid, dtype=np.float32))
@@ -282,6 +320,7 @@ def scale_search(W, xcal, alpha_grid=None, bits: int = 4, group: int = 128, work
         raise ValueError("unsupported scale_search sizes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
+    _need(workspace, "workspace", torch.uint8, 1)
     s = torch.empty(K, dtype=torch.float32, device=W.device)
     losses = np.zeros(len(a), dtype=np.float64)
     best = ctypes.c_int(-1)
@@ -317,6 +356,7 @@ def scale_search_joint(Ws, xcal, alpha_grid=None, bits: int = 4, group: int = 12
         _need(W, f"Ws[{i}]", torch.float16, 2)
         if W.shape[1] != K:
             raise ValueError("every W must be [N_l, K] with the K of xcal")
+        _same_device(xcal.device, (f"Ws[{i}]", W))
     if alpha_grid is None:
         alpha_grid = (np.arange(20, dtype=np.float64) / 20).astype(np.float32)
     a = np.ascontiguousarray(np.asarray(alpha_grid, dtype=np.float32))
@@ -326,6 +366,8 @@ def scale_search_joint(Ws, xcal, alpha_grid=None, bits: int = 4, group: int = 12
         raise ValueError("unsupported scale_search_joint sizes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=xcal.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(xcal.device, ("workspace", workspace))
     s = torch.empty(K, dtype=torch.float32, device=xcal.device)
     losses = np.zeros(len(a), dtype=np.float64)
     best = ctypes.c_int(-1)
@@ -347,7 +389,9 @@ def fold_norm_weight(gamma, s, out=None, stream=None):
     _need(s, "s", torch.float32, 1)
     if s.numel() != gamma.numel():
         raise ValueError("gamma and s must have K entries each")
-    y = torch.empty_like(gamma) if out is None else out
+    _same_device(gamma.device, ("s", s))
+    y = torch.empty_like(gamma) if out is None else \
+        _out(out, "out", torch.float16, tuple(gamma.shape), gamma.device)
     check(lib().awq_fold_norm_weight(_ptr(gamma), _ptr(s), gamma.numel(), _ptr(y),
                                      _stream(stream)), "awq_fold_norm_weight")
     return y
@@ -361,7 +405,8 @@ def rmsnorm(X, gamma, eps: float = 1e-6, out=None, stream=None):
     M, K = X.shape
     if gamma.numel() != K:
         raise ValueError("gamma must have K entries")
-    y = torch.empty_like(X) if out is None else out
+    _same_device(X.device, ("gamma", gamma))
+    y = torch.empty_like(X) if out is None else _out(out, "out", torch.float16, (M, K), X.device)
     check(lib().awq_rmsnorm(_ptr(X), _ptr(gamma), M, K, ctypes.c_float(eps), _ptr(y),
                             _stream(stream)), "awq_rmsnorm")
     return y
