@@ -30,6 +30,29 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
 // mantissa gives the fp16 value 1024 + c * 2^e exactly.
 constexpr uint32_t kMagic2 = 0x64006400u;
 
+// The unpack constants in registers, made once per kernel outside its loops
+// (the empty asm is not moved out of a loop by the compiler, so a mask made
+// at its use would cost one scalar move per use): the fp16 magic number in a
+// VGPR and the nibble / 3-bit masks in SGPRs, so that (w & mask) | magic is
+// one v_and_or_b32 (see and_or). Fields a kernel does not use cost nothing.
+struct UnpackRegs {
+  uint32_t magic;     // kMagic2
+  uint32_t lo4, hi4;  // int4: codes 0, 4 (0x000F000F) and 1, 5 (0x00F000F0) of a word
+  uint32_t m3[5];     // int3: the five pair masks of a 10-code word
+};
+__device__ __forceinline__ UnpackRegs unpack_regs() {
+  UnpackRegs r;
+  r.magic = in_vgpr(kMagic2);
+  r.lo4 = in_sgpr(0x000F000Fu);
+  r.hi4 = in_sgpr(0x00F000F0u);
+  r.m3[0] = in_sgpr(0x001C0007u);
+  r.m3[1] = in_sgpr(0x00E00038u);
+  r.m3[2] = in_sgpr(0x0007000Eu);
+  r.m3[3] = in_sgpr(0x00380070u);
+  r.m3[4] = in_sgpr(0x00070380u);
+  return r;
+}
+
 // Grid of one quantization group (asymmetric round-to-nearest, the range
 // always containing 0, "number of levels" read as 2^b - 1 steps). All
 // operations are single IEEE float32 roundings: the library is compiled with

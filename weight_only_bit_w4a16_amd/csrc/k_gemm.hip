@@ -59,15 +59,15 @@ __device__ __forceinline__ uint32_t plo(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t phi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
-// (a & m) | o as one v_and_or_b32, with the mask in an SGPR (and the caller's
-// o in a VGPR, see in_vgpr): a VOP3 instruction takes no literal on gfx950,
-// so with both constants visible the compiler would emit an AND and an OR.
-// The instruction itself is the compiler's, not inline asm: only then does
-// it keep the wait states gfx950 requires between a VALU write and an MFMA
-// reading the result (it does not track writes made by inline asm, and an
-// MFMA issued right after such a write can read the register's old value).
+// (a & m) | o as one v_and_or_b32: m in an SGPR and o in a VGPR (from
+// unpack_regs), since a VOP3 instruction takes no literal on gfx950 and with
+// both constants visible the compiler would emit an AND and an OR. The
+// instruction is the compiler's own, not inline asm: only then does it keep
+// the wait states gfx950 requires between a VALU write and an MFMA reading
+// the result (it does not track writes made by inline asm, and an MFMA
+// issued right after such a write can read the register's old value).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  return (a & in_sgpr(m)) | o;
+  return (a & m) | o;
 }
 __device__ __forceinline__ uint32_t hbits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 hv(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -163,11 +163,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   constexpr int BNO = EPI == 2 ? BN / 2 : BN;  // outputs per tile along N
   __shared__ __align__(16) uint16_t lds_a[2][BM * STR];
   __shared__ __align__(16) uint16_t lds_b[2][BN * STR];
-  // per tile row of B: e_n (dequantization) and 2^-e_n (epilogue)
-  __shared__ int row_exp[BMODE != 0 ? BN : 1];
+  // per tile row of B: 2^-e_n (epilogue)
   __shared__ float row_post[BMODE != 0 ? BN : 1];
-  // e_n of this thread's B rows (int4: one row; int3: one per item)
-  int rexp[BMODE == 3 ? C::BIT : 1];
+  // e_n of this thread's B row
+  int rexp[1];
   // fp16 step delta * 2^e of a row: exact (a power-of-two product) unless it
   // leaves fp16's range; compact storage holds delta in fp16 already, and
   // v_ldexp_f16 scales it without a round trip through float32
@@ -180,6 +179,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const UnpackRegs ur = unpack_regs();  // masks and magic number, loop-invariant
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
@@ -345,7 +345,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   };
   auto store_b = [&](const St& st, int buf, int i) {
     uint16_t* lb = lds_b[buf];
-    const uint32_t magic = in_vgpr(kMagic2);
     if constexpr (BMODE == 0) {
       const int id = tid + NT * i;
       const int r = id / (BK / 8), c8 = id % (BK / 8);
@@ -355,12 +354,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
       const uint32_t w = st.b[i];
       const uint32_t w8 = w >> 8;
-      const h2 e0 = (hv(and_or(w, 0x000F000Fu, magic)) + dq.ze) * dq.dh;
-      const h2 e1 = (hv(and_or(w8, 0x000F000Fu, magic)) + dq.ze) * dq.dh;
+      const h2 e0 = (hv(and_or(w, ur.lo4, ur.magic)) + dq.ze) * dq.dh;
+      const h2 e1 = (hv(and_or(w8, ur.lo4, ur.magic)) + dq.ze) * dq.dh;
       const h2 o0 =
-          __builtin_elementwise_fma(hv(and_or(w, 0x00F000F0u, magic)), sixteenth, dq.zo) * dq.dh;
+          __builtin_elementwise_fma(hv(and_or(w, ur.hi4, ur.magic)), sixteenth, dq.zo) * dq.dh;
       const h2 o1 =
-          __builtin_elementwise_fma(hv(and_or(w8, 0x00F000F0u, magic)), sixteenth, dq.zo) * dq.dh;
+          __builtin_elementwise_fma(hv(and_or(w8, ur.hi4, ur.magic)), sixteenth, dq.zo) * dq.dh;
       *reinterpret_cast<u32x4*>(&lb[r * STR + 8 * (w0 + i)]) =
           u32x4{hbits(e0), hbits(e1), hbits(o0), hbits(o1)};
     } else {
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const int r = id >> 2, qt = id & 3;
       const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
       const float zf = (float)((st.zw[i] >> st.zsh[i]) & ZMASK);
-      const _Float16 d16 = row_step(st.d[i], rexp[i]);
+      const _Float16 d16 = row_step(st.d[i], rexp[0]);
       const h2 dh = {d16, d16};
       h2 add[5];
 #pragma unroll
@@ -389,9 +388,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         const bool use = qt == 0 || (qt == 3 ? u > 0 : u < 3);
         const uint32_t w = st.b[i][u];
         const uint32_t t8 = w >> 8, u1 = w << 1;
-        const uint32_t raw[5] = {and_or(w, 0x001C0007u, magic), and_or(w, 0x00E00038u, magic),
-                                 and_or(t8, 0x0007000Eu, magic), and_or(t8, 0x00380070u, magic),
-                                 and_or(u1, 0x00070380u, magic)};
+        const uint32_t raw[5] = {and_or(w, ur.m3[0], ur.magic), and_or(w, ur.m3[1], ur.magic),
+                                 and_or(t8, ur.m3[2], ur.magic), and_or(t8, ur.m3[3], ur.magic),
+                                 and_or(u1, ur.m3[4], ur.magic)};
         uint32_t pr[5];  // (c0,c6) (c1,c7) (c3,c8) (c4,c9) (c2,c5) as c - z times delta
 #pragma unroll
         for (int p = 0; p < 5; ++p)
@@ -482,42 +481,79 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     constexpr int i = decltype(I)::value;
     load_step(stg[i], min(i, last), std::integral_constant<bool, BMODE == 4 && i % 2 == 0>{});
   };
-  if constexpr (BMODE != 0) {
-    // row exponents: the TPR threads of tile row r (adjacent lanes) scan the
-    // row's steps 16 at a time, all loads of a batch in flight together
+  if constexpr (BMODE == 0) {
+    unroll_c<0, NST>(prime);
+  } else {
+    // Row exponents. The TPR threads of tile row r (adjacent lanes) take the
+    // largest step of the groups this workgroup's K range touches (a split's
+    // own range: its partial sums are stored unscaled, so splits need not
+    // agree on e). They are also the threads that dequantize row r, so each
+    // keeps e in a register; only the epilogue's 2^-e goes through LDS (read
+    // after the K loop's barriers). The first eight 16-byte scale loads go
+    // out before the stages' loads, so waiting for them does not wait for
+    // the stages (loads return in order).
     constexpr int TPR = NT / BN;
     static_assert(NT % BN == 0 && (TPR & (TPR - 1)) == 0 && TPR <= 64, "threads per tile row");
+    static_assert(BMODE != 3 || C::BIT == 1, "int3: one B item (row) per thread");
+    static_assert(BMODE != 4 || TPR <= 8, "int4: a thread's B words lie in row tid / TPR");
     const int r = tid / TPR, sub = tid % TPR;
     const size_t n = (size_t)brow_n(r);
     const void* Sp = bsel(r) ? S2 : S;
+    const int glo = (kofs * BK) >> (7 + gshift);
+    const int ghi = min(ng, ((((kofs + nsteps) * BK) - 1) >> (7 + gshift)) + 1);
+    const int len = ghi - glo;
     float dmax = 0.f;
-    for (int g0 = 16 * sub; g0 < ng; g0 += 16 * TPR) {
-      float v[16];
+    if constexpr (!CS) {
+      // float32 steps, four per 16-byte load; chunks past the range re-read
+      // its last four steps (harmless for a max)
+      const float* srow = static_cast<const float*>(Sp) + n * ng;
+      const int nchunk = (len + 3) >> 2;
+      auto chunk = [&](int c) {
+        return *reinterpret_cast<const u32x4a4*>(srow + min(glo + 4 * c, ghi - 4));
+      };
+      u32x4a4 v[8];
+      if (len >= 4) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = group_scale<CS>(Sp, n, ng, min(g0 + u, ng - 1));
+        for (int u = 0; u < 8; ++u) v[u] = chunk(sub + TPR * u);
+      }
+      unroll_c<0, NST>(prime);
+      if (len >= 4) {
+        for (int c0 = 0;;) {
+          // (through a float vector: __builtin_bit_cast of one element of an
+          // integer vector reads element 0 in this compiler)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) dmax = fmaxf(dmax, v[u]);
+          for (int u = 0; u < 8; ++u) {
+            const floatx4 f = __builtin_bit_cast(floatx4, v[u]);
+            dmax = fmaxf(dmax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
+          }
+          c0 += 8 * TPR;
+          if (c0 >= nchunk) break;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = chunk(c0 + sub + TPR * u);
+        }
+      } else {
+        for (int g = glo + sub; g < ghi; g += TPR) dmax = fmaxf(dmax, srow[g]);
+      }
+    } else {  // fp16 steps: 16 scalar loads in flight
+      unroll_c<0, NST>(prime);
+      for (int g0 = glo + 16 * sub; g0 < ghi; g0 += 16 * TPR) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = group_scale<CS>(Sp, n, ng, min(g0 + u, ghi - 1));
+#pragma unroll
+        for (int u = 0; u < 16; ++u) dmax = fmaxf(dmax, v[u]);
+      }
     }
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, off));
-    if (sub == 0) {
-      // dmax = f 2^x with f in [1/2, 1): e = 11 - x; a zero or non-finite
-      // maximum (nothing to scale) keeps e = 0
-      int e = 0;
-      if (dmax > 0.f && dmax <= 3.4e38f) e = 11 - __builtin_amdgcn_frexp_expf(dmax);
-      e = max(-126, min(126, e));
-      row_exp[r] = e;
-      row_post[r] = __builtin_ldexpf(1.0f, -e);
-    }
-    __syncthreads();
-    if constexpr (BMODE == 4) {
-      rexp[0] = row_exp[(tid * C::BW) / 8];
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::BIT; ++i) rexp[i] = row_exp[(tid + NT * i) >> 2];
-    }
+    // dmax = f 2^x with f in [1/2, 1): e = 11 - x; a zero or non-finite
+    // maximum (nothing to scale) keeps e = 0
+    int e = 0;
+    if (dmax > 0.f && dmax <= 3.4e38f) e = 11 - __builtin_amdgcn_frexp_expf(dmax);
+    e = max(-126, min(126, e));
+    if (sub == 0) row_post[r] = __builtin_ldexpf(1.0f, -e);
+    rexp[0] = e;  // int4: this thread's B row is (tid BW) / 8 = r; int3: (tid >> 2) = r
   }
-  unroll_c<0, NST>(prime);
   set_dq(stg[0]);
   store_all(stg[0], 0);
   load_step(stg[0], min(NST, last), std::integral_constant<bool, BMODE == 4>{});

@@ -92,15 +92,15 @@ __device__ __forceinline__ void load_x32(const uint16_t* p, uint32_t* d) {
 // ---------------------------------------------------------------------------
 enum { kOffset = 0, kExact = 1 };
 
-// (a & m) | o as one v_and_or_b32, with the mask in an SGPR (and the caller's
-// o in a VGPR, see in_vgpr): a VOP3 instruction takes no literal on gfx950,
-// so with both constants visible the compiler would emit an AND and an OR.
-// The instruction itself is the compiler's, not inline asm: only then does
-// it keep the wait states gfx950 requires between a VALU write and an MFMA
-// reading the result (it does not track writes made by inline asm, and an
-// MFMA issued right after such a write can read the register's old value).
+// (a & m) | o as one v_and_or_b32: m in an SGPR and o in a VGPR (from
+// unpack_regs), since a VOP3 instruction takes no literal on gfx950 and with
+// both constants visible the compiler would emit an AND and an OR. The
+// instruction is the compiler's own, not inline asm: only then does it keep
+// the wait states gfx950 requires between a VALU write and an MFMA reading
+// the result (it does not track writes made by inline asm, and an MFMA
+// issued right after such a write can read the register's old value).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  return (a & in_sgpr(m)) | o;
+  return (a & m) | o;
 }
 
 template <int MODE, int MP, int PF, bool CS>
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
   }
   __syncthreads();
 
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint16_t* xlane = X + (size_t)xr * K + 32 * jj;
@@ -248,10 +248,10 @@ __global__ __launch_bounds__(256) void gemv_w4_kernel(
       for (int t = 0; t < 4; ++t) {
         const uint32_t x = w[t];
         const uint32_t x8 = x >> 8;
-        e[2 * t] = and_or(x, 0x000F000Fu, magic);      // (c0, c4)
-        o[2 * t] = and_or(x, 0x00F000F0u, magic);      // (16 c1, 16 c5)
-        e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);  // (c2, c6)
-        o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);  // (16 c3, 16 c7)
+        e[2 * t] = and_or(x, ur.lo4, ur.magic);      // (c0, c4)
+        o[2 * t] = and_or(x, ur.hi4, ur.magic);      // (16 c1, 16 c5)
+        e[2 * t + 1] = and_or(x8, ur.lo4, ur.magic);  // (c2, c6)
+        o[2 * t + 1] = and_or(x8, ur.hi4, ur.magic);  // (16 c3, 16 c7)
       }
       if constexpr (MODE == kOffset) {
         const floatx4 de = mfma16(a1, u32x4{e[4], e[5], e[6], e[7]},
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
     }
   const int items = DUAL ? 2 * cnt : cnt;  // ring items (rows, or gate/up row pairs)
   const int last = max(items - 1, 0);
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + 16 * j + 4 * jj;
   const uint32_t* qlane2 = DUAL ? Q2 + 16 * j + 4 * jj : qlane;
@@ -512,10 +512,10 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
           for (int t = 0; t < 4; ++t) {
             const uint32_t x = w[t];
             const uint32_t x8 = x >> 8;
-            e[2 * t] = and_or(x, 0x000F000Fu, magic);
-            o[2 * t] = and_or(x, 0x00F000F0u, magic);
-            e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
-            o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
+            e[2 * t] = and_or(x, ur.lo4, ur.magic);
+            o[2 * t] = and_or(x, ur.hi4, ur.magic);
+            e[2 * t + 1] = and_or(x8, ur.lo4, ur.magic);
+            o[2 * t + 1] = and_or(x8, ur.hi4, ur.magic);
           }
           const int ps = seg * SP + s;
           floatx4 acc = mfma16(xs[ps][0][lane], u32x4{e[0], e[1], e[2], e[3]}, zero4);
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
     db[s] = 0.f;
     zb[s] = 0u;
   }
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + 16 * j + 4 * jj;
   const uint32_t* qlane2 = DUAL ? Q2 + (qlane - Q) : qlane;
@@ -726,10 +726,10 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
         for (int t = 0; t < 4; ++t) {
           const uint32_t x = w[t];
           const uint32_t x8 = x >> 8;
-          e[2 * t] = and_or(x, 0x000F000Fu, magic);
-          o[2 * t] = and_or(x, 0x00F000F0u, magic);
-          e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
-          o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
+          e[2 * t] = and_or(x, ur.lo4, ur.magic);
+          o[2 * t] = and_or(x, ur.hi4, ur.magic);
+          e[2 * t + 1] = and_or(x8, ur.lo4, ur.magic);
+          o[2 * t + 1] = and_or(x8, ur.hi4, ur.magic);
         }
 #pragma unroll
         for (int tk = 0; tk < MT; ++tk) {
@@ -946,7 +946,7 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
     }
   const int items = DUAL ? 2 * cnt : cnt;  // ring items (rows, or gate/up row pairs)
   const int last = max(items - 1, 0);
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + woff;
   const uint32_t* qlane2 = DUAL ? Q2 + woff : qlane;
@@ -973,11 +973,11 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
           for (int q = 0; q < 4; ++q) {
             const uint32_t x = w[q];
             const uint32_t t8 = x >> 8, u1 = x << 1;
-            pr[5 * q + 0] = and_or(x, 0x001C0007u, magic);
-            pr[5 * q + 1] = and_or(x, 0x00E00038u, magic);
-            pr[5 * q + 2] = and_or(t8, 0x0007000Eu, magic);
-            pr[5 * q + 3] = and_or(t8, 0x00380070u, magic);
-            pr[5 * q + 4] = and_or(u1, 0x00070380u, magic);
+            pr[5 * q + 0] = and_or(x, ur.m3[0], ur.magic);
+            pr[5 * q + 1] = and_or(x, ur.m3[1], ur.magic);
+            pr[5 * q + 2] = and_or(t8, ur.m3[2], ur.magic);
+            pr[5 * q + 3] = and_or(t8, ur.m3[3], ur.magic);
+            pr[5 * q + 4] = and_or(u1, ur.m3[4], ur.magic);
           }
           floatx4 acc = mfma16(xs[s][0][lane], u32x4{pr[0], pr[1], pr[2], pr[3]}, zero4);
           acc = mfma16(xs[s][1][lane], u32x4{pr[4], pr[5], pr[6], pr[7]}, acc);
@@ -1209,7 +1209,7 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
     db[s] = 0.f;
     zb[s] = 0u;
   }
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* qlane = Q + woff;
   const uint32_t* qlane2 = DUAL ? Q2 + (qlane - Q) : qlane;
@@ -1236,11 +1236,11 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
         for (int q = 0; q < 4; ++q) {
           const uint32_t x = w[q];
           const uint32_t t8 = x >> 8, u1 = x << 1;
-          pr[5 * q + 0] = and_or(x, 0x001C0007u, magic);
-          pr[5 * q + 1] = and_or(x, 0x00E00038u, magic);
-          pr[5 * q + 2] = and_or(t8, 0x0007000Eu, magic);
-          pr[5 * q + 3] = and_or(t8, 0x00380070u, magic);
-          pr[5 * q + 4] = and_or(u1, 0x00070380u, magic);
+          pr[5 * q + 0] = and_or(x, ur.m3[0], ur.magic);
+          pr[5 * q + 1] = and_or(x, ur.m3[1], ur.magic);
+          pr[5 * q + 2] = and_or(t8, ur.m3[2], ur.magic);
+          pr[5 * q + 3] = and_or(t8, ur.m3[3], ur.magic);
+          pr[5 * q + 4] = and_or(u1, ur.m3[4], ur.magic);
         }
 #pragma unroll
         for (int tk = 0; tk < MT; ++tk) {
@@ -1612,7 +1612,7 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
   sz_store(0);
   __syncthreads();
 
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nit; ++j) {  // j: item
     const int buf = j & 1;
@@ -1635,10 +1635,10 @@ __global__ __launch_bounds__(512) void gemv_w4_mx_kernel(
         for (int t = 0; t < 4; ++t) {
           const uint32_t x = w[t];
           const uint32_t x8 = x >> 8;
-          e[2 * t] = and_or(x, 0x000F000Fu, magic);
-          o[2 * t] = and_or(x, 0x00F000F0u, magic);
-          e[2 * t + 1] = and_or(x8, 0x000F000Fu, magic);
-          o[2 * t + 1] = and_or(x8, 0x00F000F0u, magic);
+          e[2 * t] = and_or(x, ur.lo4, ur.magic);
+          o[2 * t] = and_or(x, ur.hi4, ur.magic);
+          e[2 * t + 1] = and_or(x8, ur.lo4, ur.magic);
+          o[2 * t + 1] = and_or(x8, ur.hi4, ur.magic);
         }
         const floatx4 de = mfma16(av[i][1], u32x4{e[4], e[5], e[6], e[7]},
                                   mfma16(av[i][0], u32x4{e[0], e[1], e[2], e[3]}, zero4));

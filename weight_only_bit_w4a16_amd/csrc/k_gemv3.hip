@@ -39,15 +39,15 @@ constexpr int GSTR = 13 * WSTR;
 __device__ __constant__ int kPairLo[5] = {0, 1, 3, 4, 2};
 __device__ __constant__ int kPairHi[5] = {6, 7, 8, 9, 5};
 
-// (a & m) | o as one v_and_or_b32, with the mask in an SGPR (and the caller's
-// o in a VGPR, see in_vgpr): a VOP3 instruction takes no literal on gfx950,
-// so with both constants visible the compiler would emit an AND and an OR.
-// The instruction itself is the compiler's, not inline asm: only then does
-// it keep the wait states gfx950 requires between a VALU write and an MFMA
-// reading the result (it does not track writes made by inline asm, and an
-// MFMA issued right after such a write can read the register's old value).
+// (a & m) | o as one v_and_or_b32: m in an SGPR and o in a VGPR (from
+// unpack_regs), since a VOP3 instruction takes no literal on gfx950 and with
+// both constants visible the compiler would emit an AND and an OR. The
+// instruction is the compiler's own, not inline asm: only then does it keep
+// the wait states gfx950 requires between a VALU write and an MFMA reading
+// the result (it does not track writes made by inline asm, and an MFMA
+// issued right after such a write can read the register's old value).
 __device__ __forceinline__ uint32_t and_or3(uint32_t a, uint32_t m, uint32_t o) {
-  return (a & in_sgpr(m)) | o;
+  return (a & m) | o;
 }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict
   }
   __syncthreads();
 
-  const uint32_t magic = in_vgpr(kMagic2);
+  const UnpackRegs ur = unpack_regs();
   for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
     const int items = min(RB, N - rb * RB) * ng;
 #pragma unroll
@@ -164,9 +164,9 @@ __global__ __launch_bounds__(256) void gemv_w3_kernel(const uint16_t* __restrict
         for (int k = 0; k < 13; ++k) {
           const uint32_t w = wv[u][k];
           const uint32_t t8 = w >> 8, u1 = w << 1;
-          const uint32_t pr[5] = {and_or3(w, 0x001C0007u, magic), and_or3(w, 0x00E00038u, magic),
-                                  and_or3(t8, 0x0007000Eu, magic), and_or3(t8, 0x00380070u, magic),
-                                  and_or3(u1, 0x00070380u, magic)};
+          const uint32_t pr[5] = {and_or3(w, ur.m3[0], ur.magic), and_or3(w, ur.m3[1], ur.magic),
+                                  and_or3(t8, ur.m3[2], ur.magic), and_or3(t8, ur.m3[3], ur.magic),
+                                  and_or3(u1, ur.m3[4], ur.magic)};
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
             if (m < M) {
