@@ -188,6 +188,24 @@ awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const
                                uint16_t* Y, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * product of awq_w4a16_matmul_ws, same arguments, kernels and results,
+ * with the split-K planes in a scratch array the library holds in device
+ * memory (16 MiB on each GPU it runs on, from first load to the end of the
+ * process) instead of a caller workspace. The call allocates nothing; the
+ * caller still owns X, qpacked, scales, zeros and Y. A shape whose split
+ * plan needs more than 16 MiB returns AWQ_ERR_WORKSPACE (on a 256-unit GPU
+ * every plan fits). Every call on one GPU shares that GPU's scratch and
+ * leaves its contents behind (nothing in it needs clearing: each split
+ * writes its whole plane before the planes are added), so calls that
+ * overlap on one GPU race: order them on one stream. The first call on a
+ * device looks up the scratch's address there (no allocation).
+ * Asynchronous on `stream`. */
+awq_status awq_w4a16_matmul_noalloc(const uint16_t* X, const uint32_t* qpacked,
+                                    const float* scales, const uint8_t* zeros, int M, int N, int K,
+                                    int bits, int group, uint16_t* Y, void* stream);
+
 /* The gate and up projections of a gated MLP fused into one call (hungho77
  * blog -- "Why the engine is part of the method": the speed-up comes from
  * kernels that fuse operators). Both projections read the same activation

@@ -122,6 +122,24 @@ def test_matmul_workspace_plan():
     assert W(0, 4096, 4096, 4, 128) == 0
 
 
+def test_matmul_noalloc_validation():
+    """The allocation-free product validates like the others before any HIP
+    call, and without a device returns AWQ_ERR_NO_DEVICE; no plan on a
+    256-unit part needs more than its 16 MiB of scratch."""
+    h = awq.lib()
+    E = _lib
+    f = lambda X=P, M=32, N=4096, K=4096, bits=4, group=128: h.awq_w4a16_matmul_noalloc(  # noqa: E731
+        X, P, P, P, M, N, K, bits, group, P2, NULL)
+    assert f(X=NULL) == E.AWQ_ERR_INVALID_ARG
+    assert f(X=MIS) == E.AWQ_ERR_INVALID_ARG
+    assert f(M=0) == E.AWQ_ERR_INVALID_ARG
+    assert f(bits=5) == E.AWQ_ERR_UNSUPPORTED
+    assert f() == E.AWQ_ERR_NO_DEVICE          # splits K
+    assert f(M=1) == E.AWQ_ERR_NO_DEVICE       # decode
+    assert f(M=2048, N=256) == E.AWQ_ERR_NO_DEVICE  # the largest plan: exactly 16 MiB
+    assert h.awq_w4a16_matmul_workspace_bytes(2048, 256, 4096, 4, 128) == 16 << 20
+
+
 def test_matmul_ws_validation():
     h = awq.lib()
     E = _lib

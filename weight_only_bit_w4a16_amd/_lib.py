@@ -36,6 +36,7 @@ SIGNATURES = {
     "awq_w4a16_matmul_kernel": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p]),
     "awq_w4a16_matmul_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "awq_w4a16_matmul_ws": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, _p]),
+    "awq_w4a16_matmul_noalloc": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),
     "awq_compact_group_params": (_i, [_p, _p, _i, _i, _i, _p, _p, _p]),
     "awq_w4a16_matmul_compact": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _i, _p]),
     "awq_w4a16_gate_up_silu": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),

@@ -1,9 +1,11 @@
 // C-ABI layer of libawq: argument validation (before any HIP call), device
-// check, dispatch to the kernel launchers, error mapping. Stateless.
+// check, dispatch to the kernel launchers, error mapping. Stateless apart
+// from the per-device address of the allocation-free product's scratch.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/awq.h"
 #include "awq_internal.h"
@@ -55,10 +57,49 @@ awq_status check_group(int K, int bits, int group, int* g_out) {
 // whether the automatic choice runs this shape on a decode kernel
 bool auto_decode(int M, int bits) { return bits == 4 ? M <= 16 : M <= awq::kGemvW3MaxM; }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of awq_w4a16_matmul_noalloc: the split-K planes of the product in
+// a file-scope device array instead of a caller workspace. A split plan runs
+// at most one workgroup per compute unit on tiles of at most 128 x 128
+// outputs, one float32 per output and split, so 256 units x 128 x 128 x 4 B
+// = 16 MiB holds every plan on a 256-unit GPU. Each GPU the library runs on
+// holds its own copy of the array until the process ends; host code reaches
+// it only through the device address looked up below, never by its name
+// (which on the host is a stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// the current device's address of `scratch`, looked up once per device with
+// that device current
+awq_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return AWQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return AWQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return AWQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AWQ_OK;
+}
+
+// ws / ws_bytes: a caller workspace (nullptr: none); noalloc: use the
+// file-scope scratch as the workspace
 awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* scales,
                        const void* zeros, int M, int N, int K, int bits, int group, uint16_t* Y,
                        void* stream, int kernel, bool cs, void* ws = nullptr,
-                       size_t ws_bytes = 0) {
+                       size_t ws_bytes = 0, bool noalloc = false) {
   if (!X || !qpacked || !scales || !zeros || !Y) return AWQ_ERR_INVALID_ARG;
   if (M <= 0 || N <= 0 || K <= 0) return AWQ_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(qpacked) || !aligned16(scales) || !aligned16(zeros) ||
@@ -76,8 +117,15 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* s
   const bool decode = kernel == 1 || kernel == 2 || (kernel == 0 && auto_decode(M, bits));
   if (ws != nullptr && !decode && ws_bytes < awq::gemm_workspace_bytes(M, N, K, bits))
     return AWQ_ERR_WORKSPACE;
+  if (noalloc && !decode && awq::gemm_workspace_bytes(M, N, K, bits) > kNoAllocScratchBytes)
+    return AWQ_ERR_WORKSPACE;
   st = device_ready();
   if (st != AWQ_OK) return st;
+  if (noalloc && !decode) {
+    st = noalloc_scratch(&ws);
+    if (st != AWQ_OK) return st;
+    ws_bytes = kNoAllocScratchBytes;
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const __half* x = reinterpret_cast<const __half*>(X);
@@ -218,6 +266,13 @@ awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const
                                void* stream) {
   return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, 0, false,
                      workspace, workspace_bytes);
+}
+
+awq_status awq_w4a16_matmul_noalloc(const uint16_t* X, const uint32_t* qpacked,
+                                    const float* scales, const uint8_t* zeros, int M, int N, int K,
+                                    int bits, int group, uint16_t* Y, void* stream) {
+  return matmul_impl(X, qpacked, scales, zeros, M, N, K, bits, group, Y, stream, 0, false,
+                     nullptr, 0, true);
 }
 
 awq_status awq_compact_group_params(const float* scales, const uint8_t* zeros, int N, int K,
