@@ -31,6 +31,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# BLAS threads for the oracle's timed leg: one per core this process may run
+# on, set before numpy is first imported (a value already in the environment
+# is kept); the leg records what the BLAS library actually uses
+HOST_CORES = len(os.sched_getaffinity(0))
+for _v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS"):
+    os.environ.setdefault(_v, str(HOST_CORES))
+
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 FP16_MFMA_PEAK_TF = 2500.0  # MI355X dense fp16 matrix, TFLOP/s
 
@@ -50,50 +57,182 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 256 MiB device copy first (a kernel of known "
                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters)")
-    p.add_argument("--cpu-seconds", type=float, default=8.0,
+    p.add_argument("--cpu-seconds", type=float, default=4.0,
                    help="approximate budget for the oracle's timed sample")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the per-configuration table")
+    p.add_argument("--kernels", action="store_true",
+                   help="only run each hot kernel a few times (decode M=1 and the prefill on "
+                        "the headline layer, the 16-row-block decode at M=8 on the "
+                        "11008x4096 layer, the search), for counter runs; no JSON line")
     return p.parse_args()
 
 
 def cpu_baseline(w, W, Xc, s_np, budget_s):
-    """The oracle, as it stands, on the host cores: the decode product on a
-    sample of output rows (same unit as `value`), plus the pack step."""
+    """The oracle, as it stands, on this host's cores: every step of the path
+    on bounded samples of the same workload, each timed alone and scaled to
+    the whole layer by its own unit of work.
+
+      search   oracle.scale_search (20 alpha, 512 calibration tokens) on a
+               sample of output rows; its work is linear in the rows
+      pack     oracle.quantize_pack of the whole matrix
+      prefill  oracle.matmul at the prefill M over a sample of output rows
+      decode   oracle.matmul at M = 1 over a sample of output rows (the
+               leg in `value`'s unit, GB/s of algorithmic bytes)
+      decode_1thread  the same at M = 1 on the 4096 x 4096 layer with one
+               BLAS thread
+
+    The sum of the scaled legs is the oracle's time for one step of the
+    path, beside the GPU's ms_per_step."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import awq_oracle as O
     import datagen
 
-    cores = len(os.sched_getaffinity(0))
-    X1 = O.fold_inv_scale(datagen.decode_input(w, 1), s_np)
-    rows = 256
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = blas[0]["num_threads"] if blas else None
+    per_row_bytes = O.words_per_row(w.K, w.bits, w.group) * 4 + (w.K // w.group) * 5 + 2
+    grid = datagen.alpha_grid(w.n_alpha)
+    legs = {}
+
+    # search on a row sample (the statistic and scales are whole-layer work
+    # that does not grow with the rows; they are included in the sample)
+    n_s = min(w.N, 384)
     t0 = time.perf_counter()
-    qp, sc, z = O.quantize_pack(W[:rows], s_np, w.bits, w.group)
-    t_pack = time.perf_counter() - t0
-    wpr = qp.shape[1]
-    # grow the sample until it takes about the budget
-    done_rows, t_mm = 0, 0.0
-    chunk = rows
-    while t_mm < budget_s and done_rows < w.N:
-        lo = done_rows
-        chunk = min(chunk, w.N - lo)
-        qpc, scc, zc = O.quantize_pack(W[lo:lo + chunk], s_np, w.bits, w.group)
+    O.scale_search(W[:n_s], Xc, grid, w.bits, w.group)
+    t = time.perf_counter() - t0
+    legs["search"] = {"sample_rows": n_s, "s": round(t, 3), "full_layer_s": round(t * w.N / n_s, 2),
+                      "tflops": round(2.0 * w.T * n_s * w.K * len(grid) / t / 1e12, 4)}
+
+    # the whole matrix
+    t0 = time.perf_counter()
+    qp, sc, z = O.quantize_pack(W, s_np, w.bits, w.group)
+    t = time.perf_counter() - t0
+    legs["pack"] = {"rows": w.N, "s": round(t, 3), "full_layer_s": round(t, 2),
+                    "gbs_of_fp16_W": round(w.N * w.K * 2 / t / 1e9, 3)}
+
+    # prefill at the workload's prefill M on a row sample
+    M_pre = w.prefill_M[0] if w.prefill_M else 2048
+    n_p = min(w.N, 256)
+    Xp = O.fold_inv_scale(datagen.decode_input(w, M_pre), s_np)
+    t0 = time.perf_counter()
+    O.matmul(Xp, qp[:n_p], sc[:n_p], z[:n_p], w.bits, w.group, w.K)
+    t = time.perf_counter() - t0
+    legs["prefill"] = {"M": M_pre, "sample_rows": n_p, "s": round(t, 3),
+                       "full_layer_s": round(t * w.N / n_p, 2),
+                       "gflops": round(2.0 * M_pre * n_p * w.K / t / 1e9, 2)}
+
+    # decode at M = 1: grow the row sample until it takes about the budget
+    X1 = O.fold_inv_scale(datagen.decode_input(w, 1), s_np)
+    done, t_mm, chunk = 0, 0.0, 256
+    while t_mm < budget_s and done < w.N:
+        c = min(chunk, w.N - done)
         t0 = time.perf_counter()
-        O.matmul(X1, qpc, scc, zc, w.bits, w.group, w.K)
+        O.matmul(X1, qp[done:done + c], sc[done:done + c], z[done:done + c], w.bits, w.group, w.K)
         t_mm += time.perf_counter() - t0
-        done_rows += chunk
+        done += c
         chunk = min(chunk * 2, 4096)
-    per_row_bytes = wpr * 4 + (w.K // w.group) * 5 + 2  # codes + scales + zeros + y
-    byt = done_rows * per_row_bytes + 2 * w.K
+    dec_gbs = (done * per_row_bytes + 2 * w.K) / t_mm / 1e9
+    legs["decode"] = {"M": 1, "sample_rows": done, "s": round(t_mm, 3),
+                      "full_layer_s": round(t_mm * w.N / done, 3), "gbs": round(dec_gbs, 4)}
+
+    # one BLAS thread, M = 1 on the 4096 x 4096 layer (all rows)
+    w2 = datagen.WORKLOADS["llama7b_attn_4096x4096_int4"]
+    W2 = datagen.weight(w2)
+    q2, s2, z2 = O.quantize_pack(W2, None, w2.bits, w2.group)
+    x2 = datagen.decode_input(w2, 1)
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        O.matmul(x2, q2, s2, z2, w2.bits, w2.group, w2.K)
+        t = time.perf_counter() - t0
+    b2 = w2.N * (O.words_per_row(w2.K, w2.bits, w2.group) * 4 + (w2.K // w2.group) * 5 + 2) + 2 * w2.K
+    legs["decode_1thread"] = {"workload": w2.name, "M": 1, "s": round(t, 3),
+                              "gbs": round(b2 / t / 1e9, 4)}
+
+    step_s = sum(legs[k]["full_layer_s"] for k in ("search", "pack", "prefill", "decode"))
     return {
-        "value": round(byt / t_mm / 1e9, 4),
+        "value": round(dec_gbs, 4),
         "unit": "GB/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle.matmul (float64, numpy BLAS) at M=1 over {done_rows} of {w.N} "
-                   f"output rows of {w.name}; oracle.quantize_pack of {rows} rows took "
-                   f"{t_pack:.2f} s ({rows * w.K * 2 / t_pack / 1e9:.3f} GB/s of fp16 W)"),
-        "threads_env": os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS"),
+        "sample": (f"{w.name}: oracle.matmul at M=1 over {done} of {w.N} output rows "
+                   f"(the value); search on {n_s} rows, pack of all rows, prefill M={M_pre} "
+                   f"on {n_p} rows, each scaled to the layer in 'legs'"),
+        "host_cores": HOST_CORES,
+        "blas": (f"{blas[0]['internal_api']} {blas[0].get('version')} {threads} threads"
+                 if blas else None),
+        "legs": legs,
+        "oracle_step_s": round(step_s, 1),
+    }
+
+
+def probe_lib():
+    import ctypes
+    h = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_w4a16_amd", "libawq_probe.so"))
+    P, I = ctypes.c_void_p, ctypes.c_int
+    h.awq_probe_stream_read.argtypes = [P, ctypes.c_size_t, I, P, P]
+    h.awq_probe_mfma.argtypes = [P, I, I, P, P]
+    h.awq_probe_clock.argtypes = [P, I, I, P]
+    for f in (h.awq_probe_stream_read, h.awq_probe_mfma, h.awq_probe_clock):
+        f.restype = I
+    return h
+
+
+def ceilings(torch, dev, stream, bufs, reps):
+    """Practical ceilings on this GPU, in this run: a streaming read of the
+    same rotated weight buffers the decode reads (16-byte nontemporal loads,
+    16 in flight per thread, 2048 workgroups: the fastest of the patterns
+    measured), and a loop of independent fp16 32x32x16 MFMAs on
+    random-valued operands (the clock the part holds under that load)."""
+    import ctypes
+    import numpy as np
+    h = probe_lib()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    out = torch.empty(8192, dtype=torch.int32, device=dev)
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+
+    def launch_all():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _ in range(reps):
+            for b in bufs:
+                assert h.awq_probe_stream_read(vp(b), nbytes // 16, 2048, vp(out), st) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch_all()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch_all()
+    g.replay()
+    ts = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3 / (reps * len(bufs))
+    del g
+    seed = (torch.rand(128 * 8, device=dev) * 2 - 1).half()
+    fout = torch.empty(4 * 1024, dtype=torch.float32, device=dev)
+    st = ctypes.c_void_p(stream.cuda_stream)
+    iters = 1000
+    assert h.awq_probe_mfma(vp(seed), 1024, 100, vp(fout), st) == 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    assert h.awq_probe_mfma(vp(seed), 1024, iters, vp(fout), st) == 0
+    b.record(stream)
+    torch.cuda.synchronize()
+    mfma_flops = 1024 * 4 * iters * 8 * (2.0 * 32 * 32 * 16)
+    return {
+        "stream_read_bytes": nbytes, "stream_read_us": round(us, 2),
+        "stream_read_gbs": round(nbytes / us / 1e3, 1),
+        "mfma_probe_tflops": round(mfma_flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1),
     }
 
 
@@ -101,8 +240,8 @@ def config_table(awq, torch, datagen, dev, stream):
     """Every workload's product at each of its decode and prefill M, on
     rotated copies of its packed weights (at least 512 MiB in all, at most
     64 copies: the smallest layer stays partly in the 256 MB cache), timed
-    with HIP events around a replayed graph of back-to-back calls (two
-    passes over the copies). Weights ~ N(0, 0.02), activations ~ N(0, 1)."""
+    with HIP events around a replayed graph of back-to-back calls (passes
+    over the copies, at least 32 calls). Weights ~ N(0, 0.02), activations ~ N(0, 1)."""
     import numpy as np
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
@@ -124,9 +263,12 @@ def config_table(awq, torch, datagen, dev, stream):
                     awq.w4a16_matmul(X, *sets[r], w.bits, w.group, out=Y)
             stream.wait_stream(side)
             torch.cuda.synchronize()
+            # at least 32 calls per graph, as in the headline measurement (the
+            # graph's own start-up spread over as many launches)
+            passes = max(2, -(-32 // R))
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(2):
+                for _ in range(passes):
                     for r in range(R):
                         awq.w4a16_matmul(X, *sets[r], w.bits, w.group, out=Y)
             g.replay()
@@ -138,7 +280,7 @@ def config_table(awq, torch, datagen, dev, stream):
                 b.record(stream)
                 times.append((a, b))
             torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3 / (2 * R)
+            us = float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3 / (passes * R)
             del g
             byt = packed + 2 * M * w.K + 2 * M * w.N
             fl = 2.0 * M * w.N * w.K
@@ -152,6 +294,50 @@ def config_table(awq, torch, datagen, dev, stream):
         del sets
         torch.cuda.empty_cache()
     return table
+
+
+def copy_calibration(torch, dev):
+    """One plain device copy of 256 MiB: a kernel of known traffic (256 MiB
+    read, 256 MiB written), to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def kernels_only(awq, torch, datagen, dev):
+    """A few launches of each hot kernel on cold weights, for counter runs
+    (rocprofv3 --pmc serializes every dispatch): on the headline layer the
+    search, the pack, 10 decode launches at M = 1 over 5 rotated copies and
+    2 prefill launches at M = 2048; on the 11008 x 4096 layer 10 launches of
+    the 16-row-block decode kernel at M = 8 over 24 rotated copies."""
+    w = datagen.WORKLOADS[datagen.HEADLINE]
+    W = torch.from_numpy(datagen.weight(w)).to(dev)
+    Xc = torch.from_numpy(datagen.calibration(w)).to(dev)
+    grid = datagen.alpha_grid(w.n_alpha)
+    s, _, _ = awq.scale_search(W, Xc, grid, w.bits, w.group)
+    copies = [awq.quantize_pack(W, s, w.bits, w.group) for _ in range(5)]
+    del W
+    X1 = awq.fold_inv_scale(torch.from_numpy(datagen.decode_input(w, 1)).to(dev), s)
+    for i in range(10):
+        awq.w4a16_matmul(X1, *copies[i % 5], w.bits, w.group)
+    Xp = awq.fold_inv_scale(torch.from_numpy(datagen.decode_input(w, 2048)).to(dev), s)
+    for i in range(2):
+        awq.w4a16_matmul(Xp, *copies[i], w.bits, w.group)
+    torch.cuda.synchronize()
+    del copies, Xp
+    w = datagen.WORKLOADS["llama7b_mlp_down_11008x4096_int4"]
+    Wd = torch.from_numpy(datagen.weight(w)).to(dev)
+    q = awq.quantize_pack(Wd, None, w.bits, w.group)
+    copies = [q] + [tuple(t.clone() for t in q) for _ in range(23)]
+    X8 = torch.from_numpy(datagen.decode_input(w, 8)).to(dev)
+    for i in range(10):
+        awq.w4a16_matmul(X8, *copies[(2 * i) % 24], w.bits, w.group)
+    torch.cuda.synchronize()
+    print("kernels done", flush=True)
 
 
 def main():
@@ -170,6 +356,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.kernels:
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        kernels_only(awq, torch, datagen, dev)
+        return
     w = datagen.WORKLOADS[args.workload or datagen.HEADLINE]
     M_dec = 1
     M_pre = w.prefill_M[0] if w.prefill_M else 2048
@@ -201,6 +392,17 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     rec = {"search": [], "pack": [], "fold": [], "prefill": [], "decode_batch": []}
+    # shader clock: one short probe launch after each decode graph (and a
+    # few at idle), compared with the 100 MHz real-time counter
+    import ctypes
+    plib = probe_lib()
+    clk = torch.zeros(2 * (args.steps + args.warmup + 16), dtype=torch.int64, device=dev)
+    clk_slot = [0]
+
+    def clock_probe():
+        assert plib.awq_probe_clock(ctypes.c_void_p(clk.data_ptr()), clk_slot[0], 200,
+                                    ctypes.c_void_p(stream.cuda_stream)) == 0
+        clk_slot[0] += 1
 
     def step(i, timed):
         e = {k: (ev(), ev()) for k in ("search", "pack", "fold", "prefill")}
@@ -226,6 +428,7 @@ def main():
         ba.record(stream)
         graphs[i % R].replay()
         bb.record(stream)
+        clock_probe()
         if timed:
             for k in e:
                 rec[k].append(e[k])
@@ -233,13 +436,7 @@ def main():
         return best
 
     if args.copy_calibration:
-        a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        copy_calibration(torch, dev)
 
     # fill every copy once, then warm up
     s0, _, _ = awq.scale_search(W, Xc, grid, w.bits, w.group, workspace=ws)
@@ -263,14 +460,25 @@ def main():
                     awq.w4a16_matmul(X1f, *copies[(g + r) % R], w.bits, w.group, out=Y1)
         graphs.append(cg)
     torch.cuda.synchronize()
+    for _ in range(8):  # idle clock
+        clock_probe()
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    clk_first_timed = clk_slot[0]
     t0 = time.perf_counter()
     for i in range(args.steps):
         best = step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    ck = clk.cpu().numpy().reshape(-1, 2)[: clk_slot[0]].astype(np.float64)
+    mhz = ck[:, 0] / np.maximum(ck[:, 1], 1.0) * 100.0
+    clock = {"idle_mhz": round(float(np.median(mhz[:8])), 0),
+             "after_decode_mhz_mean": round(float(np.mean(mhz[clk_first_timed:])), 0),
+             "after_decode_mhz_min": round(float(np.min(mhz[clk_first_timed:])), 0)}
+    ceil = ceilings(torch, dev, stream, [c[0] for c in copies], 4)
 
     # context, outside the timed steps: the same layer unquantized, torch's
     # fp16 F.linear (hipBLASLt) on the fp16 W, as a black box. The pages'
@@ -379,6 +587,12 @@ def main():
             "kernel": f"prefill GEMM (M={M_pre})", "flops_per_launch": pre_flops,
             "mean_us": round(pre_ms * 1e3, 1),
         },
+        "ceilings": dict(ceil, **{
+            "what": "same run: streaming read of the rotated weight buffers, fp16 MFMA loop",
+            "decode_frac_of_stream_read": round(dec_gbs / ceil["stream_read_gbs"], 4),
+            "prefill_frac_of_mfma_probe": round(pre_tfs / ceil["mfma_probe_tflops"], 4),
+        }),
+        "shader_clock": clock,
         "context_fp16_linear": {
             "what": "torch F.linear on the fp16 W of the same layer (hipBLASLt), black box",
             "decode_M1_us": round(lin_dec_ms * 1e3, 2),
