@@ -169,20 +169,26 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
 /* Bytes of device workspace with which awq_w4a16_matmul_ws splits the K
  * range of this product over several workgroups per output tile (0: the
  * shape runs without splitting, or the arguments are invalid). Splitting is
- * used when even the smallest prefill tiles leave compute units idle: M
- * beyond the decode range with few output tiles (for example M = 17..256 on
- * a 4096-wide layer). */
+ * used when even the smallest prefill tiles leave compute units idle (M
+ * beyond the decode range with few output tiles, for example M = 17..256 on
+ * a 4096-wide layer), and by the int4 decode kernel for 2 <= M <= 16 on
+ * rows of more than 8192 codes. The bytes are a 64 KiB counter region
+ * followed by one float32 [M, N] plane per split. */
 size_t awq_w4a16_matmul_workspace_bytes(int M, int N, int K, int bits, int group);
 
 /* awq_w4a16_matmul with a workspace (same arithmetic contract). With a
  * split, every split writes its float32 sums over its part of K to its own
- * [M, N] plane of the workspace and a second kernel adds the planes in split
- * order, so the result does not depend on timing. workspace: dev, 16-byte
- * aligned, at least awq_w4a16_matmul_workspace_bytes(M, N, K, bits, group)
- * bytes, any contents, owned by the caller; calls that share a workspace
- * must be ordered on one stream. NULL runs without splitting; a non-NULL
- * workspace that is too small returns AWQ_ERR_WORKSPACE. Asynchronous on
- * `stream`. */
+ * [M, N] plane of the workspace, and the planes are added in split order
+ * (prefill: by a second kernel; int4 decode: by the split that finishes a
+ * 16-row block of outputs last, which it learns from that block's counter
+ * in the workspace's first 64 KiB), so the result does not depend on
+ * timing. workspace: dev, 16-byte aligned, at least
+ * awq_w4a16_matmul_workspace_bytes(M, N, K, bits, group) bytes, owned by
+ * the caller; its first 64 KiB zero-filled before the first call that uses
+ * it (every call leaves them zero; the rest may hold anything); calls that
+ * share a workspace must be ordered on one stream. NULL runs without
+ * splitting; a non-NULL workspace that is too small returns
+ * AWQ_ERR_WORKSPACE. Asynchronous on `stream`. */
 awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const float* scales,
                                const uint8_t* zeros, int M, int N, int K, int bits, int group,
                                uint16_t* Y, void* workspace, size_t workspace_bytes,
@@ -191,16 +197,17 @@ awq_status awq_w4a16_matmul_ws(const uint16_t* X, const uint32_t* qpacked, const
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
  * product of awq_w4a16_matmul_ws, same arguments, kernels and results,
- * with the split-K planes in a scratch array the library holds in device
- * memory (16 MiB on each GPU it runs on, from first load to the end of the
- * process) instead of a caller workspace. The call allocates nothing; the
- * caller still owns X, qpacked, scales, zeros and Y. A shape whose split
- * plan needs more than 16 MiB returns AWQ_ERR_WORKSPACE (on a 256-unit GPU
- * every plan fits). Every call on one GPU shares that GPU's scratch and
- * leaves its contents behind (nothing in it needs clearing: each split
- * writes its whole plane before the planes are added), so calls that
- * overlap on one GPU race: order them on one stream. The first call on a
- * device looks up the scratch's address there (no allocation).
+ * with the workspace (counter region and split-K planes) in a scratch
+ * array the library holds in device memory (16 MiB + 64 KiB on each GPU it
+ * runs on, zero when loaded, from first load to the end of the process)
+ * instead of a caller workspace. The call allocates nothing; the caller
+ * still owns X, qpacked, scales, zeros and Y. A shape whose split plan
+ * needs more than that returns AWQ_ERR_WORKSPACE (on a 256-unit GPU every
+ * prefill plan fits, and every decode plan with N * K up to about 1.9e9 at
+ * M <= 8, 5.4e8 at M <= 16). Every call on one GPU shares that
+ * GPU's scratch and leaves its planes behind and its counters zero, so calls
+ * that overlap on one GPU race: order them on one stream. The first call on
+ * a device looks up the scratch's address there (no allocation).
  * Asynchronous on `stream`. */
 awq_status awq_w4a16_matmul_noalloc(const uint16_t* X, const uint32_t* qpacked,
                                     const float* scales, const uint8_t* zeros, int M, int N, int K,

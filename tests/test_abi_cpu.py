@@ -101,21 +101,36 @@ def test_matmul_validation():
 
 def test_matmul_workspace_plan():
     """The split plan on a 256-compute-unit part (the count assumed without a
-    device): tiles 128 wide and 32, 64 or 128 tall, split over K until about
-    one workgroup per unit; decode shapes and shapes that fill the part need
-    none. Bytes: one float32 [M, N] plane per split."""
+    device): prefill tiles 128 wide and 32, 64 or 128 tall, split over K until
+    about one workgroup per unit; int4 decode at 2 <= M <= 16 on rows of
+    more than 8192 codes, 16-row blocks split over K until about 8
+    wavefronts per unit; other decode shapes and shapes that fill the part
+    need none. Bytes: one float32 [M, N] plane per split, after a 64 KiB
+    counter region."""
     h = awq.lib()
     W = h.awq_w4a16_matmul_workspace_bytes
-    assert W(16, 4096, 4096, 4, 128) == 0  # decode kernel
-    assert W(4, 4096, 4096, 3, 128) == 0
+    C = 64 << 10  # the counter region at the head of a split workspace
+    assert W(4, 4096, 4096, 3, 128) == 0  # int3 decode kernel
+    assert W(1, 4096, 4096, 4, 128) == 0  # M = 1 decode kernel
+    assert W(2, 4096, 4096, 4, 128) == 0  # M = 2 on the per-token-row decode kernel
+    # int4 decode, 2 <= M <= 16: rows of up to 8192 codes run unsplit on the
+    # one-pass kernel
+    assert W(16, 4096, 4096, 4, 128) == 0
+    assert W(8, 28672, 8192, 4, 128) == 0
+    # longer rows: 16-row blocks, K split for 8 wavefronts per unit and the
+    # LDS (29 chunks of 128 codes at M <= 8, 16 at M <= 16); 11008 = 86
+    # chunks in 8 splits of 11 (the last one 9), one [M, N] plane per split
+    assert W(8, 4096, 11008, 4, 128) == C + 8 * 8 * 4096 * 4
+    # 28672 codes = 224 chunks at M = 16: 14 splits of 16
+    assert W(16, 8192, 28672, 4, 128) == C + 14 * 16 * 8192 * 4
     assert W(2048, 28672, 8192, 4, 128) == 0  # whole rounds of big tiles
     assert W(256, 11008, 4096, 3, 128) == 0  # 172 tiles of 128 x 128: no split
     # int4, M = 32: 32 tiles of 32 x 128, 8 splits of 8 steps (64 codes each)
-    assert W(32, 4096, 4096, 4, 128) == 8 * 32 * 4096 * 4
+    assert W(32, 4096, 4096, 4, 128) == C + 8 * 32 * 4096 * 4
     # int3, M = 64: 32 tiles of 64 x 128; 86 steps of 128 codes in 8 splits
-    assert W(64, 4096, 11008, 3, 128) == 8 * 64 * 4096 * 4
+    assert W(64, 4096, 11008, 3, 128) == C + 8 * 64 * 4096 * 4
     # M = 256: 64 tiles of 128 x 128 in 4 splits
-    assert W(256, 4096, 11008, 3, 128) == 4 * 256 * 4096 * 4
+    assert W(256, 4096, 11008, 3, 128) == C + 4 * 256 * 4096 * 4
     # few steps: at least 8 per split (K = 512: 8 steps, no split)
     assert W(32, 256, 512, 4, 128) == 0
     assert W(32, 4096, 4096, 5, 128) == 0  # invalid
@@ -136,8 +151,8 @@ def test_matmul_noalloc_validation():
     assert f(bits=5) == E.AWQ_ERR_UNSUPPORTED
     assert f() == E.AWQ_ERR_NO_DEVICE          # splits K
     assert f(M=1) == E.AWQ_ERR_NO_DEVICE       # decode
-    assert f(M=2048, N=256) == E.AWQ_ERR_NO_DEVICE  # the largest plan: exactly 16 MiB
-    assert h.awq_w4a16_matmul_workspace_bytes(2048, 256, 4096, 4, 128) == 16 << 20
+    assert f(M=2048, N=256) == E.AWQ_ERR_NO_DEVICE  # the largest plan: 16 MiB of planes
+    assert h.awq_w4a16_matmul_workspace_bytes(2048, 256, 4096, 4, 128) == (16 << 20) + (64 << 10)
 
 
 def test_matmul_ws_validation():
@@ -145,16 +160,23 @@ def test_matmul_ws_validation():
     E = _lib
     need = h.awq_w4a16_matmul_workspace_bytes(32, 4096, 4096, 4, 128)
 
-    def ws(w, nbytes, M=32):
-        return h.awq_w4a16_matmul_ws(P, P, P, P, M, 4096, 4096, 4, 128, P2, w, nbytes, NULL)
+    def ws(w, nbytes, M=32, K=4096):
+        return h.awq_w4a16_matmul_ws(P, P, P, P, M, 4096, K, 4, 128, P2, w, nbytes, NULL)
 
     assert ws(P, need - 16) == E.AWQ_ERR_WORKSPACE
     assert ws(MIS, need) == E.AWQ_ERR_INVALID_ARG
+    # the int4 decode kernel for 2 <= M <= 16 splits long rows with a
+    # workspace too
+    need8 = h.awq_w4a16_matmul_workspace_bytes(8, 4096, 11008, 4, 128)
+    assert need8 > 0
+    assert ws(P, need8 - 16, M=8, K=11008) == E.AWQ_ERR_WORKSPACE
     import torch
     if not torch.cuda.is_available():  # valid requests: no device to run them
         assert ws(P, need) == E.AWQ_ERR_NO_DEVICE
         assert ws(NULL, 0) == E.AWQ_ERR_NO_DEVICE
-        assert ws(P, 0, M=8) == E.AWQ_ERR_NO_DEVICE  # decode shapes ignore the workspace
+        assert ws(P, need8, M=8, K=11008) == E.AWQ_ERR_NO_DEVICE
+        assert ws(NULL, 0, M=8, K=11008) == E.AWQ_ERR_NO_DEVICE  # runs on the multi-pass kernel
+        assert ws(P, 0, M=1) == E.AWQ_ERR_NO_DEVICE  # the M = 1 kernel takes no workspace
 
 
 def test_valid_calls_without_device_report_no_device():

@@ -445,7 +445,7 @@ def test_prefill_split_k_then_other_shapes():
     """One workspace serves calls of different shapes in a row (and the
     automatic per-stream workspace of the binding too)."""
     K = 4096
-    ws = torch.empty(awq.matmul_workspace_bytes(64, 4096, K, 4, 128), dtype=torch.uint8,
+    ws = torch.zeros(awq.matmul_workspace_bytes(64, 4096, K, 4, 128), dtype=torch.uint8,
                      device="cuda")
     for M, N in [(64, 4096), (20, 1500), (64, 4096), (33, 640)]:
         W = datagen.random_f16((N, K), 0.02, seed=N)
@@ -477,7 +477,7 @@ def test_prefill_split_k_workspace_contract():
     assert_rows_close(Yu, Yo)
     nb = awq.matmul_workspace_bytes(M, N, K)
     assert nb > 0
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     h = awq.lib()
     p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731

@@ -3,7 +3,7 @@ the C ABI, against the product with a caller workspace
 (awq_w4a16_matmul_ws): the same kernels and split plan, so the same bits.
 Two calls in a row on one GPU, the second on a smaller problem (the scratch
 keeps the first call's contents), for shapes that split K (int4 and int3),
-a shape that does not and a decode shape."""
+a shape that does not, an M = 1 decode shape and decode shapes that split K."""
 import ctypes
 
 import numpy as np
@@ -46,7 +46,7 @@ def _with_workspace(X, q, sc, z, bits):
     M, K = X.shape
     N = q.shape[0]
     nb = awq.matmul_workspace_bytes(M, N, K, bits, 128)
-    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda") if nb else None
+    ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda") if nb else None
     Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
     r = awq.lib().awq_w4a16_matmul_ws(_p(X), _p(q), _p(sc), _p(z), M, N, K, bits, 128, _p(Y),
                                      _p(ws), nb, _stream())
@@ -62,6 +62,7 @@ PAIRS = [
     ((33, 3000, 4096, 3), (20, 1000, 4096, 3)),      # int3 split K
     ((300, 2048, 2048, 4), (40, 700, 1024, 4)),      # no split
     ((1, 4096, 4096, 4), (1, 1024, 2048, 4)),        # decode
+    ((16, 4096, 11008, 4), (8, 2000, 16384, 4)),     # decode split K, 16 then 8 token rows
 ]
 
 

@@ -176,7 +176,8 @@ def _matmul_workspace(device, stream_handle, nbytes: int):
            int(getattr(stream_handle, "value", stream_handle) or 0))
     ws = _MATMUL_WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        # zero-filled: the split products keep their counters at its head
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _MATMUL_WS[key] = ws
     return ws
 
@@ -185,10 +186,10 @@ def w4a16_matmul(Xp, qpacked, scales, zeros, bits: int = 4, group: int = 128, ou
                  kernel: int = KERNEL_AUTO, stream=None, workspace=None):
     """Y = X' dequant(Q)^T (fp16 [M, N]) with X' already divided by s.
 
-    With the automatic kernel choice, shapes that split K (small M x N
-    beyond the decode range) use `workspace` (a uint8 device tensor of at
-    least matmul_workspace_bytes(...) bytes, shared only by calls ordered on
-    one stream) or, when None, one kept per device and stream."""
+    With the automatic kernel choice, shapes that split K use `workspace`
+    (a uint8 device tensor of at least matmul_workspace_bytes(...) bytes,
+    zero-filled before its first use, shared only by calls ordered on one
+    stream) or, when None, one kept per device and stream."""
     torch = _torch()
     _need(Xp, "Xp", torch.float16, 2)
     _need(qpacked, "qpacked", torch.int32, 2)

@@ -40,6 +40,7 @@ COMMON = [
 # VGPRs (they are read back right away), the prefill kernel in AGPRs
 EXTRA = {
     "k_gemv.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    "k_gemv_mb.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -60,15 +60,18 @@ bool auto_decode(int M, int bits) { return bits == 4 ? M <= 16 : M <= awq::kGemv
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Scratch of awq_w4a16_matmul_noalloc: the split-K planes of the product in
-// a file-scope device array instead of a caller workspace. A split plan runs
-// at most one workgroup per compute unit on tiles of at most 128 x 128
-// outputs, one float32 per output and split, so 256 units x 128 x 128 x 4 B
-// = 16 MiB holds every plan on a 256-unit GPU. Each GPU the library runs on
-// holds its own copy of the array until the process ends; host code reaches
-// it only through the device address looked up below, never by its name
-// (which on the host is a stand-in, not a device address).
-constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+// Scratch of awq_w4a16_matmul_noalloc: the workspace of a split product
+// (its counter region, then the split-K planes) in a file-scope device array
+// instead of a caller workspace. A prefill split plan runs at most one
+// workgroup per compute unit on tiles of at most 128 x 128 outputs, one
+// float32 per output and split, so 256 units x 128 x 128 x 4 B = 16 MiB of
+// planes hold every prefill plan on a 256-unit GPU; the array adds the
+// counter region. It is zero when the code object is loaded (a zero-filled
+// section), and every call leaves its counters zero. Each GPU the library
+// runs on holds its own copy of the array until the process ends; host code
+// reaches it only through the device address looked up below, never by its
+// name (which on the host is a stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = ((size_t)16 << 20) + awq::kSplitCtrBytes;
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
@@ -115,17 +118,21 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* s
   if (kernel == 2 && bits == 3) return AWQ_ERR_UNSUPPORTED;
   if (ws != nullptr && !aligned16(ws)) return AWQ_ERR_INVALID_ARG;
   const bool decode = kernel == 1 || kernel == 2 || (kernel == 0 && auto_decode(M, bits));
-  if (ws != nullptr && !decode && ws_bytes < awq::gemm_workspace_bytes(M, N, K, bits))
-    return AWQ_ERR_WORKSPACE;
-  if (noalloc && !decode && awq::gemm_workspace_bytes(M, N, K, bits) > kNoAllocScratchBytes)
-    return AWQ_ERR_WORKSPACE;
+  // the workspace the automatic choice splits K with (the forced decode
+  // kernels take none)
+  const size_t need = kernel != 0 ? 0
+                      : decode    ? (bits == 4 ? awq::gemv_workspace_bytes(M, N, K) : 0)
+                                  : awq::gemm_workspace_bytes(M, N, K, bits);
+  if (ws != nullptr && ws_bytes < need) return AWQ_ERR_WORKSPACE;
+  if (noalloc && need > kNoAllocScratchBytes) return AWQ_ERR_WORKSPACE;
   st = device_ready();
   if (st != AWQ_OK) return st;
-  if (noalloc && !decode) {
+  if (noalloc && need > 0) {
     st = noalloc_scratch(&ws);
     if (st != AWQ_OK) return st;
     ws_bytes = kNoAllocScratchBytes;
   }
+  if (kernel != 0) ws = nullptr;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const __half* x = reinterpret_cast<const __half*>(X);
@@ -134,7 +141,7 @@ awq_status matmul_impl(const uint16_t* X, const uint32_t* qpacked, const void* s
   if (decode) {
     if (bits == 4)
       e = awq::launch_gemv_w4(x, qpacked, scales, zeros, M, N, K, g, y, s, kernel == 2 ? 1 : 0,
-                              cs);
+                              cs, ws, ws_bytes);
     else if (M == 1 && kernel == 0)
       e = awq::launch_gemv_w3_m1(x, qpacked, scales, zeros, N, K, g, y, s, cs);
     else if (kernel == 0)
@@ -256,7 +263,7 @@ awq_status awq_w4a16_matmul_kernel(const uint16_t* X, const uint32_t* qpacked, c
 size_t awq_w4a16_matmul_workspace_bytes(int M, int N, int K, int bits, int group) {
   int g = 0;
   if (M <= 0 || N <= 0 || check_group(K, bits, group, &g) != AWQ_OK) return 0;
-  if (auto_decode(M, bits)) return 0;
+  if (auto_decode(M, bits)) return bits == 4 ? awq::gemv_workspace_bytes(M, N, K) : 0;
   return awq::gemm_workspace_bytes(M, N, K, bits);
 }
 

@@ -52,9 +52,31 @@ hipError_t launch_fold(const __half* X, const float* s, int M, int K, __half* Y,
 //
 // decode, int4, M <= 16. variant 0 picks the fastest kernel for the shape;
 // variant 1 forces the exact-dequant kernel (kept selectable for tests).
+// ws / ws_bytes: a workspace of at least gemv_workspace_bytes(M, N, K)
+// bytes lets 2 <= M <= 16 split K over workgroups (nullptr: no split).
 hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const void* scales,
                           const void* zeros, int M, int N, int K, int group, __half* Y,
-                          hipStream_t st, int variant, bool cs);
+                          hipStream_t st, int variant, bool cs, void* ws = nullptr,
+                          size_t ws_bytes = 0);
+// bytes of workspace the automatic int4 decode choice splits K with (0:
+// none for this shape)
+size_t gemv_workspace_bytes(int M, int N, int K);
+// decode, int4, 2 <= M <= 16 on 16-row blocks with the activations in LDS
+// (gemv_w4_mb_kernel): token rows stored (8 or 16), K splits, chunks of 128
+// codes per split, workgroups per split, LDS bytes, workspace bytes. splits
+// is 0 when the shape needs a split and can_split is false.
+struct MbPlan {
+  int mp, splits, spl, gx;
+  size_t lds, ws_bytes;
+};
+MbPlan mb_plan(int M, int N, int K, bool can_split);
+// whether the automatic int4 decode choice for 2 <= M <= 16 takes this
+// kernel (rows longer than one pass of gemv_w4_mx_kernel)
+bool mb_preferred(int M, int N, int K);
+// hipErrorNotSupported (nothing launched) when the plan has no splits
+hipError_t launch_gemv_w4_mb(const __half* X, const uint32_t* q, const void* scales,
+                             const void* zeros, int M, int N, int K, int group, __half* Y,
+                             hipStream_t st, bool cs, void* ws, size_t ws_bytes);
 // decode, int3, M <= 4
 hipError_t launch_gemv_w3(const __half* X, const uint32_t* q, const void* scales,
                           const void* zeros, int M, int N, int K, int group, __half* Y,
@@ -69,6 +91,11 @@ hipError_t launch_gemv_w3_mt(const __half* X, const uint32_t* q, const void* sca
 hipError_t launch_gemv_w3_m1(const __half* X, const uint32_t* q, const void* scales,
                              const void* zeros, int N, int K, int group, __half* Y, hipStream_t st,
                              bool cs);
+// The workspace of a product that splits K: a counter region first (one
+// uint32 per 16-row block of outputs; zero before the first call, and every
+// call leaves it zero), then the splits' float32 [M, N] planes.
+constexpr size_t kSplitCtrBytes = 64 * 1024;
+constexpr int kSplitMaxRowBlocks = (int)(kSplitCtrBytes / 4);
 // prefill (any M)
 hipError_t launch_gemm(const __half* X, const uint32_t* q, const void* scales, const void* zeros,
                        int M, int N, int K, int bits, int group, __half* Y, hipStream_t st,

@@ -719,8 +719,9 @@ GemmPlan gemm_plan(int M, int N, int K, int bits, bool can_split) {
   return p;
 }
 
+// planes after the counter region (which this kernel leaves alone)
 size_t plan_workspace_bytes(const GemmPlan& p, int M, int N) {
-  return p.splits <= 1 ? 0 : (size_t)p.splits * M * N * 4;
+  return p.splits <= 1 ? 0 : kSplitCtrBytes + (size_t)p.splits * M * N * 4;
 }
 
 // Y = fp16(sum of the split planes), added in split order
@@ -751,7 +752,9 @@ hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales,
   const bool zw = !CS && ((size_t)N * (size_t)(K / group)) % 4 == 0;
   const GemmPlan plan = gemm_plan(M, N, K, bits, ws != nullptr);
   if (plan.splits > 1 && ws_bytes < plan_workspace_bytes(plan, M, N)) return hipErrorInvalidValue;
-  float* wsf = plan.splits > 1 ? static_cast<float*>(ws) : nullptr;
+  float* wsf = plan.splits > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCtrBytes)
+                   : nullptr;
   const unsigned nsp = (unsigned)plan.splits;
 #define AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, NB, NE, SKV)                                   \
   do {                                                                                          \

@@ -1771,10 +1771,32 @@ hipError_t launch_gemv_w4_mx(const __half* X, const uint32_t* q, const void* sca
                                          zeros2);
 }
 
+// 2 <= M <= 4 on short rows: the M = 1 scheme per token row
+// (gemv_w4_mt_kernel); the pieces of a row, wavefronts per row, pieces per
+// wavefront and row wavefronts, and whether the automatic choice takes it
+struct MtChoice {
+  int np, seg, sp, rw;
+  bool use;
+};
+MtChoice mt_choice(int M, int N, int nch) {
+  MtChoice c;
+  c.np = (nch + 15) / 16;
+  c.seg = M * c.np <= kMtMaxItems ? 1 : 2;
+  c.sp = (c.np + c.seg - 1) / c.seg;
+  c.rw = cu_count() * (M * c.sp <= 4 ? 12 : 8) / c.seg;
+  // Two wavefronts per row only at M = 2 on 5-6 pieces (11008x4096 18.9 ->
+  // 12.2 us): at 7-8 pieces they would need more than 256 registers, and at
+  // M = 3, 4 (16 and 12 MFMAs plus about 40 VALU instructions per KB) they
+  // were slower than the 16-row-block kernel (8192x28672 M = 4 37.8 -> 50 us).
+  c.use = M >= 2 && M <= 4 && M * c.sp <= kMtMaxItems && (c.seg == 1 || (M == 2 && c.sp <= 3)) &&
+          (M == 2 || N >= 3 * c.rw);
+  return c;
+}
+
 template <bool CS>
 hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scales,
                             const void* zeros, int M, int N, int K, int group, __half* Y,
-                            hipStream_t st, int variant) {
+                            hipStream_t st, int variant, void* ws, size_t ws_bytes) {
   const int gshift = log2i(group / 128);
   const int nrb = (N + 15) / 16;
   const int nch = K / 128;
@@ -1793,18 +1815,10 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
   // 12.6 us, while 4096 rows at M = 4 went from 7.9 to 8.1). 3 wavefronts
   // per SIMD at up to 4 token-row pieces (128-136 registers; 4096x11008
   // M = 2 10.2 -> 9.4 us), else 2.
-  const int mtnp = (nch + 15) / 16;                 // pieces of a row
-  const int mtseg = M * mtnp <= kMtMaxItems ? 1 : 2;  // wavefronts per row
-  const int mtsp = (mtnp + mtseg - 1) / mtseg;      // pieces per wavefront
-  const int mtrw = cu_count() * (M * mtsp <= 4 ? 12 : 8) / mtseg;  // row wavefronts
-  // Two wavefronts per row only at M = 2 on 5-6 pieces (11008x4096 18.9 ->
-  // 12.2 us): at 7-8 pieces they would need more than 256 registers, and at
-  // M = 3, 4 (16 and 12 MFMAs plus about 40 VALU instructions per KB) they
-  // were slower than the 16-row-block kernel (8192x28672 M = 4 37.8 -> 50 us).
-  if (variant == 0 && M >= 2 && M <= 4 && M * mtsp <= kMtMaxItems &&
-      (mtseg == 1 || (M == 2 && mtsp <= 3)) && (M == 2 || N >= 3 * mtrw)) {
-    const int sp = mtsp, seg = mtseg;
-    const int nrw = min(N, max(mtrw, (N + 63) / 64));
+  const MtChoice mt = mt_choice(M, N, nch);
+  if (variant == 0 && mt.use) {
+    const int sp = mt.sp, seg = mt.seg;
+    const int nrw = min(N, max(mt.rw, (N + 63) / 64));
     const dim3 g1((unsigned)((nrw * seg + 3) / 4));
     const bool full = nch == 16 * sp * seg;
     const size_t lds = mt_lds_bytes(M, sp * seg, seg);
@@ -1845,6 +1859,11 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
     return hipGetLastError();
   }
   if (variant == 0 && M >= 2) {
+    if (mb_preferred(M, N, K)) {
+      const hipError_t e =
+          launch_gemv_w4_mb(X, q, scales, zeros, M, N, K, group, Y, st, CS, ws, ws_bytes);
+      if (e != hipErrorNotSupported) return e;
+    }
     const hipError_t e = launch_gemv_w4_mx_t<CS>(X, q, scales, zeros, M, N, K, group, Y, st,
                                                  nullptr, nullptr, nullptr);
     if (e != hipErrorNotSupported) return e;
@@ -1927,11 +1946,18 @@ hipError_t launch_gemv_w4_t(const __half* X, const uint32_t* q, const void* scal
   return hipGetLastError();
 }
 
+size_t gemv_workspace_bytes(int M, int N, int K) {
+  if (M < 2 || M > 16 || mt_choice(M, N, K / 128).use || !mb_preferred(M, N, K)) return 0;
+  return mb_plan(M, N, K, true).ws_bytes;
+}
+
 hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const void* scales,
                           const void* zeros, int M, int N, int K, int group, __half* Y,
-                          hipStream_t st, int variant, bool cs) {
-  return cs ? launch_gemv_w4_t<true>(X, q, scales, zeros, M, N, K, group, Y, st, variant)
-            : launch_gemv_w4_t<false>(X, q, scales, zeros, M, N, K, group, Y, st, variant);
+                          hipStream_t st, int variant, bool cs, void* ws, size_t ws_bytes) {
+  return cs ? launch_gemv_w4_t<true>(X, q, scales, zeros, M, N, K, group, Y, st, variant, ws,
+                                     ws_bytes)
+            : launch_gemv_w4_t<false>(X, q, scales, zeros, M, N, K, group, Y, st, variant, ws,
+                                      ws_bytes);
 }
 
 // Fused gate/up decode at M = 1, int4: Y = fp16(silu(X Wg^T) * (X Wu^T)).
