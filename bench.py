@@ -311,9 +311,10 @@ def copy_calibration(torch, dev):
 def kernels_only(awq, torch, datagen, dev):
     """A few launches of each hot kernel on cold weights, for counter runs
     (rocprofv3 --pmc serializes every dispatch): on the headline layer the
-    search, the pack, 10 decode launches at M = 1 over 5 rotated copies and
-    2 prefill launches at M = 2048; on the 11008 x 4096 layer 10 launches of
-    the 16-row-block decode kernel at M = 8 over 24 rotated copies."""
+    search, the pack, 10 decode launches at M = 1 and 10 at M = 8 over 5
+    rotated copies, and 2 prefill launches at M = 2048; on the 11008 x 4096
+    layer 10 decode launches at M = 8 over 24 rotated copies (the long-row
+    kernel with its K splits)."""
     w = datagen.WORKLOADS[datagen.HEADLINE]
     W = torch.from_numpy(datagen.weight(w)).to(dev)
     Xc = torch.from_numpy(datagen.calibration(w)).to(dev)
@@ -324,6 +325,9 @@ def kernels_only(awq, torch, datagen, dev):
     X1 = awq.fold_inv_scale(torch.from_numpy(datagen.decode_input(w, 1)).to(dev), s)
     for i in range(10):
         awq.w4a16_matmul(X1, *copies[i % 5], w.bits, w.group)
+    X8 = awq.fold_inv_scale(torch.from_numpy(datagen.decode_input(w, 8)).to(dev), s)
+    for i in range(10):
+        awq.w4a16_matmul(X8, *copies[i % 5], w.bits, w.group)
     Xp = awq.fold_inv_scale(torch.from_numpy(datagen.decode_input(w, 2048)).to(dev), s)
     for i in range(2):
         awq.w4a16_matmul(Xp, *copies[i], w.bits, w.group)
