@@ -178,11 +178,11 @@ size_t awq_w4a16_matmul_workspace_bytes(int M, int N, int K, int bits, int group
 
 /* awq_w4a16_matmul with a workspace (same arithmetic contract). With a
  * split, every split writes its float32 sums over its part of K to its own
- * [M, N] plane of the workspace, and the planes are added in split order
- * (prefill: by a second kernel; int4 decode: by the split that finishes a
- * 16-row block of outputs last, which it learns from that block's counter
- * in the workspace's first 64 KiB), so the result does not depend on
- * timing. workspace: dev, 16-byte aligned, at least
+ * [M, N] plane of the workspace, and the split that finishes an output
+ * tile last (prefill: a tile of up to 128 x 128 outputs; int4 decode: a
+ * 16-row block), which it learns from that tile's counter in the
+ * workspace's first 64 KiB, adds the tile's planes in split order, so the
+ * result does not depend on timing. workspace: dev, 16-byte aligned, at least
  * awq_w4a16_matmul_workspace_bytes(M, N, K, bits, group) bytes, owned by
  * the caller; its first 64 KiB zero-filled before the first call that uses
  * it (every call leaves them zero; the rest may hold anything); calls that

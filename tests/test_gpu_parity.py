@@ -22,6 +22,7 @@ torch = pytest.importorskip("torch")
 import weight_only_bit_w4a16_amd as awq  # noqa: E402
 
 TOL = 1e-3
+CTR_BYTES = 64 << 10  # counter region at the head of a split workspace
 
 
 def dev(a):
@@ -422,8 +423,9 @@ def test_prefill_split_k(bits, M, N, K, group):
     several workgroups per tile, whose float32 sums meet in a workspace
     (ragged M and N, a last split shorter than the others, larger groups and
     one group per row). Checked against the oracle, and repeated bit for bit
-    (the splits are added in a fixed order) on a workspace that held stale
-    values."""
+    (the splits are added in a fixed order) on a workspace whose planes held
+    stale values (its counter region zero, as the contract asks, and left
+    zero by each call)."""
     say("prefill split K", bits, M, N, K, group)
     g = K if group == -1 else group
     W = datagen.random_f16((N, K), 0.02, seed=M + N + bits)
@@ -432,9 +434,13 @@ def test_prefill_split_k(bits, M, N, K, group):
     q, sc, z = _packed(W, s, bits, group)
     nb = awq.matmul_workspace_bytes(M, N, K, bits, group)
     assert nb > 0
+    # stale planes; the counter region at the head is zero before the
+    # first call and must be left zero by it
     ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws[:CTR_BYTES].zero_()
     Y1 = host(awq.w4a16_matmul(dev(X), q, sc, z, bits, group, workspace=ws))
-    ws.fill_(0x5A)
+    assert int(ws[:CTR_BYTES].count_nonzero()) == 0
+    ws[CTR_BYTES:].fill_(0x5A)
     Y2 = host(awq.w4a16_matmul(dev(X), q, sc, z, bits, group, workspace=ws))
     assert_same_bits(Y1, Y2)
     qo, so, zo = O.quantize_pack(W, s, bits, g)

@@ -579,8 +579,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   if constexpr (EPI == 0) {
     if (SK && nsplit > 1) {
       // Split K: this split's float32 products go to plane blockIdx.y of the
-      // workspace ([split][M][N]); split_reduce_kernel adds the planes
-      float* plane = ws + (size_t)blockIdx.y * M * N;
+      // workspace ([split][M][N]), and the split that finishes the tile last
+      // (the tile's counter at the workspace's head says which) adds the
+      // planes in split order and stores Y. The planes are written through
+      // to the device-coherent level (agent-scope stores), the count is
+      // raised once every wavefront's stores have landed, and the last split
+      // reads them at that level. No fence: a device-scope fence writes back
+      // and invalidates the whole L2.
+      const size_t MN = (size_t)M * N;
+      float* plane = ws + (size_t)blockIdx.y * MN;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -591,9 +598,62 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
           for (int v = 0; v < 16; ++v) {
             const int m =
                 m0 + (BM / WGM) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (m < M && n < nend) plane[(size_t)m * N + n] = acc[i][j][v] * post;
+            if (m < M && n < nend) {
+              __hip_atomic_store(plane + (size_t)m * N + n, acc[i][j][v] * post,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
+      {
+        __builtin_amdgcn_s_waitcnt(0);  // this wavefront's plane stores are complete
+        __syncthreads();                // and every wavefront's
+        __shared__ uint32_t last_split;
+        if (tid == 0) {
+          uint32_t* ctr =
+              reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) - kSplitCtrBytes) + t;
+          const uint32_t old =
+              __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last_split = old == (uint32_t)(nsplit - 1) ? 1u : 0u;
+          // every split has counted: ready for the next call
+          if (last_split) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (last_split == 0u) return;
+        // the tile's outputs in a coalesced layout (thread -> column
+        // tid % BN, rows RS apart; the row offset is the same for a whole
+        // wavefront, so the addresses are a scalar base plus the column),
+        // CH rows at a time, each split's loads in flight together, added
+        // in split order; this split's own plane is read back like the others
+        constexpr int NT = 64 * WGM * WGN;
+        static_assert(BN % 64 == 0 && NT % BN == 0, "whole wavefronts per row");
+        constexpr int RS = NT / BN;
+        constexpr int RPT = BM / RS;
+        constexpr int CH = RPT < 32 ? RPT : 32;
+        const int rw = __builtin_amdgcn_readfirstlane(tid / BN);
+        const int c = tid % BN;
+        const unsigned cc = (unsigned)min(c, nend - 1 - n0);  // in the row
+        for (int k0 = 0; k0 < RPT; k0 += CH) {
+          float sum[CH];
+          for (int sp = 0; sp < nsplit; ++sp) {
+            float x[CH];
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+              const int m = min(m0 + rw + RS * (k0 + k), M - 1);
+              const float* base = ws + (size_t)sp * MN + (size_t)m * N + n0;
+              x[k] = __hip_atomic_load(base + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int k = 0; k < CH; ++k) sum[k] = sp == 0 ? x[k] : sum[k] + x[k];
+          }
+          if (n0 + c < nend) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+              const int m = m0 + rw + RS * (k0 + k);
+              if (m < M) Y[(size_t)m * N + n0 + c] = __half_as_ushort(__float2half_rn(sum[k]));
+            }
+          }
+        }
+      }
       return;
     }
 #pragma unroll
@@ -681,7 +741,11 @@ namespace {
 // wide: a tile re-reads its activation rows for every 128 outputs instead of
 // every 64, and no rows past M are loaded and multiplied for nothing. Each
 // split writes its float32 products to its own [M, N] plane of the
-// workspace, and a second kernel adds the planes in split order.
+// workspace, and the split that finishes a tile last (a counter per tile at
+// the workspace's head) adds the tile's planes in split order. Against a
+// separate adding kernel (rocprofv3, weights in HBM): 4096x4096 M = 17 13.5
+// -> 9.5 us, M = 64 17.8 -> 11.8, 4096x11008 M = 17 22.5 -> 18.0, M = 128
+// 31.8 -> 29.3, int3 4096x4096 M = 32 21.3 -> 16.6.
 struct GemmPlan {
   int bm, bn;    // tile
   int splits;    // K splits (1: none)
@@ -719,20 +783,12 @@ GemmPlan gemm_plan(int M, int N, int K, int bits, bool can_split) {
   return p;
 }
 
-// planes after the counter region (which this kernel leaves alone)
+// planes after the counter region
 size_t plan_workspace_bytes(const GemmPlan& p, int M, int N) {
   return p.splits <= 1 ? 0 : kSplitCtrBytes + (size_t)p.splits * M * N * 4;
 }
 
-// Y = fp16(sum of the split planes), added in split order
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws, int S,
-                                                           size_t MN, uint16_t* __restrict__ Y) {
-  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= MN) return;
-  float sum = ws[e];
-  for (int sp = 1; sp < S; ++sp) sum += ws[(size_t)sp * MN + e];
-  Y[e] = __half_as_ushort(__float2half_rn(sum));
-}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int M, int N, int K, int bits) {
@@ -756,21 +812,24 @@ hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales,
                    ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCtrBytes)
                    : nullptr;
   const unsigned nsp = (unsigned)plan.splits;
-#define AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, NB, NE, SKV)                                   \
+#define AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, NB, NE, SKV)                                  \
   do {                                                                                          \
     const dim3 grid(tiles_of(M, (NE) - (NB), BM, BN), nsp);                                     \
     if (zw)                                                                                     \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST, CS, SKV>), grid,   \
-                         dim3(64 * WGM * WGN), 0, st, x, q, scales, zeros, M, N, K, wpr, gshift, \
-                         y, nullptr, 0, nullptr, nullptr, nullptr, NB, NE, wsf, plan.spl);      \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, true, NST, CS, SKV>),         \
+                         grid, dim3(64 * WGM * WGN), 0, st, x, q, scales, zeros, M, N, K, wpr,  \
+                         gshift, y, nullptr, 0, nullptr, nullptr, nullptr, NB, NE, wsf,         \
+                         plan.spl);                                                             \
     else                                                                                        \
-      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST, CS, SKV>), grid,  \
-                         dim3(64 * WGM * WGN), 0, st, x, q, scales, zeros, M, N, K, wpr, gshift, \
-                         y, nullptr, 0, nullptr, nullptr, nullptr, NB, NE, wsf, plan.spl);      \
+      hipLaunchKernelGGL((gemm_kernel<BMODE, 0, BM, BN, WGM, WGN, false, NST, CS, SKV>),        \
+                         grid, dim3(64 * WGM * WGN), 0, st, x, q, scales, zeros, M, N, K, wpr,  \
+                         gshift, y, nullptr, 0, nullptr, nullptr, nullptr, NB, NE, wsf,         \
+                         plan.spl);                                                             \
   } while (0)
 #define AWQ_GEMM(BMODE, BM, BN, WGM, WGN, NST, NB, NE) \
   AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, NB, NE, false)
-#define AWQ_GEMM_S(BMODE, BM, BN, WGM, WGN, NST) AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, 0, N, true)
+#define AWQ_GEMM_S(BMODE, BM, BN, WGM, WGN, NST) \
+  AWQ_GEMM_K(BMODE, BM, BN, WGM, WGN, NST, 0, N, true)
   if (plan.splits > 1) {
     // split K: int4 32 x 128 (4 wavefronts of 32 x 32), 64 x 128 (2 x 2 of
     // 32 x 64) or 128 x 128 tiles
@@ -784,9 +843,6 @@ hipError_t launch_gemm_t(const __half* X, const uint32_t* q, const void* scales,
       if (plan.bm == 128) AWQ_GEMM_S(3, 128, 128, 4, 2, 4);
       else AWQ_GEMM_S(3, 64, 128, 2, 4, 4);
     }
-    const size_t mn = (size_t)M * N;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st,
-                       wsf, plan.splits, mn, y);
   } else if (bits == 4) {
     if (plan.bm == 256) {
       // Whole rounds of 256 x 256 tiles (one per compute unit each), and the
