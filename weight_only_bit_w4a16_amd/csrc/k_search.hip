@@ -112,6 +112,83 @@ __global__ __launch_bounds__(256) void fake_quant_error_kernel(const uint16_t* _
   }
 }
 
+// The scaled form for NA candidate scales in one pass over W: E_a =
+// fp16(2^8 (W s_a - (q - z) delta)) for s_a = s + a K, written to E + a N K.
+// The codes and the bits of E_a are those of fake_quant_error_kernel (same
+// group grid, same rounding, same operation order); W is read once for the
+// NA candidates instead of once each. The tie test takes the exact division
+// when t = wp / delta (approximated) lies within 2^-16 of a half-integer,
+// written as |t - rint(t)| > 1/2 - 2^-16.
+template <int BITS, int TPG, bool SYM, int NA>
+__global__ __launch_bounds__(256) void fake_quant_error_multi_kernel(
+    const uint16_t* __restrict__ W, const float* __restrict__ s, int N, int K,
+    uint16_t* __restrict__ E) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  const int tr = blockIdx.x * 256 + threadIdx.x;
+  const bool active = tr < K / 8;
+  const int tt = active ? tr : K / 8 - TPG + (tr % TPG);
+  const int k0 = 8 * tt;
+  float sv[NA][8];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const float4 s0 = *reinterpret_cast<const float4*>(s + (size_t)a * K + k0);
+    const float4 s1 = *reinterpret_cast<const float4*>(s + (size_t)a * K + k0 + 4);
+    sv[a][0] = s0.x; sv[a][1] = s0.y; sv[a][2] = s0.z; sv[a][3] = s0.w;
+    sv[a][4] = s1.x; sv[a][5] = s1.y; sv[a][6] = s1.z; sv[a][7] = s1.w;
+  }
+  const size_t NK = (size_t)N * K;
+  uint4 raw = *reinterpret_cast<const uint4*>(W + (size_t)blockIdx.y * K + k0);
+  for (int nr = blockIdx.y; nr < N; nr += gridDim.y) {
+    const size_t n = (size_t)nr;
+    const int nx = min(nr + (int)gridDim.y, N - 1);
+    const uint4 next = *reinterpret_cast<const uint4*>(W + (size_t)nx * K + k0);
+    const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    raw = next;
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = h2f((uint16_t)(i & 1 ? rw[i >> 1] >> 16 : rw[i >> 1] & 0xffffu));
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      float wp[8];
+      float mn, mx;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        wp[i] = w[i] * sv[a][i];
+        mn = i == 0 ? wp[i] : fminf(mn, wp[i]);
+        mx = i == 0 ? wp[i] : fmaxf(mx, wp[i]);
+      }
+#pragma unroll
+      for (int off = 1; off < TPG; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, TPG));
+        mx = fmaxf(mx, __shfl_xor(mx, off, TPG));
+      }
+      const GroupGrid gg = grid_of<SYM, BITS>(mn, mx);
+      const float zf = (float)gg.z;
+      uint32_t hv[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t h[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 2 * p + e;
+          const float t = wp[i] * gg.rdelta;
+          float qf = rintf(t);
+          if (__builtin_fabsf(t - qf) > 0.5f - 0x1p-16f) qf = rintf(wp[i] / gg.delta);
+          // clamp(q, 0, QMAX) - z with q = qf + z
+          const float qc = __builtin_amdgcn_fmed3f(qf, -zf, (float)QMAX - zf);
+          const float back = qc * gg.delta;
+          h[e] = __half_as_ushort(__float2half_rn((wp[i] - back) * 256.0f));
+        }
+        hv[p] = h[0] | (h[1] << 16);
+      }
+      if (active)
+        *reinterpret_cast<uint4*>(E + (size_t)a * NK + n * K + k0) =
+            make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    }
+  }
+}
+
 // The same for per-output-channel groups (the whole row): one workgroup of
 // 512 threads per row, the row in registers between the row-wide min / max
 // and the error terms (chunk c of thread t: codes 8 (t + 512 c) .. + 7).
@@ -232,7 +309,7 @@ Layout layout(int maxN, int K, int T, int n_alpha, unsigned max_tiles, int n_lay
   L.s_all = L.m + align256((size_t)K * 8);
   L.xs = L.s_all + align256((size_t)n_alpha * K * 4);
   L.e = L.xs + align256((size_t)T * K * 2);
-  L.partial = L.e + align256((size_t)maxN * K * 4);  // E [N, K] or hi/lo D [N, 2K]
+  L.partial = L.e + align256((size_t)maxN * K * 4);  // two E planes [2][N, K] or hi/lo D [N, 2K]
   L.lloss = L.partial + align256((size_t)n_alpha * max_tiles * 8);
   L.total = L.lloss + (n_layers > 1 ? align256((size_t)n_layers * n_alpha * 8) : 0);
   return L;
@@ -251,6 +328,51 @@ hipError_t layer_losses(const __half* W, const __half* Xc, int N, int K, int T,
   // 1/sqrt(T N); from 2^18 on it stays below about 1.2e-5
   const bool scaled = (long long)T * N >= (1LL << 18);
   hipError_t e;
+  if (scaled && !row_group(group)) {
+    // candidates in pairs: one pass over W writes both error terms (E holds
+    // two [N, K] fp16 planes), then the fold and the contraction of each
+    for (int a = 0; a < n_alpha; a += 2) {
+      const int na = min(2, n_alpha - a);
+      const float* s = s_all + (size_t)a * K;
+#define AWQ_FM(B, TP, SY, NA)                                                              \
+  hipLaunchKernelGGL((fake_quant_error_multi_kernel<B, TP, SY, NA>), fgrid, dim3(256), 0, st, \
+                     w, s, N, K, E)
+#define AWQ_FM2(B, TP)                         \
+  do {                                         \
+    if (na == 2 && zero_point)                 \
+      AWQ_FM(B, TP, false, 2);                 \
+    else if (na == 2)                          \
+      AWQ_FM(B, TP, true, 2);                  \
+    else if (zero_point)                       \
+      AWQ_FM(B, TP, false, 1);                 \
+    else                                       \
+      AWQ_FM(B, TP, true, 1);                  \
+  } while (0)
+      if (bits == 4) {
+        if (group == 128) AWQ_FM2(4, 16);
+        else if (group == 256) AWQ_FM2(4, 32);
+        else AWQ_FM2(4, 64);
+      } else {
+        if (group == 128) AWQ_FM2(3, 16);
+        else if (group == 256) AWQ_FM2(3, 32);
+        else AWQ_FM2(3, 64);
+      }
+#undef AWQ_FM2
+#undef AWQ_FM
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      for (int b = 0; b < na; ++b) {
+        e = launch_fold(Xc, s_all + (size_t)(a + b) * K, T, K, reinterpret_cast<__half*>(Xs), st);
+        if (e != hipSuccess) return e;
+        e = launch_sqnorm_abt(Xs, E + (size_t)b * N * K, T, N, K, false,
+                              partial + (size_t)(a + b) * tiles, st);
+        if (e != hipSuccess) return e;
+      }
+    }
+    hipLaunchKernelGGL(reduce_loss_kernel, dim3(n_alpha), dim3(256), 0, st, partial, (int)tiles,
+                       1.0 / 65536.0, loss);
+    return hipGetLastError();
+  }
   for (int a = 0; a < n_alpha; ++a) {
     const float* s = s_all + (size_t)a * K;
 #define AWQ_FQ(B, TP, SC, SY)                                                                  \
