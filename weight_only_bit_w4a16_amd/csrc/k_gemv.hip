@@ -335,6 +335,32 @@ int cu_count() {
 }  // namespace
 
 
+// Rows of the streaming decode kernels (one row per wavefront at a time).
+// The dispatcher deals workgroup b to XCD b % 8. When the grid is a multiple
+// of 8, XCD x takes the contiguous rows [x N / 8, (x + 1) N / 8) and its
+// wavefronts interleave over them, so each XCD's L2 and address translation
+// see one eighth of the matrix; otherwise (or if some wavefront would get
+// more than 64 rows, or by_xcd is off) every wavefront interleaves over all
+// N rows. A wavefront's rows are first, first + stride, ... (count of them,
+// <= 64). Kernel traces (old and new mapping in one process): 8192x28672
+// M = 1 25.3 -> 24.2 us, int3 4096x11008 M = 1 8.0 -> 7.8 and M = 2 9.6 ->
+// 9.2, the others within 1%; the int4 few-token kernel keeps the plain
+// mapping (8192x28672 M = 2 28.8 -> 31.5 us with it).
+struct RowMap {
+  int first, stride, count;
+};
+__device__ __forceinline__ RowMap row_map(int N, int per_wg, int idx, bool by_xcd = true) {
+  const int G = gridDim.x;
+  int first = blockIdx.x * per_wg + idx, stride = G * per_wg, end = N;
+  if (by_xcd && (G & 7) == 0 && ((N + 7) >> 3) <= 64 * (G >> 3) * per_wg) {
+    const int xc = blockIdx.x & 7;
+    stride = (G >> 3) * per_wg;
+    first = (int)(((long long)N * xc) >> 3) + (blockIdx.x >> 3) * per_wg + idx;
+    end = (int)(((long long)N * (xc + 1)) >> 3);
+  }
+  return RowMap{first, stride, first < end ? (end - 1 - first) / stride + 1 : 0};
+}
+
 // ---------------------------------------------------------------------------
 // M = 1: one row per wavefront at a time, read as contiguous 1 KB pieces.
 //
@@ -383,14 +409,15 @@ __global__ __launch_bounds__(256) void gemv_w4_m1_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int seg = SEG > 1 ? wave % SEG : 0;  // pieces seg*SP .. seg*SP + SP - 1
-  const int gw = blockIdx.x * (4 / SEG) + wave / SEG;
-  const int NW = gridDim.x * (4 / SEG);
+  const RowMap rm = row_map(N, 4 / SEG, wave / SEG);
+  const int gw = rm.first;  // rows gw, gw + NW, ... of this wavefront
+  const int NW = rm.stride;
   const int j = lane & 15;
   const int jj = lane >> 4;
   const int nch = K >> 7;  // groups of 128 codes per row; NP = ceil(nch / 16)
   const int ngr = max(1, nch >> gshift);
   const int wpr = K >> 3;
-  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int cnt = rm.count;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
   const bool diag = jj == (j >> 2);
 
@@ -611,14 +638,15 @@ __global__ __launch_bounds__(256) void gemv_w4_mt_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int seg = SEG > 1 ? wave % SEG : 0;  // pieces seg*SP .. seg*SP + SP - 1
-  const int gw = blockIdx.x * (4 / SEG) + wave / SEG;
-  const int NW = gridDim.x * (4 / SEG);
+  const RowMap rm = row_map(N, 4 / SEG, wave / SEG, false);
+  const int gw = rm.first;  // rows gw, gw + NW, ... of this wavefront
+  const int NW = rm.stride;
   const int j = lane & 15;
   const int jj = lane >> 4;
   const int nch = K >> 7;
   const int ngr = max(1, nch >> gshift);
   const int wpr = K >> 3;
-  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int cnt = rm.count;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
   const bool diag = jj == (j >> 2);
 
@@ -845,13 +873,14 @@ __global__ __launch_bounds__(256) void gemv_w3_m1_kernel(
   __shared__ float2 xcs[SP][16];   // (C, S) of group 16*piece + j
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * 4 + wave;
-  const int NW = gridDim.x * 4;
+  const RowMap rm = row_map(N, 4, wave);
+  const int gw = rm.first;  // rows gw, gw + NW, ... of this wavefront
+  const int NW = rm.stride;
   const int j = lane & 15;
   const int jj = lane >> 4;
   const int nch = K >> 7;  // 128-code blocks per row; SP = ceil(nch / 16)
   const int ngr = max(1, nch >> gshift);  // groups per row
-  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int cnt = rm.count;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
   const bool diag = jj == (j >> 2);
   const int woff = w3_first_word(jj);
@@ -1109,13 +1138,14 @@ __global__ __launch_bounds__(256) void gemv_w3_mt_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int seg = SEG > 1 ? wave % SEG : 0;
-  const int gw = blockIdx.x * (4 / SEG) + wave / SEG;
-  const int NW = gridDim.x * (4 / SEG);
+  const RowMap rm = row_map(N, 4 / SEG, wave / SEG);
+  const int gw = rm.first;  // rows gw, gw + NW, ... of this wavefront
+  const int NW = rm.stride;
   const int j = lane & 15;
   const int jj = lane >> 4;
   const int nch = K >> 7;
   const int ngr = max(1, nch >> gshift);
-  const int cnt = gw < N ? (N - 1 - gw) / NW + 1 : 0;  // rows of this wavefront (<= 64)
+  const int cnt = rm.count;  // rows of this wavefront (<= 64)
   const int rdiag = j & 3;
   const bool diag = jj == (j >> 2);
   const int woff = w3_first_word(jj);
