@@ -14,7 +14,10 @@ max_n |Y - Y*| <= 1e-3 * max_n |Y*|).
 - groups of 256 and 512 codes and one group per row;
 - the same shape without a workspace (the multi-pass kernel) and with one,
   and two calls with one workspace giving the same bits (the first call
-  leaves the workspace's counters zero for the second).
+  leaves the workspace's counters zero for the second);
+- both weight-load forms: rows of 28672 codes on 8192 rows (the full-line
+  form's staging would add K splits there, so the plan keeps the 16-row
+  loads) and the shapes above (full-line loads through LDS).
 """
 import ctypes
 import sys
@@ -159,3 +162,15 @@ def test_mb_with_and_without_workspace():
     assert np.array_equal(out[0].view(np.uint16), out[1].view(np.uint16))
     check(W, X, None, 128, out[0])
     check(W, X, None, 128, out[2])
+
+
+def test_mb_long_rows_plain_loads():
+    """28672 codes per row, 8192 rows, M = 8: the plan keeps the 16-row
+    loads here (sampled rows against the oracle)."""
+    N, K, M = 8192, 28672, 8
+    say("mb long rows", M, N, K)
+    W = datagen.random_f16((N, K), 0.02, seed=31)
+    X = datagen.random_f16((M, K), 1.0, seed=32)
+    q, sc, z = packed(W, None, 128)
+    Y = host(awq.w4a16_matmul(dev(X), q, sc, z))
+    check(W, X, None, 128, Y, rows_of(N, seed=3, count=120))

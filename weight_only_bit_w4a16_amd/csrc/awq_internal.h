@@ -63,10 +63,12 @@ hipError_t launch_gemv_w4(const __half* X, const uint32_t* q, const void* scales
 size_t gemv_workspace_bytes(int M, int N, int K);
 // decode, int4, 2 <= M <= 16 on 16-row blocks with the activations in LDS
 // (gemv_w4_mb_kernel): token rows stored (8 or 16), K splits, chunks of 128
-// codes per split, workgroups per split, LDS bytes, workspace bytes. splits
-// is 0 when the shape needs a split and can_split is false.
+// codes per split, workgroups per split, full-line weight loads, LDS bytes,
+// workspace bytes. splits is 0 when the shape needs a split and can_split is
+// false.
 struct MbPlan {
   int mp, splits, spl, gx;
+  bool fl;
   size_t lds, ws_bytes;
 };
 MbPlan mb_plan(int M, int N, int K, bool can_split);

@@ -30,6 +30,16 @@
 // last (a counter per row block at the workspace's head) adds the planes
 // in split order, so the result does not depend on which split is last;
 // with S = 1 the wavefront stores fp16 directly.
+//
+// Full-line weight loads (FL). The MFMA layout puts 16 rows in every 16
+// lanes, so a load in that layout fetches 16 rows x 64 B. With FL a
+// wavefront instead loads a chunk pair of its 16 rows as two 8 rows x
+// 128 B loads (lane i: bytes 16 (i % 8) of the 128-byte span of row i / 8),
+// writes them to its own 2 KB of LDS, at 16-byte slot 8 n + (u ^ (n % 8))
+// for row n and part u (both the write and the read below meet no bank
+// conflict), and reads each chunk back in the MFMA layout (row nl, part
+// 4 c + q). The plan takes FL when the staging buffers leave the split
+// count unchanged.
 #include "awq_internal.h"
 #include "device_common.h"
 
@@ -69,25 +79,29 @@ constexpr int kMbMaxSpl = 40;
 // of zeros (16 MP operands of 16 bytes per chunk), then per wavefront its
 // row block's group parameters per chunk: float32 steps [16][pst] and uint8
 // zero points [16][pst], pst = spl rounded up to odd (the 16 rows of a
-// chunk fall in distinct banks)
+// chunk fall in distinct banks), and with full-line loads (fl) a 2 KB
+// staging buffer for a chunk pair of its 16 rows
 struct MbLds {
-  uint32_t a_bytes, pst, wave_bytes, total;
+  uint32_t a_bytes, pst, par_bytes, wave_bytes, total;
 };
-__host__ __device__ constexpr MbLds mb_lds(int spl, int mp) {
+constexpr uint32_t kMbStage = 2048;
+__host__ __device__ constexpr MbLds mb_lds(int spl, int mp, bool fl) {
   const uint32_t a = (uint32_t)(spl + 1) * 16u * (uint32_t)mp * 16u;
   const uint32_t pst = (uint32_t)spl | 1u;
-  const uint32_t wb = (16u * pst * 5u + 15u) & ~15u;
-  return MbLds{a, pst, wb, a + (uint32_t)kMbWaves * wb};
+  const uint32_t pb = (16u * pst * 5u + 15u) & ~15u;
+  const uint32_t wb = pb + (fl ? kMbStage : 0u);
+  return MbLds{a, pst, pb, wb, a + (uint32_t)kMbWaves * wb};
 }
 
 }  // namespace
 
 // Plain group parameters (float32 steps, uint8 zero points, [N][ng] each).
 // MP: token rows stored in LDS (8 or 16). PL: write float32 planes (S > 1)
-// instead of fp16 Y. LDS layout: mb_lds; the operands are
+// instead of fp16 Y. FL: full-line weight loads. LDS layout: mb_lds; the
+// operands are
 // [chunk][mfma j][q][m < MP].
 // (4 wavefronts per SIMD: two workgroups per compute unit, 128 registers)
-template <int MP, bool PL>
+template <int MP, bool PL, bool FL>
 __global__ __launch_bounds__(64 * kMbWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 gemv_w4_mb_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ Q, const void* __restrict__ S,
@@ -109,10 +123,13 @@ gemv_w4_mb_kernel(
   const int gw = blockIdx.x * kMbWaves + wave;  // wavefront among the split's
   const int GW = gridDim.x * kMbWaves;
   const int nrw = gw < nrb ? (nrb - 1 - gw) / GW + 1 : 0;  // row blocks of this wavefront
-  const MbLds lay = mb_lds(spl, MP);
+  const MbLds lay = mb_lds(spl, MP, FL);
   char* const lds = reinterpret_cast<char*>(a_lds);
   float* const p_step = reinterpret_cast<float*>(lds + lay.a_bytes + wave * lay.wave_bytes);
   uint8_t* const p_zero = reinterpret_cast<uint8_t*>(p_step + 16 * lay.pst);
+  // FL staging (16-byte aligned: the operand and parameter blocks are)
+  u32x4* const p_stage =
+      reinterpret_cast<u32x4*>(lds + lay.a_bytes + wave * lay.wave_bytes + lay.par_bytes);
 
   const int nop = ncw * kChunkOps;
 
@@ -124,6 +141,10 @@ gemv_w4_mb_kernel(
   const char* srow = nullptr;
   const char* zrow = nullptr;
   uint32_t qoff = 0;  // this lane's offset from qrow
+  // FL: this lane's row (i / 8 and 8 + i / 8) and 16-byte part of a
+  // 128-byte span, and the two rows' offsets from qrow
+  const int fr = lane >> 3, fu = lane & 7;
+  uint32_t foff[2] = {0u, 0u};
   uint32_t prow = 0;  // this lane's row within the block (rows past N repeat row N - 1)
   // parameter loads: lane (nl, q) takes row nl, chunks q, q + 4, ... (a
   // load past the split's last chunk reads a later chunk of the row, or
@@ -138,6 +159,11 @@ gemv_w4_mb_kernel(
     srow = static_cast<const char*>(S) + (size_t)rb * 16 * ngr * 4;
     zrow = static_cast<const char*>(Z) + (size_t)rb * 16 * ngr;
     qoff = prow * rowq + 16u * q;
+    if constexpr (FL) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        foff[h] = (uint32_t)min(8 * h + fr, N - 1 - rb * 16) * rowq + 16u * (uint32_t)(fu & 3);
+    }
 #pragma unroll
     for (int i = 0; i < kPar; ++i) {
       if (4 * i < ncw) {  // uniform
@@ -156,9 +182,21 @@ gemv_w4_mb_kernel(
       }
     }
   };
+  // slot r <- chunk t; FL: slots r, r + 1 (r even) <- the chunk pair
+  // (t, t + 1) of rows 0-7 and 8-15 (a second chunk past the split's last
+  // reads the last one again)
   auto load_w = [&](int r, int t) {
-    const int c = c0 + min(t, ncw - 1);
-    wr[r] = ld_nt(reinterpret_cast<const u32x4*>(qrow + (size_t)c * 64 + qoff));
+    if constexpr (FL) {
+      if ((r & 1) == 0) {
+        const int c = c0 + min(t + (fu >> 2), ncw - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          wr[r + h] = ld_nt(reinterpret_cast<const u32x4*>(qrow + (size_t)c * 64 + foff[h]));
+      }
+    } else {
+      const int c = c0 + min(t, ncw - 1);
+      wr[r] = ld_nt(reinterpret_cast<const u32x4*>(qrow + (size_t)c * 64 + qoff));
+    }
   };
   auto prologue = [&]() {
 #pragma unroll
@@ -241,10 +279,23 @@ gemv_w4_mb_kernel(
         const h2 zo = hv((0xD400u + 16u * z) * 0x00010001u);  // -(64 + z)
         const u32x4* ap = reinterpret_cast<const u32x4*>(lds + abase + (uint32_t)min(t, ncw) *
                                                                            (kChunkOps * 16u));
+        u32x4 wv;
+        if constexpr (FL) {
+          // the pair through LDS: stored, its slots refilled, and this
+          // item's 16 bytes read back in the MFMA layout
+          if ((r & 1) == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) p_stage[8 * (8 * h + fr) + (fu ^ fr)] = wr[r + h];
+            load_w(r, t + kMbRing);
+          }
+          wv = p_stage[8 * nl + ((4 * (r & 1) + q) ^ (nl & 7))];
+        } else {
+          wv = wr[r];
+        }
         u32x4 b[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t x = wr[r][j], x8 = x >> 8;
+          const uint32_t x = wv[j], x8 = x >> 8;
           b[j] = u32x4{
               hbits(hv(and_or(x, ur.lo4, ur.magic)) + ze),
               hbits(__builtin_elementwise_fma(hv(and_or(x, ur.hi4, ur.magic)), sixteenth, zo)),
@@ -255,7 +306,7 @@ gemv_w4_mb_kernel(
         // (issued here, item by item: the scheduler would otherwise gather
         // the round's loads at its end, where the next round's first item
         // waits for them at once)
-        load_w(r, t + kMbRing);
+        if constexpr (!FL) load_w(r, t + kMbRing);
         floatx4 s = zero4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) s = mfma16(ap[j * 4 * MP], b[j], s);
@@ -347,11 +398,11 @@ constexpr uint32_t kMbLdsMax = 80 * 1024;
 // wavefronts the plan aims for per compute unit
 constexpr int kMbWavesPerCu = 8;
 
-template <int MP, bool PL>
+template <int MP, bool PL, bool FL>
 hipError_t mb_allow_lds(size_t lds) {
   static size_t allowed = 64 * 1024;
   if (lds <= allowed) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute((const void*)gemv_w4_mb_kernel<MP, PL>,
+  const hipError_t e = hipFuncSetAttribute((const void*)gemv_w4_mb_kernel<MP, PL, FL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e == hipSuccess) allowed = lds;
   return e;
@@ -369,19 +420,27 @@ MbPlan mb_plan(int M, int N, int K, bool can_split) {
   const int nrb = (N + 15) / 16;
   const int waves = kMbWavesPerCu * mb_cu_count();
   // chunks per split: what the LDS and the staging registers hold
-  int spl_max = kMbMaxSpl;
-  while (spl_max > 1 && mb_lds(spl_max, mp).total > kMbLdsMax) --spl_max;
-  int s = (nch + spl_max - 1) / spl_max;
-  if (can_split) s = max(s, min((waves + nrb - 1) / nrb, max(1, nch / 2)));
+  auto splits_of = [&](bool fl) {
+    int spl_max = kMbMaxSpl;
+    while (spl_max > 1 && mb_lds(spl_max, mp, fl).total > kMbLdsMax) --spl_max;
+    int s = (nch + spl_max - 1) / spl_max;
+    if (can_split) s = max(s, min((waves + nrb - 1) / nrb, max(1, nch / 2)));
+    const int spl = (nch + s - 1) / s;
+    return (nch + spl - 1) / spl;
+  };
+  int s = splits_of(false);
   const int spl = (nch + s - 1) / s;
   s = (nch + spl - 1) / spl;
+  // full-line loads when their staging leaves the splits as they are
+  const bool fl = splits_of(true) == s && mb_lds(spl, mp, true).total <= kMbLdsMax;
   if (s > 1 && (!can_split || nrb > kSplitMaxRowBlocks)) return p;  // splits == 0: not supported
   const int rbw = max(1, (nrb * s) / waves);
   p.mp = mp;
   p.splits = s;
   p.spl = spl;
   p.gx = (nrb + kMbWaves * rbw - 1) / (kMbWaves * rbw);
-  p.lds = mb_lds(spl, mp).total;
+  p.fl = fl;
+  p.lds = mb_lds(spl, mp, fl).total;
   p.ws_bytes = s > 1 ? kSplitCtrBytes + (size_t)s * M * N * 4 : 0;
   return p;
 }
@@ -414,20 +473,26 @@ hipError_t launch_gemv_w4_mb(const __half* X, const uint32_t* q, const void* sca
                   ? reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCtrBytes)
                   : nullptr;
   const dim3 grid((unsigned)p.gx, (unsigned)p.splits), block(64 * kMbWaves);
-#define AWQ_MB(MPV, PLV)                                                                      \
-  do {                                                                                        \
-    const hipError_t ea = mb_allow_lds<MPV, PLV>(p.lds);                                      \
-    if (ea != hipSuccess) return ea;                                                          \
-    hipLaunchKernelGGL((gemv_w4_mb_kernel<MPV, PLV>), grid, block, p.lds, st, x, q, scales,    \
-                       zeros, y, pl, ctr, M, N, K, gshift, p.spl);                            \
+#define AWQ_MB(MPV, PLV, FLV)                                                                  \
+  do {                                                                                          \
+    const hipError_t ea = mb_allow_lds<MPV, PLV, FLV>(p.lds);                                   \
+    if (ea != hipSuccess) return ea;                                                            \
+    hipLaunchKernelGGL((gemv_w4_mb_kernel<MPV, PLV, FLV>), grid, block, p.lds, st, x, q, scales, \
+                       zeros, y, pl, ctr, M, N, K, gshift, p.spl);                              \
+  } while (0)
+#define AWQ_MB2(MPV, PLV)                   \
+  do {                                      \
+    if (p.fl) AWQ_MB(MPV, PLV, true);       \
+    else AWQ_MB(MPV, PLV, false);           \
   } while (0)
   if (p.mp == 8) {
-    if (pl) AWQ_MB(8, true);
-    else AWQ_MB(8, false);
+    if (pl) AWQ_MB2(8, true);
+    else AWQ_MB2(8, false);
   } else {
-    if (pl) AWQ_MB(16, true);
-    else AWQ_MB(16, false);
+    if (pl) AWQ_MB2(16, true);
+    else AWQ_MB2(16, false);
   }
+#undef AWQ_MB2
 #undef AWQ_MB
   return hipGetLastError();
 }
