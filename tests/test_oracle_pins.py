@@ -334,6 +334,24 @@ def test_matmul_exact_rationals(bits, K, N, M):
     assert O.matmul(e, qp, sc, z, bits, 128, K)[0, 0] == (codes0[5] - int(z[0, 0])) * float(sc[0, 0])
 
 
+def test_matmul_rows_selects_output_channels():
+    """Row r of the weights holds the code r mod 16 everywhere (step 1,
+    zero point 0), so column r of Y is (r mod 16) times the row sum of X:
+    matmul_rows must return those columns in the order asked for."""
+    N, K, M = 20, 128, 3
+    q = (np.arange(N)[:, None] % 16) * np.ones((1, K), dtype=np.int64)
+    qp = O.pack(q, 4, 128)
+    sc = np.ones((N, 1), np.float32)
+    z = np.zeros((N, 1), np.uint8)
+    X = datagen.random_f16((M, K), 1.0, seed=40)
+    rowsum = X.astype(np.float64).sum(axis=1)
+    rows = [17, 2, 9, 2]
+    Y = O.matmul_rows(X, qp, sc, z, 4, 128, K, rows)
+    assert Y.shape == (M, len(rows))
+    for i, r in enumerate(rows):
+        assert np.allclose(Y[:, i], (r % 16) * rowsum, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # P10: textbook per-channel affine fake quantization
 # ---------------------------------------------------------------------------
