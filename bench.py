@@ -348,7 +348,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this hot path runs on one GPU; --gpus must be 1 "
-              "(multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+              "(a sharded multi-GPU run is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
