@@ -342,10 +342,11 @@ int cu_count() {
 // see one eighth of the matrix; otherwise (or if some wavefront would get
 // more than 64 rows, or by_xcd is off) every wavefront interleaves over all
 // N rows. A wavefront's rows are first, first + stride, ... (count of them,
-// <= 64). Kernel traces (old and new mapping in one process): 8192x28672
-// M = 1 25.3 -> 24.2 us, int3 4096x11008 M = 1 8.0 -> 7.8 and M = 2 9.6 ->
-// 9.2, the others within 1%; the int4 few-token kernel keeps the plain
-// mapping (8192x28672 M = 2 28.8 -> 31.5 us with it).
+// <= 64). Kernel traces (old and new mapping in one process, three boxes):
+// 8192x28672 M = 1 22.1 -> 21.8, 25.3 -> 24.2 and 23.6 -> 23.8 us; int3
+// 4096x11008 M = 2 9.6 -> 9.2-9.4; the others within 2%. The int4
+// few-token kernel keeps the plain mapping (8192x28672 M = 2 28.8 -> 31.5
+// us with it).
 struct RowMap {
   int first, stride, count;
 };
