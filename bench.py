@@ -282,10 +282,17 @@ def config_table(awq, torch, datagen, dev, stream):
             torch.cuda.synchronize()
             us = float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3 / (passes * R)
             del g
-            byt = packed + 2 * M * w.K + 2 * M * w.N
+            # algorithmic bytes: codes at 10 per 32-bit word for int3
+            # (rows of ceil(K / 10) words rounded up to 4), 8 per word for
+            # int4; the stored int3 rows keep every 128-code block on a word
+            # boundary (13 words per block), about 1% more
+            wpr_alg = w.K // 8 if w.bits == 4 else -(-(-(-w.K // 10)) // 4) * 4
+            byt = w.N * wpr_alg * 4 + sc.numel() * 5 + 2 * M * w.K + 2 * M * w.N
             fl = 2.0 * M * w.N * w.K
             row = {"workload": w.name, "M": M, "us": round(us, 2),
                    "GB/s": round(byt / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 1)}
+            if w.bits == 3:
+                row["stored_bytes"] = packed + 2 * M * w.K + 2 * M * w.N
             if M in w.decode_M:
                 row["hbm_frac"] = round(byt / us / 1e3 / HBM_PEAK_GBS, 4)
             else:
