@@ -17,7 +17,8 @@ max_n |Y - Y*| <= 1e-3 * max_n |Y*|).
   leaves the workspace's counters zero for the second);
 - both weight-load forms: rows of 28672 codes on 8192 rows (the full-line
   form's staging would add K splits there, so the plan keeps the 16-row
-  loads) and the shapes above (full-line loads through LDS).
+  loads; at M = 16 with one workgroup per compute unit and the wide LDS)
+  and the shapes above (full-line loads through LDS).
 """
 import ctypes
 import sys
@@ -164,10 +165,12 @@ def test_mb_with_and_without_workspace():
     check(W, X, None, 128, out[2])
 
 
-def test_mb_long_rows_plain_loads():
-    """28672 codes per row, 8192 rows, M = 8: the plan keeps the 16-row
-    loads here (sampled rows against the oracle)."""
-    N, K, M = 8192, 28672, 8
+@pytest.mark.parametrize("M", [8, 16])
+def test_mb_long_rows_plain_loads(M):
+    """28672 codes per row, 8192 rows: the plan keeps the 16-row loads here,
+    and at M = 16 takes one workgroup per compute unit with the wide LDS
+    (8 splits instead of 14; sampled rows against the oracle)."""
+    N, K = 8192, 28672
     say("mb long rows", M, N, K)
     W = datagen.random_f16((N, K), 0.02, seed=31)
     X = datagen.random_f16((M, K), 1.0, seed=32)

@@ -393,8 +393,9 @@ int mb_cu_count() {
 }
 
 // LDS of a workgroup: at most 80 KB, so that two workgroups share a
-// compute unit
+// compute unit (kMbLdsWide: one workgroup per unit)
 constexpr uint32_t kMbLdsMax = 80 * 1024;
+constexpr uint32_t kMbLdsWide = 156 * 1024;
 // wavefronts the plan aims for per compute unit
 constexpr int kMbWavesPerCu = 8;
 
@@ -418,11 +419,16 @@ MbPlan mb_plan(int M, int N, int K, bool can_split) {
   const int mp = M <= 8 ? 8 : 16;
   const int nch = K / 128;
   const int nrb = (N + 15) / 16;
-  const int waves = kMbWavesPerCu * mb_cu_count();
+  const int cus = mb_cu_count();
+  const int waves = kMbWavesPerCu * cus;
   // chunks per split: what the LDS and the staging registers hold
-  auto splits_of = [&](bool fl) {
+  auto spl_max_of = [&](bool fl, uint32_t cap) {
     int spl_max = kMbMaxSpl;
-    while (spl_max > 1 && mb_lds(spl_max, mp, fl).total > kMbLdsMax) --spl_max;
+    while (spl_max > 1 && mb_lds(spl_max, mp, fl).total > cap) --spl_max;
+    return spl_max;
+  };
+  auto splits_of = [&](bool fl) {
+    const int spl_max = spl_max_of(fl, kMbLdsMax);
     int s = (nch + spl_max - 1) / spl_max;
     if (can_split) s = max(s, min((waves + nrb - 1) / nrb, max(1, nch / 2)));
     const int spl = (nch + s - 1) / s;
@@ -441,7 +447,39 @@ MbPlan mb_plan(int M, int N, int K, bool can_split) {
   p.gx = (nrb + kMbWaves * rbw - 1) / (kMbWaves * rbw);
   p.fl = fl;
   p.lds = mb_lds(spl, mp, fl).total;
-  p.ws_bytes = s > 1 ? kSplitCtrBytes + (size_t)s * M * N * 4 : 0;
+  // 16 stored token rows: their activation operands take twice the LDS, so
+  // under the two-per-unit limit the splits get shorter and more numerous.
+  // When that plan also has more workgroups than units, take one workgroup
+  // per unit with up to kMbLdsWide of LDS if it needs at most 3/4 of the
+  // splits and still gives 7/8 of the units a workgroup: the split count and
+  // row blocks per wavefront with the most workgroups, the fewest splits
+  // among equals (rows of 28672 codes on 8192 rows: 8 splits in 256
+  // workgroups instead of 14 in 308)
+  if (mp == 16 && can_split && s > 1 && p.gx * s > cus) {
+    const int wmax = spl_max_of(false, kMbLdsWide);
+    int best_w = 0, bs = 0, bspl = 0, bgx = 0;
+    for (int s2 = max(2, (nch + wmax - 1) / wmax); 4 * s2 <= 3 * s; ++s2) {
+      const int sp2 = (nch + s2 - 1) / s2;
+      if ((nch + sp2 - 1) / sp2 != s2) continue;
+      for (int r = 1; r <= 16; ++r) {
+        const int gx = (nrb + kMbWaves * r - 1) / (kMbWaves * r);
+        if (gx * s2 <= cus && gx * s2 > best_w) {
+          best_w = gx * s2;
+          bs = s2;
+          bspl = sp2;
+          bgx = gx;
+        }
+      }
+    }
+    if (bs > 1 && 8 * best_w >= 7 * cus) {
+      p.splits = bs;
+      p.spl = bspl;
+      p.gx = bgx;
+      p.fl = false;
+      p.lds = mb_lds(bspl, mp, false).total;
+    }
+  }
+  p.ws_bytes = p.splits > 1 ? kSplitCtrBytes + (size_t)p.splits * M * N * 4 : 0;
   return p;
 }
 
