@@ -104,8 +104,9 @@ def test_matmul_workspace_plan():
     device): prefill tiles 128 wide and 32, 64 or 128 tall, split over K until
     about one workgroup per unit; int4 decode at 2 <= M <= 16 on rows of
     more than 8192 codes, 16-row blocks split over K until about 8
-    wavefronts per unit; other decode shapes and shapes that fill the part
-    need none. Bytes: one float32 [M, N] plane per split, after a 64 KiB
+    wavefronts per unit (at M = 16 one workgroup per unit with a wider LDS
+    when that needs far fewer splits); other decode shapes and shapes that
+    fill the part need none. Bytes: one float32 [M, N] plane per split, after a 64 KiB
     counter region."""
     h = awq.lib()
     W = h.awq_w4a16_matmul_workspace_bytes
@@ -121,8 +122,10 @@ def test_matmul_workspace_plan():
     # LDS (29 chunks of 128 codes at M <= 8, 16 at M <= 16); 11008 = 86
     # chunks in 8 splits of 11 (the last one 9), one [M, N] plane per split
     assert W(8, 4096, 11008, 4, 128) == C + 8 * 8 * 4096 * 4
-    # 28672 codes = 224 chunks at M = 16: 14 splits of 16
-    assert W(16, 8192, 28672, 4, 128) == C + 14 * 16 * 8192 * 4
+    # 28672 codes = 224 chunks at M = 16: 14 splits of 16 would take 308
+    # workgroups for 256 units, so one workgroup per unit with the wide LDS
+    # takes 8 splits of 28
+    assert W(16, 8192, 28672, 4, 128) == C + 8 * 16 * 8192 * 4
     assert W(2048, 28672, 8192, 4, 128) == 0  # whole rounds of big tiles
     assert W(256, 11008, 4096, 3, 128) == 0  # 172 tiles of 128 x 128: no split
     # int4, M = 32: 32 tiles of 32 x 128, 8 splits of 8 steps (64 codes each)
