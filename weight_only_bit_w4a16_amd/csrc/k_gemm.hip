@@ -757,8 +757,13 @@ GemmPlan gemm_plan(int M, int N, int K, int bits, bool can_split) {
   const unsigned cus = (unsigned)cu_n();
   GemmPlan p{64, 64, 1, 0, 0};
   if (bits == 4) {
+    // 128 x 128 tiles once they fill 5/8 of the compute units: one 4-wavefront
+    // tile per unit then beats four rounds of 64 x 64 tiles (kernel traces,
+    // K = 4096: 256 x 11008 57.6 -> 51.6 us, 192 x 11008 65.5 -> 49.5,
+    // 256 x 14336 74.7 -> 51.9; at half the units 64 x 64 still wins:
+    // 256 x 8192 41.1 against 47.1, 512 x 4096 42.3 against 49.2)
     if (tiles_of(M, N, 256, 256) >= cus) p.bm = p.bn = 256;
-    else if (tiles_of(M, N, 128, 128) >= cus) p.bm = p.bn = 128;
+    else if (tiles_of(M, N, 128, 128) * 8 >= cus * 5) p.bm = p.bn = 128;
   } else if (tiles_of(M, N, 128, 128) * 2 >= cus) {
     p.bm = p.bn = 128;
   }
