@@ -396,8 +396,15 @@ int mb_cu_count() {
 // compute unit (kMbLdsWide: one workgroup per unit)
 constexpr uint32_t kMbLdsMax = 80 * 1024;
 constexpr uint32_t kMbLdsWide = 156 * 1024;
-// wavefronts the plan aims for per compute unit
+// wavefronts the plan aims for per compute unit when it sets the K splits
 constexpr int kMbWavesPerCu = 8;
+// ... and when it spreads the row blocks over the wavefronts: two
+// workgroups per unit once the splits are set (kernel traces, same sums:
+// 28672-code rows on 8192 rows at M = 2, 4, 8 40.8 -> 39.7, 41.6 -> 40.3,
+// 41.6 -> 40.2 us; 8704-code rows on 28672 rows at M = 8 47.8 -> 45.7 us;
+// other long-row shapes unchanged; raising the splits for it instead was
+// slower on 11008-code rows, 13.6 -> 16.8 us at M = 4 and 8)
+constexpr int kMbRowWavesPerCu = 16;
 
 template <int MP, bool PL, bool FL>
 hipError_t mb_allow_lds(size_t lds) {
@@ -413,7 +420,7 @@ hipError_t mb_allow_lds(size_t lds) {
 // The K splits: as few as the LDS allows, raised (with a workspace) until
 // the row blocks times the splits give about kMbWavesPerCu wavefronts per
 // compute unit, keeping at least two chunks per split; then as many row
-// blocks per wavefront as keep that many wavefronts.
+// blocks per wavefront as keep kMbRowWavesPerCu wavefronts per unit.
 MbPlan mb_plan(int M, int N, int K, bool can_split) {
   MbPlan p{};
   const int mp = M <= 8 ? 8 : 16;
@@ -440,7 +447,7 @@ MbPlan mb_plan(int M, int N, int K, bool can_split) {
   // full-line loads when their staging leaves the splits as they are
   const bool fl = splits_of(true) == s && mb_lds(spl, mp, true).total <= kMbLdsMax;
   if (s > 1 && (!can_split || nrb > kSplitMaxRowBlocks)) return p;  // splits == 0: not supported
-  const int rbw = max(1, (nrb * s) / waves);
+  const int rbw = max(1, (nrb * s) / (kMbRowWavesPerCu * cus));
   p.mp = mp;
   p.splits = s;
   p.spl = spl;
