@@ -915,9 +915,14 @@ hipError_t launch_gemm_gate_up(const __half* X, const uint32_t* qg, const float*
                          zg, M, N, K, wpr, gshift, y, nullptr, 0, qu, su, zu, 0, N, nullptr, 0);  \
   } while (0)
   if (bits == 4) {
-    if (tiles_of(M, N, 256, 128) >= cus)
+    // the bigger tile once its tiles fill 5/8 of the compute units (kernel
+    // traces, same outputs: 2 x 28672 x 8192 at M = 256 402.6 -> 275.9 us,
+    // 2 x 11008 x 4096 at M = 512 152.3 -> 131.5 us and at M = 128
+    // 70.3 -> 49.3 us; at 86 big tiles, 2 x 11008 x 4096 at M = 192 and
+    // 256, the 128 x 128 tile stays faster: 85.9 against 107.1 us)
+    if (tiles_of(M, N, 256, 128) * 8 >= cus * 5)
       AWQ_GU(4, 256, 256, 2, 4, 2);
-    else if (tiles_of(M, N, 128, 64) >= cus)
+    else if (tiles_of(M, N, 128, 64) * 8 >= cus * 5)
       AWQ_GU(4, 128, 128, 2, 2, 4);
     else
       AWQ_GU(4, 64, 128, 2, 2, 4);
