@@ -757,13 +757,18 @@ GemmPlan gemm_plan(int M, int N, int K, int bits, bool can_split) {
   const unsigned cus = (unsigned)cu_n();
   GemmPlan p{64, 64, 1, 0, 0};
   if (bits == 4) {
-    // 128 x 128 tiles once they fill 5/8 of the compute units: one 4-wavefront
-    // tile per unit then beats four rounds of 64 x 64 tiles (kernel traces,
-    // K = 4096: 256 x 11008 57.6 -> 51.6 us, 192 x 11008 65.5 -> 49.5,
-    // 256 x 14336 74.7 -> 51.9; at half the units 64 x 64 still wins:
-    // 256 x 8192 41.1 against 47.1, 512 x 4096 42.3 against 49.2)
-    if (tiles_of(M, N, 256, 256) >= cus) p.bm = p.bn = 256;
-    else if (tiles_of(M, N, 128, 128) * 8 >= cus * 5) p.bm = p.bn = 128;
+    // Rounds of tiles, one per compute unit at a time: a 256 x 256 tile
+    // takes about 3 times as long as a 128 x 128 one, which takes about 2.5
+    // times a 64 x 64 one (kernel traces, M x N at K = 4096: 256 x 11008
+    // 57.6 us on 64 x 64 tiles -> 51.6 on 128 x 128, 1024 x 4096 92.8 ->
+    // 55.3, 768 x 11008 149.1 -> 121.5 on 256 x 256, and at K = 8192
+    // 512 x 28672 352.7 -> 276.6; the rule keeps 64 x 64 for 256 x 8192,
+    // 41.1 against 47.1, and 128 x 128 for 256 x 28672, 189.1 against 208.6)
+    const unsigned big = tiles_of(M, N, 256, 256), mid = tiles_of(M, N, 128, 128);
+    const unsigned small = tiles_of(M, N, 64, 64);
+    auto rounds = [&](unsigned t) { return (t + cus - 1) / cus; };
+    if (big >= cus || 3 * rounds(big) <= rounds(mid)) p.bm = p.bn = 256;
+    else if (5 * rounds(mid) <= 2 * rounds(small)) p.bm = p.bn = 128;
   } else if (tiles_of(M, N, 128, 128) * 2 >= cus) {
     p.bm = p.bn = 128;
   }
