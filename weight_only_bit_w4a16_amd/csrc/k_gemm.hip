@@ -110,6 +110,10 @@ struct Stage<3, BM, BN, NT> {
   uint32_t zw[Cfg<3, BM, BN, NT>::BIT], zsh[Cfg<3, BM, BN, NT>::BIT];
 };
 
+// first word loaded by quarter qt of an int3 group: 0, 4, 7, 9 (a shift and a
+// mask; the nested ternary became branches)
+__device__ __forceinline__ int int3_quarter_word(int qt) { return (0x09070400 >> (8 * qt)) & 0xff; }
+
 // f(integral_constant<int, i>) for i = I .. N-1, in order
 template <int I, int N, typename F>
 __device__ __forceinline__ void unroll_c(F&& f) {
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
         const int n = brow_n(r);
         // dword-aligned 16-byte load that stays inside the group: quarter 3
         // reads words 9..12 and uses the last three
-        const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
+        const int w0 = int3_quarter_word(qt);
         const u32x4a4 v =
             ld_nt(reinterpret_cast<const u32x4a4*>(Q + (size_t)n * wpr + ks * 13 + w0));
         st.b[i] = u32x4{v[0], v[1], v[2], v[3]};
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       const float offh[5] = {256.f, 32.f, 1024.f, 128.f, 1024.f};
       const int id = tid + NT * i;
       const int r = id >> 2, qt = id & 3;
-      const int w0 = qt == 0 ? 0 : (qt == 1 ? 4 : (qt == 2 ? 7 : 9));
+      const int w0 = int3_quarter_word(qt);
       const float zf = (float)((st.zw[i] >> st.zsh[i]) & ZMASK);
       const _Float16 d16 = row_step(st.d[i], rexp[0]);
       const h2 dh = {d16, d16};
@@ -383,9 +387,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
       for (int p = 0; p < 5; ++p) add[p] = h2{(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        // quarter 0 stores words 0-3, quarters 1 and 2 their first three,
-        // quarter 3 (loaded from word 9) words 10-12
-        const bool use = qt == 0 || (qt == 3 ? u > 0 : u < 3);
+        // quarters load words 0-3, 4-7, 7-10 and 9-12 and store all four:
+        // words 7, 9 and 10 are stored by two lanes of the same row with the
+        // same values (same word, same step and zero point), so no lane
+        // needs a branch around its stores (one kept the MFMAs of the step
+        // from interleaving with this work)
         const uint32_t w = st.b[i][u];
         const uint32_t t8 = w >> 8, u1 = w << 1;
         const uint32_t raw[5] = {and_or(w, ur.m3[0], ur.magic), and_or(w, ur.m3[1], ur.magic),
@@ -395,14 +401,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
 #pragma unroll
         for (int p = 0; p < 5; ++p)
           pr[p] = hbits(__builtin_elementwise_fma(hv(raw[p]), mul[p], add[p]) * dh);
-        if (use) {
-          uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * (w0 + u)]);
-          pb[0] = plo(pr[0], pr[1]);                             // (c0, c1)
-          pb[1] = plo(pr[4], pr[2]);                             // (c2, c3)
-          pb[2] = __builtin_amdgcn_perm(pr[4], pr[3], 0x07060100u);  // (c4, c5)
-          pb[3] = phi(pr[0], pr[1]);                             // (c6, c7)
-          pb[4] = phi(pr[2], pr[3]);                             // (c8, c9)
-        }
+        uint32_t* pb = reinterpret_cast<uint32_t*>(&lb[r * STR + 10 * (w0 + u)]);
+        pb[0] = plo(pr[0], pr[1]);                             // (c0, c1)
+        pb[1] = plo(pr[4], pr[2]);                             // (c2, c3)
+        pb[2] = __builtin_amdgcn_perm(pr[4], pr[3], 0x07060100u);  // (c4, c5)
+        pb[3] = phi(pr[0], pr[1]);                             // (c6, c7)
+        pb[4] = phi(pr[2], pr[3]);                             // (c8, c9)
       }
     }
   };
@@ -426,15 +430,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   const int arow = (BM / WGM) * wm + lr;
   const int brow = (BN / WGN) * wn + lr;
 
-  auto mma = [&](const uint16_t* la, const uint16_t* lb, int kk) {
+  // operand fragments of sub-step kk, and the MFMAs of one sub-step
+  auto frags = [&](const uint16_t* la, const uint16_t* lb, int kk, u32x4* fa, u32x4* fb) {
     const int ko = kk * 16 + lk;
-    u32x4 fa[TM], fb[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       fa[i] = *reinterpret_cast<const u32x4*>(&la[(arow + 32 * i) * STR + ko]);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       fb[j] = *reinterpret_cast<const u32x4*>(&lb[(brow + 32 * j) * STR + ko]);
+  };
+  auto mfmas = [&](const u32x4* fa, const u32x4* fb) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -443,24 +449,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
   constexpr int NKS = C::SLOTS / 16;
   // one pipeline step: MFMAs on buffer cur, with the stores of stage sst
   // into the other buffer spread over the sub-steps, then the loads of
-  // stage lst
+  // stage lst. The fragments of sub-step kk + 1 are read from LDS before
+  // the MFMAs of sub-step kk, so their latency overlaps those MFMAs (two
+  // sub-steps ahead measured the same).
+  constexpr int PFD = 1;
   auto step = [&](int cur, const St& sst, St& lst, int lks, auto SZ) {
     if constexpr (SZ.value) set_dq(sst);
     const uint16_t* la = lds_a[cur];
     const uint16_t* lb = lds_b[cur];
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) {
-      mma(la, lb, kk);
-      if (kk < NKS - 1) {
-        if (kk < NA) store_a(sst, cur ^ 1, kk);
-        if (kk < NB) store_b(sst, cur ^ 1, kk);
+    u32x4 fa[PFD + 1][TM], fb[PFD + 1][TN];
+    unroll_c<0, (PFD < NKS ? PFD : NKS)>(
+        [&](auto I) { frags(la, lb, decltype(I)::value, fa[decltype(I)::value], fb[decltype(I)::value]); });
+    unroll_c<0, NKS>([&](auto KK) {
+      constexpr int kk = decltype(KK)::value;
+      constexpr int nb = (kk + PFD) % (PFD + 1);
+      if constexpr (kk + PFD < NKS) frags(la, lb, kk + PFD, fa[nb], fb[nb]);
+      mfmas(fa[kk % (PFD + 1)], fb[kk % (PFD + 1)]);
+      if constexpr (kk < NKS - 1) {
+        if constexpr (kk < NA) store_a(sst, cur ^ 1, kk);
+        if constexpr (kk < NB) store_b(sst, cur ^ 1, kk);
       } else {
-#pragma unroll
-        for (int i = kk; i < NA; ++i) store_a(sst, cur ^ 1, i);
-#pragma unroll
-        for (int i = kk; i < NB; ++i) store_b(sst, cur ^ 1, i);
+        unroll_c<kk, NA>([&](auto I) { store_a(sst, cur ^ 1, decltype(I)::value); });
+        unroll_c<kk, NB>([&](auto I) { store_b(sst, cur ^ 1, decltype(I)::value); });
       }
-    }
+    });
     load_step(lst, lks, SZ);
     __syncthreads();
     // keep the next step's dequantization below the barrier: hoisted above
