@@ -374,17 +374,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
                          {(_Float16)0.5f, (_Float16)1.f},
                          {(_Float16)0.0625f, (_Float16)0.125f},
                          {(_Float16)0.0078125f, (_Float16)1.f}};
+      // magic offsets of the five pairs, as 1024 - offset (fp16, exact)
       const float offl[5] = {1024.f, 128.f, 512.f, 64.f, 8.f};
       const float offh[5] = {256.f, 32.f, 1024.f, 128.f, 1024.f};
       const int id = tid + NT * i;
       const int r = id >> 2, qt = id & 3;
       const int w0 = int3_quarter_word(qt);
-      const float zf = (float)((st.zw[i] >> st.zsh[i]) & ZMASK);
+      const uint32_t z = (st.zw[i] >> st.zsh[i]) & ZMASK;
       const _Float16 d16 = row_step(st.d[i], rexp[0]);
       const h2 dh = {d16, d16};
+      // -(offset + z) per half: -(1024 + z) from the fp16 bit pattern, plus
+      // 1024 - offset, in packed fp16 (every value an integer below 2048,
+      // so exact: the same bits as the float32 sums rounded to fp16)
+      const h2 mz = hv((0xE400u + z) * 0x00010001u);
       h2 add[5];
 #pragma unroll
-      for (int p = 0; p < 5; ++p) add[p] = h2{(_Float16)(-(offl[p] + zf)), (_Float16)(-(offh[p] + zf))};
+      for (int p = 0; p < 5; ++p)
+        add[p] = mz + h2{(_Float16)(1024.f - offl[p]), (_Float16)(1024.f - offh[p])};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         // quarters load words 0-3, 4-7, 7-10 and 9-12 and store all four:
