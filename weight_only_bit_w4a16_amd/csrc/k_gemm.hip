@@ -464,8 +464,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(
     const uint16_t* la = lds_a[cur];
     const uint16_t* lb = lds_b[cur];
     u32x4 fa[PFD + 1][TM], fb[PFD + 1][TN];
-    unroll_c<0, (PFD < NKS ? PFD : NKS)>(
-        [&](auto I) { frags(la, lb, decltype(I)::value, fa[decltype(I)::value], fb[decltype(I)::value]); });
+    unroll_c<0, (PFD < NKS ? PFD : NKS)>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      frags(la, lb, i, fa[i], fb[i]);
+    });
     unroll_c<0, NKS>([&](auto KK) {
       constexpr int kk = decltype(KK)::value;
       constexpr int nb = (kk + PFD) % (PFD + 1);
