@@ -15,6 +15,11 @@ namespace awq {
 // thread w gathers the 24-bit pieces that cover codes 10w..10w+9 from its
 // neighbours and writes word w.
 // ---------------------------------------------------------------------------
+// The packed codes, steps and zero points go out with nontemporal stores: a
+// packed matrix is read later (by the products), not by the next kernel, and
+// with ordinary stores its lines were written back to HBM while the next
+// kernel ran (the decode launches right after a pack of the 8192x28672 layer
+// took 24.2 instead of 22.3 us; same bits, same pack time).
 template <int BITS, int TPG, bool SYM>
 __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ W,
                                                          const float* __restrict__ s, int N, int K,
@@ -79,22 +84,22 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
 
     uint32_t* qrow = Q + n * wpr;
     if (BITS == 4) {
-      if (active) qrow[g * (G / 8) + j] = packed;
+      if (active) __builtin_nontemporal_store(packed, qrow + g * (G / 8) + j);
     } else {
       const int jb = j & 15;                         // lane in the 128-code block
       const int blk = g * (G / 128) + (j >> 4);      // block of the row
       const uint32_t word = int3_block_word(packed, jb);
       if (active) {
         if (jb < 13) {
-          qrow[13 * blk + jb] = word;
+          __builtin_nontemporal_store(word, qrow + 13 * blk + jb);
         } else if (blk == K / 128 - 1 && 13 * blk + jb < wpr) {
-          qrow[13 * blk + jb] = 0u;  // row padding to 16 bytes
+          __builtin_nontemporal_store(0u, qrow + 13 * blk + jb);  // row padding to 16 bytes
         }
       }
     }
     if (active && j == 0) {
-      scales[n * ng + g] = gg.delta;
-      zeros[n * ng + g] = (uint8_t)gg.z;
+      __builtin_nontemporal_store(gg.delta, scales + n * ng + g);
+      __builtin_nontemporal_store((uint8_t)gg.z, zeros + n * ng + g);
     }
   }
 }
@@ -156,9 +161,9 @@ __global__ __launch_bounds__(512) void quant_pack_row_kernel(const uint16_t* __r
       const uint32_t word = int3_block_word(packed, jb);
       if (k0 < K) {
         if (jb < 13)
-          qrow[13 * blk + jb] = word;
+          __builtin_nontemporal_store(word, qrow + 13 * blk + jb);
         else if (blk == K / 128 - 1 && 13 * blk + jb < wpr)
-          qrow[13 * blk + jb] = 0u;  // row padding to 16 bytes
+          __builtin_nontemporal_store(0u, qrow + 13 * blk + jb);  // row padding to 16 bytes
       }
     }
   }
