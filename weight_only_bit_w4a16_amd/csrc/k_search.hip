@@ -183,8 +183,11 @@ __global__ __launch_bounds__(256) void fake_quant_error_multi_kernel(
         hv[p] = h[0] | (h[1] << 16);
       }
       if (active)
-        *reinterpret_cast<uint4*>(E + (size_t)a * NK + n * K + k0) =
-            make_uint4(hv[0], hv[1], hv[2], hv[3]);
+        // nontemporal: the planes (0.94 GB for a pair on 8192x28672) pass
+        // through the caches once (the contraction that reads them then ran
+        // 1-2% faster; same bits)
+        __builtin_nontemporal_store(u32x4{hv[0], hv[1], hv[2], hv[3]},
+                                    reinterpret_cast<u32x4*>(E + (size_t)a * NK + n * K + k0));
     }
   }
 }
